@@ -1,0 +1,263 @@
+"""Float64 CPU oracle of the sparse-MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links
+this module: only the tests, the package's smoke check and the CPU-baseline
+leg of the benchmark do. It shares no code with the HIP path.
+
+It is the plain definition of the layer, written in float64 numpy from the
+pages, one step per function, in the pages' order:
+
+  1. router logits  L = x . W_r^T                     (mlxcel #845 "Checkpoint
+     weight layout": the router is mlp.router.gate; HF "AFMoE" doc,
+     AfmoeForCausalLM outputs: router_logits are raw, one row per token)
+  2. scores         s = sigmoid(L)  (or softmax)      (mlxcel #845 "Routing
+     detail": score_func sigmoid; HF "AFMoE" doc, key features / expert
+     routing: sigmoid or softmax scoring)
+  3. selection key  key = s + expert_bias             (mlxcel #845 "Routing
+     detail": bias added for selection only; mlxcel #763 "Architecture
+     specification", MoE bullet: e_score_correction_bias, selection only)
+  4. top-k          first k experts in the order (key desc, index asc)
+  5. gather         g = s[idx]   (unbiased scores, mlxcel #845 "Routing detail")
+  6. route_norm     w = g / sum(g)                    (mlxcel #845 "Routing detail")
+  7. route_scale    w *= route_scale                  (mlxcel #845 "Routing
+     detail"; HF "AFMoE" doc, route_scale: scaling for the routed experts)
+  8. experts        y = W_d[e] . act(W_g[e] . x, W_u[e] . x)
+     silu:      act(g,u) = g*sigmoid(g)*u              (HF "AFMoE" doc, hidden_act)
+     swigluoai: act(g,u) = g'*sigmoid(alpha*g')*(u'+beta), g'=min(g,limit),
+                u'=clip(u,-limit,limit)                (mlxcel #763, Activation)
+  9. shared experts y_s = W_sd . act(W_sg . x, W_su . x), always on, weight 1
+     (HF "AFMoE" doc, shared experts; mlxcel #763 MoE bullet: a shared expert
+     packed as slot E participates with a fixed score of 1.0)
+ 10. combine        out = sum_j w_j * y_{idx_j} + sum_s y_s
+
+Readings where the pages are silent are listed in the design notes: the bias
+is added to the post-sigmoid scores; normalise then scale; no epsilon in the
+norm; ties go to the lower expert index and the k indices are emitted in the
+selection order; the selection key is formed in float64 from fp32 logits.
+
+Inputs are the exact stored values: bf16 tensors arrive as uint16 bit arrays
+and are widened exactly to float64 here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# storage decoding (exact)
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    """Exact float64 value of a stored tensor (uint16 = bf16 bits)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(F64)
+    return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------
+# routing
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """L[t, e] = sum_h x[t, h] * W_r[e, h]   (router.gate, a bias-free linear)."""
+    return as_f64(x) @ as_f64(w_router).T
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-z)) in float64."""
+    z = np.asarray(z, dtype=F64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def scores(logits: np.ndarray, score_func: str = "sigmoid") -> np.ndarray:
+    """Per-expert scores from the router logits (float64)."""
+    L = np.asarray(logits, dtype=F64)
+    if score_func == "sigmoid":
+        return sigmoid(L)
+    if score_func == "softmax":
+        m = L.max(axis=-1, keepdims=True)
+        ez = np.exp(L - m)
+        return ez / ez.sum(axis=-1, keepdims=True)
+    raise ValueError(score_func)
+
+
+def selection_keys(s: np.ndarray, expert_bias: np.ndarray | None) -> np.ndarray:
+    """key = s + b: the bias only ever enters the selection."""
+    if expert_bias is None:
+        return np.array(s, dtype=F64, copy=True)
+    return np.asarray(s, dtype=F64) + as_f64(expert_bias)[None, :]
+
+
+def select_topk(keys: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest keys per row, in the total order
+    (key descending, expert index ascending); emitted in that order.
+
+    A stable sort on -key keeps equal keys in ascending index order."""
+    order = np.argsort(-np.asarray(keys, dtype=F64), axis=-1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def route_weights(s: np.ndarray, idx: np.ndarray, route_norm: bool,
+                  route_scale: float) -> np.ndarray:
+    """Gather the UNBIASED scores of the chosen experts, renormalise them to
+    sum to one (route_norm), then multiply by route_scale."""
+    g = np.take_along_axis(np.asarray(s, dtype=F64), idx.astype(np.int64), axis=-1)
+    if route_norm:
+        den = g.sum(axis=-1, keepdims=True)
+        w = np.divide(g, den, out=np.zeros_like(g), where=den != 0.0)
+    else:
+        w = g
+    return w * F64(route_scale)
+
+
+def route(logits: np.ndarray, expert_bias: np.ndarray | None, k: int,
+          score_func: str = "sigmoid", route_norm: bool = True,
+          route_scale: float = 1.0):
+    """Steps 2-7: returns (s, keys, idx [T,k] int32, w [T,k] float64)."""
+    s = scores(logits, score_func)
+    keys = selection_keys(s, expert_bias)
+    idx = select_topk(keys, k)
+    w = route_weights(s, idx, route_norm, route_scale)
+    return s, keys, idx, w
+
+
+def boundary_gap(keys: np.ndarray, k: int) -> float:
+    """Smallest gap between the k-th and (k+1)-th key over all rows (0 means
+    an exact tie straddles the boundary somewhere)."""
+    E = keys.shape[-1]
+    if k >= E:
+        return float("inf")
+    srt = -np.sort(-np.asarray(keys, dtype=F64), axis=-1)
+    return float(np.min(srt[:, k - 1] - srt[:, k]))
+
+
+# ----------------------------------------------------------------------------
+# grouping of the (token, slot) rows by expert
+
+def permute(idx: np.ndarray, num_experts: int):
+    """Stable counting sort of the rows r = t*k + j by expert.
+
+    Returns counts[E], offsets[E+1] (exclusive scan), sorted_rows[T*k]
+    (rows of expert 0 in ascending r, then expert 1, ...) and row_pos, the
+    inverse permutation (row_pos[sorted_rows[p]] = p)."""
+    e_of_row = idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(e_of_row, minlength=num_experts).astype(np.int32)
+    offsets = np.zeros(num_experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_rows = np.argsort(e_of_row, kind="stable").astype(np.int32)
+    row_pos = np.empty_like(sorted_rows)
+    row_pos[sorted_rows] = np.arange(sorted_rows.size, dtype=np.int32)
+    return counts, offsets, sorted_rows, row_pos
+
+
+# ----------------------------------------------------------------------------
+# expert MLPs
+
+def act_silu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """SwiGLU with SiLU: silu(gate) * up."""
+    return g * sigmoid(g) * u
+
+
+def act_swigluoai(g: np.ndarray, u: np.ndarray, alpha: float, limit: float,
+                  beta: float) -> np.ndarray:
+    """clamp-SwiGLU: x_glu (gate) clamped from above at limit, x_linear (up)
+    clamped to [-limit, limit]; x_glu * sigmoid(alpha*x_glu) * (x_linear+beta)."""
+    gc = np.minimum(g, F64(limit))
+    uc = np.clip(u, -F64(limit), F64(limit))
+    return gc * sigmoid(F64(alpha) * gc) * (uc + F64(beta))
+
+
+def activation(cfg: dict):
+    if cfg["hidden_act"] == "silu":
+        return act_silu
+    if cfg["hidden_act"] == "swigluoai":
+        a, l, b = cfg["act_alpha"], cfg["act_limit"], cfg["act_beta"]
+        return lambda g, u: act_swigluoai(g, u, a, l, b)
+    raise ValueError(cfg["hidden_act"])
+
+
+def mlp_hidden(xr: np.ndarray, wg: np.ndarray, wu: np.ndarray, act) -> np.ndarray:
+    """act(x . W_g^T, x . W_u^T) for rows xr [n,H], W [I,H] (float64)."""
+    return act(xr @ wg.T, xr @ wu.T)
+
+
+def mlp_out(h: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """h . W_d^T for h [n,I], W_d [H,I]."""
+    return h @ wd.T
+
+
+# ----------------------------------------------------------------------------
+# the whole layer
+
+def _shared_weights(inp, cfg):
+    """List of (W_g, W_u, W_d) float64 triples of the always-on experts."""
+    S = cfg["num_shared_experts"]
+    if S == 0:
+        return []
+    if cfg["shared_packed"]:
+        E = cfg["num_experts"]
+        return [(as_f64(inp.w_gate[E]), as_f64(inp.w_up[E]), as_f64(inp.w_down[E]))]
+    return [(as_f64(inp.ws_gate[s]), as_f64(inp.ws_up[s]), as_f64(inp.ws_down[s]))
+            for s in range(S)]
+
+
+def moe_forward(inp, cfg: dict, logits: np.ndarray | None = None,
+                want_hidden: bool = False) -> dict:
+    """Full layer over all T tokens. `logits` (fp32 values) replaces step 1
+    when given. Expert weights are widened to float64 one expert at a time."""
+    T = inp.x.shape[0]
+    E, k = cfg["num_experts"], cfg["num_experts_per_tok"]
+    x = as_f64(inp.x)
+    L = router_logits(inp.x, inp.w_router) if logits is None else as_f64(logits)
+    s, keys, idx, w = route(L, inp.expert_bias, k, cfg["score_func"],
+                            bool(cfg["route_norm"]), cfg["route_scale"])
+    counts, offsets, sorted_rows, row_pos = permute(idx, E)
+    act = activation(cfg)
+    out = np.zeros((T, x.shape[1]), F64)
+    I = cfg["moe_intermediate_size"]
+    h = np.zeros((T * k, I), F64) if want_hidden else None
+    for e in range(E):
+        rows = sorted_rows[offsets[e]:offsets[e + 1]]
+        if rows.size == 0:
+            continue
+        toks = rows // k
+        he = mlp_hidden(x[toks], as_f64(inp.w_gate[e]), as_f64(inp.w_up[e]), act)
+        if want_hidden:
+            h[offsets[e]:offsets[e + 1]] = he
+        ye = mlp_out(he, as_f64(inp.w_down[e]))
+        wr = w.reshape(-1)[rows]
+        np.add.at(out, toks, wr[:, None] * ye)
+    hs_all = []
+    for (wg, wu, wd) in _shared_weights(inp, cfg):
+        hs = mlp_hidden(x, wg, wu, act)
+        hs_all.append(hs)
+        out += mlp_out(hs, wd)
+    res = dict(logits=L, scores=s, keys=keys, idx=idx, w=w, counts=counts,
+               offsets=offsets, sorted_rows=sorted_rows, row_pos=row_pos, out=out)
+    if want_hidden:
+        res["h"] = h
+        res["h_shared"] = np.concatenate(hs_all, axis=1) if hs_all else None
+    return res
+
+
+def moe_forward_tokens(inp, cfg: dict, tokens, logits_rows: np.ndarray | None = None) -> dict:
+    """The layer's output rows for a subset of tokens only (routing is per
+    token, so each row is computed independently). logits_rows [n,E] (fp32
+    values) replaces step 1 for those tokens when given."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    k = cfg["num_experts_per_tok"]
+    x = as_f64(inp.x[tokens])
+    L = (as_f64(inp.x[tokens]) @ as_f64(inp.w_router).T if logits_rows is None
+         else as_f64(logits_rows))
+    s, keys, idx, w = route(L, inp.expert_bias, k, cfg["score_func"],
+                            bool(cfg["route_norm"]), cfg["route_scale"])
+    act = activation(cfg)
+    out = np.zeros((tokens.size, x.shape[1]), F64)
+    for e in np.unique(idx):
+        sel_t, sel_j = np.nonzero(idx == e)
+        he = mlp_hidden(x[sel_t], as_f64(inp.w_gate[e]), as_f64(inp.w_up[e]), act)
+        ye = mlp_out(he, as_f64(inp.w_down[e]))
+        out[sel_t] += w[sel_t, sel_j][:, None] * ye
+    for (wg, wu, wd) in _shared_weights(inp, cfg):
+        out += mlp_out(mlp_hidden(x, wg, wu, act), wd)
+    return dict(logits=L, idx=idx, w=w, out=out)

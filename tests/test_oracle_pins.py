@@ -1,0 +1,365 @@
+"""Pins of the float64 oracle against facts fixed outside the oracle itself:
+hand-worked examples of the routing rule, closed forms, brute-force top-k,
+invariants of the selection-only bias and of route_norm, and degenerate
+layers that reduce to a textbook MLP or a dense mixture.
+
+Pages: mlxcel issue #845 (Arcee AFMoE) "Routing detail"; HF Transformers doc
+"AFMoE" (AfmoeConfig, expert routing, shared experts); mlxcel issue #763
+(MiniMax-M3) "Architecture specification" (MoE and Activation bullets) and
+"Implementation plan" (tests of router selection with bias and of the packed
+shared expert).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from workloads import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+ULP1 = np.finfo(np.float64).eps
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _logit(s):
+    return {"0": 0.0, "ln3": math.log(3.0), "-ln3": -math.log(3.0),
+            "ln4": math.log(4.0), "-ln4": -math.log(4.0)}[s]
+
+
+# --------------------------------------------------------------------------
+# sigmoid
+
+def test_sigmoid_closed_forms():
+    assert O.sigmoid(np.array([0.0]))[0] == 0.5
+    assert abs(O.sigmoid(np.array([math.log(3.0)]))[0] - 0.75) <= 2 * ULP1
+    assert abs(O.sigmoid(np.array([-math.log(4.0)]))[0] - 0.2) <= 2 * ULP1
+    z = np.linspace(-30, 30, 2001)
+    assert np.max(np.abs(O.sigmoid(z) + O.sigmoid(-z) - 1.0)) <= 2 * ULP1
+    # saturation: exactly 1.0 far right; monotone
+    assert O.sigmoid(np.array([40.0]))[0] == 1.0
+    assert np.all(np.diff(O.sigmoid(z)) >= 0)
+
+
+def test_softmax_scores():
+    L = np.random.default_rng(1).standard_normal((5, 7))
+    s = O.scores(L, "softmax")
+    assert np.allclose(s.sum(-1), 1.0, rtol=0, atol=4 * ULP1)
+    assert np.allclose(O.scores(np.zeros((1, 4)), "softmax"), 0.25, rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
+# routing rule: hand-worked example
+
+def test_route_hand_example():
+    g = _gold("route_hand_example.json")
+    for case in g["cases"]:
+        L = np.array([[_logit(v) for v in case["logits"]]])
+        b = np.array(case["bias"], dtype=np.float64)
+        s, keys, idx, w = O.route(L, b, g["k"], "sigmoid", g["route_norm"], g["route_scale"])
+        assert np.allclose(s[0], case["scores"], rtol=0, atol=4 * ULP1)
+        assert idx[0].tolist() == case["idx"], case["what"]
+        assert np.allclose(w[0], case["w"], rtol=4 * ULP1, atol=0), case["what"]
+        if "idx_without_bias" in case:
+            _, _, idx0, _ = O.route(L, None, g["k"], "sigmoid", True, g["route_scale"])
+            assert idx0[0].tolist() == case["idx_without_bias"]
+
+
+def test_route_hand_example_catches_bias_on_logits():
+    """A plausible mistake (bias added to the logits) changes the selection."""
+    case = _gold("route_hand_example.json")["cases"][0]
+    L = np.array([[_logit(v) for v in case["logits"]]])
+    b = np.array(case["bias"])
+    wrong = O.select_topk(O.sigmoid(L + b), 2)
+    assert wrong[0].tolist() != case["idx"]
+
+
+# --------------------------------------------------------------------------
+# top-k: brute force over all subsets
+
+def _brute_topk(key_row, k):
+    """All k-subsets where every chosen key beats every unchosen one (greater,
+    or equal with a lower index)."""
+    E = key_row.size
+    good = []
+    for sub in itertools.combinations(range(E), k):
+        chosen = set(sub)
+        ok = True
+        for a in chosen:
+            for c in range(E):
+                if c in chosen:
+                    continue
+                if not (key_row[a] > key_row[c] or (key_row[a] == key_row[c] and a < c)):
+                    ok = False
+                    break
+            if not ok:
+                break
+        if ok:
+            good.append(sub)
+    return good
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (5, 2), (8, 3), (12, 4), (6, 6)])
+def test_topk_bruteforce(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    for trial in range(40):
+        if trial % 2:
+            keys = rng.choice(np.array([0.1, 0.5, 0.5, 0.9, 1.0]), size=(1, E))  # many exact ties
+        else:
+            keys = rng.random((1, E))
+        idx = O.select_topk(keys, k)[0]
+        subs = _brute_topk(keys[0], k)
+        assert len(subs) == 1
+        assert sorted(idx.tolist()) == list(subs[0])
+        # emitted in the total order: key desc, then index asc
+        for a, c in zip(idx[:-1], idx[1:]):
+            assert keys[0, a] > keys[0, c] or (keys[0, a] == keys[0, c] and a < c)
+
+
+# --------------------------------------------------------------------------
+# bias and norm invariants
+
+def _rand_route_inputs(T=300, E=16, seed=3):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E)) * 2.0
+    b = rng.uniform(-0.3, 0.3, E)
+    return L, b
+
+
+def test_weights_come_from_unbiased_scores():
+    L, b = _rand_route_inputs()
+    s, keys, idx, w = O.route(L, b, 4, "sigmoid", True, 2.5)
+    g = np.take_along_axis(O.sigmoid(L), idx.astype(np.int64), 1)
+    assert np.array_equal(w, g / g.sum(1, keepdims=True) * 2.5)
+
+
+def test_bias_shift_invariance():
+    L, b = _rand_route_inputs()
+    _, _, i1, w1 = O.route(L, b, 4, "sigmoid", True, 1.7)
+    _, _, i2, w2 = O.route(L, b + 0.25, 4, "sigmoid", True, 1.7)  # exact in fp64 here
+    keep = np.all(i1 == i2, axis=1)
+    assert keep.mean() > 0.95
+    assert np.array_equal(w1[keep], w2[keep])
+
+
+def test_bias_changes_selection_never_weights():
+    L, b = _rand_route_inputs()
+    _, _, ib, wb = O.route(L, b, 4, "sigmoid", True, 1.0)
+    _, _, i0, w0 = O.route(L, None, 4, "sigmoid", True, 1.0)
+    same = np.all(ib == i0, axis=1)
+    assert 0 < same.sum() < same.size      # the bias does change some selections
+    assert np.array_equal(wb[same], w0[same])
+
+
+@pytest.mark.parametrize("k,scale", [(1, 2.826), (3, 1.0), (6, 2.0), (8, 2.826)])
+def test_norm_sums_to_route_scale(k, scale):
+    L, b = _rand_route_inputs(E=16)
+    _, _, _, w = O.route(L, b, k, "sigmoid", True, scale)
+    assert np.max(np.abs(w.sum(1) - scale)) <= 4 * ULP1 * k * scale
+    if k == 1:
+        assert np.all(w == scale)
+
+
+def test_norm_off_gives_scaled_scores():
+    L, b = _rand_route_inputs()
+    s, _, idx, w = O.route(L, b, 3, "sigmoid", False, 2.0)
+    assert np.array_equal(w, 2.0 * np.take_along_axis(s, idx.astype(np.int64), 1))
+
+
+# --------------------------------------------------------------------------
+# activations: closed-form points
+
+def test_activation_points():
+    g = _gold("activation_points.json")
+    for p in g["swigluoai"]:
+        v = O.act_swigluoai(np.float64(p["g"]), np.float64(p["u"]), g["alpha"], g["limit"], g["beta"])
+        assert abs(v - p["value"]) <= 1e-13 * max(1.0, abs(p["value"])), p
+    for p in g["silu"]:
+        v = O.act_silu(np.float64(p["g"]), np.float64(p["u"]))
+        assert abs(v - p["value"]) <= 1e-15, p
+
+
+# --------------------------------------------------------------------------
+# permutation
+
+def test_permute_properties():
+    rng = np.random.default_rng(5)
+    T, E, k = 97, 11, 3
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[:, :] = np.where(rng.random((T, k)) < 0.0, 0, idx)
+    counts, offsets, sr, rp = O.permute(idx, E)
+    assert counts.sum() == T * k
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(np.sort(sr), np.arange(T * k))
+    flat = idx.reshape(-1)
+    for e in range(E):
+        seg = sr[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)        # stable: ascending row order
+    assert np.array_equal(rp[sr], np.arange(T * k))
+
+
+# --------------------------------------------------------------------------
+# degenerate layers
+
+def _tiny_cfg(**kw):
+    c = dict(hidden_size=8, num_experts=3, num_experts_per_tok=2,
+             moe_intermediate_size=4, num_shared_experts=1,
+             shared_intermediate_size=4, shared_packed=0, score_func="sigmoid",
+             route_norm=1, route_scale=1.0, hidden_act="silu", act_alpha=1.702,
+             act_limit=7.0, act_beta=1.0, dtype="f32")
+    c.update(kw)
+    return c
+
+
+def _tiny_inputs(cfg, T=5, seed=11):
+    rng = np.random.default_rng(seed)
+    H, E, I = cfg["hidden_size"], cfg["num_experts"], cfg["moe_intermediate_size"]
+    S, Is = cfg["num_shared_experts"], cfg["shared_intermediate_size"]
+    Et = E + (1 if cfg["shared_packed"] else 0)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    inp = synth.MoeInputs(cfg=cfg, x=f(T, H), w_router=f(E, H) * np.float32(0.5),
+                          expert_bias=(rng.uniform(-0.2, 0.2, E)).astype(np.float32),
+                          w_gate=f(Et, I, H) * np.float32(0.3), w_up=f(Et, I, H) * np.float32(0.3),
+                          w_down=f(Et, H, I) * np.float32(0.3))
+    if S and not cfg["shared_packed"]:
+        inp.ws_gate, inp.ws_up, inp.ws_down = (f(S, Is, H) * np.float32(0.3),
+                                               f(S, Is, H) * np.float32(0.3),
+                                               f(S, H, Is) * np.float32(0.3))
+    return inp
+
+
+def _loop_swiglu_mlp(x, wg, wu, wd, act):
+    """Textbook SwiGLU MLP with explicit loops over the [out, in] layout."""
+    I, H = wg.shape
+    y = np.zeros(H)
+    hid = np.zeros(I)
+    for i in range(I):
+        gs = 0.0
+        us = 0.0
+        for h in range(H):
+            gs += float(wg[i, h]) * float(x[h])
+            us += float(wu[i, h]) * float(x[h])
+        hid[i] = act(gs, us)
+    for o in range(H):
+        acc = 0.0
+        for i in range(I):
+            acc += float(wd[o, i]) * hid[i]
+        y[o] = acc
+    return y
+
+
+def _py_silu(g, u):
+    return g / (1.0 + math.exp(-g)) * u
+
+
+def test_single_expert_is_scaled_mlp():
+    cfg = _tiny_cfg(num_experts=1, num_experts_per_tok=1, num_shared_experts=0,
+                    route_scale=2.826)
+    inp = _tiny_inputs(cfg)
+    res = O.moe_forward(inp, cfg)
+    for t in range(inp.x.shape[0]):
+        ref = 2.826 * _loop_swiglu_mlp(inp.x[t], inp.w_gate[0], inp.w_up[0], inp.w_down[0], _py_silu)
+        assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_all_experts_unnormalised_is_dense_mixture():
+    cfg = _tiny_cfg(num_experts_per_tok=3, route_norm=0)
+    inp = _tiny_inputs(cfg)
+    inp.expert_bias[:] = 0
+    res = O.moe_forward(inp, cfg)
+    for t in range(inp.x.shape[0]):
+        ref = _loop_swiglu_mlp(inp.x[t], inp.ws_gate[0], inp.ws_up[0], inp.ws_down[0], _py_silu)
+        for e in range(3):
+            logit = sum(float(inp.x[t, h]) * float(inp.w_router[e, h]) for h in range(8))
+            ref = ref + (1.0 / (1.0 + math.exp(-logit))) * _loop_swiglu_mlp(
+                inp.x[t], inp.w_gate[e], inp.w_up[e], inp.w_down[e], _py_silu)
+        assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_packed_shared_equals_separate():
+    cfg_p = _tiny_cfg(shared_packed=1, route_scale=2.0, hidden_act="swigluoai")
+    inp_p = _tiny_inputs(cfg_p)
+    cfg_s = dict(cfg_p, shared_packed=0)
+    E = cfg_p["num_experts"]
+    inp_s = synth.MoeInputs(cfg=cfg_s, x=inp_p.x, w_router=inp_p.w_router,
+                            expert_bias=inp_p.expert_bias,
+                            w_gate=inp_p.w_gate[:E], w_up=inp_p.w_up[:E], w_down=inp_p.w_down[:E],
+                            ws_gate=inp_p.w_gate[E:], ws_up=inp_p.w_up[E:], ws_down=inp_p.w_down[E:])
+    a = O.moe_forward(inp_p, cfg_p)
+    b = O.moe_forward(inp_s, cfg_s)
+    assert np.array_equal(a["idx"], b["idx"]) and np.all(a["idx"] < E)
+    assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
+
+
+def test_two_shared_equal_one_concatenated():
+    cfg2 = _tiny_cfg(num_shared_experts=2)
+    inp2 = _tiny_inputs(cfg2)
+    cfg1 = dict(cfg2, num_shared_experts=1, shared_intermediate_size=8)
+    inp1 = synth.MoeInputs(cfg=cfg1, x=inp2.x, w_router=inp2.w_router,
+                           expert_bias=inp2.expert_bias, w_gate=inp2.w_gate,
+                           w_up=inp2.w_up, w_down=inp2.w_down,
+                           ws_gate=inp2.ws_gate.reshape(1, 8, 8),
+                           ws_up=inp2.ws_up.reshape(1, 8, 8),
+                           ws_down=np.concatenate([inp2.ws_down[0], inp2.ws_down[1]], axis=1)[None])
+    a = O.moe_forward(inp2, cfg2)
+    b = O.moe_forward(inp1, cfg1)
+    assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
+
+
+def test_tokens_subset_matches_full():
+    cfg = _tiny_cfg(num_experts=6, num_experts_per_tok=2, hidden_act="swigluoai")
+    inp = _tiny_inputs(cfg, T=9)
+    full = O.moe_forward(inp, cfg, want_hidden=True)
+    sub = O.moe_forward_tokens(inp, cfg, [0, 4, 8])
+    assert np.array_equal(sub["idx"], full["idx"][[0, 4, 8]])
+    assert np.allclose(sub["out"], full["out"][[0, 4, 8]], rtol=1e-13, atol=1e-13)
+
+
+def test_loop_layer_matches_vectorised():
+    """Whole tiny layer through explicit per-token loops."""
+    cfg = _tiny_cfg(num_experts=5, num_experts_per_tok=2, route_scale=1.5)
+    inp = _tiny_inputs(cfg, T=6)
+    res = O.moe_forward(inp, cfg)
+    for t in range(6):
+        logits = [sum(float(inp.x[t, h]) * float(inp.w_router[e, h]) for h in range(8)) for e in range(5)]
+        s = [1.0 / (1.0 + math.exp(-v)) for v in logits]
+        key = [s[e] + float(inp.expert_bias[e]) for e in range(5)]
+        chosen = sorted(range(5), key=lambda e: (-key[e], e))[:2]
+        den = sum(s[e] for e in chosen)
+        y = _loop_swiglu_mlp(inp.x[t], inp.ws_gate[0], inp.ws_up[0], inp.ws_down[0], _py_silu)
+        for e in chosen:
+            y = y + 1.5 * s[e] / den * _loop_swiglu_mlp(inp.x[t], inp.w_gate[e], inp.w_up[e], inp.w_down[e], _py_silu)
+        assert res["idx"][t].tolist() == chosen
+        assert np.allclose(res["out"][t], y, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the workload table agrees with the values the pages print
+
+def test_workloads_use_page_constants():
+    pc = _gold("page_constants.json")
+    c2 = synth.CONFIGS["afmoe_default_T4096"]
+    d = pc["afmoe_defaults"]
+    for key in ("hidden_size", "moe_intermediate_size", "num_experts",
+                "num_experts_per_tok", "num_shared_experts", "route_scale", "hidden_act"):
+        assert c2[key] == d[key], key
+    assert c2["w_std"] == d["initializer_range"]
+    c3 = synth.CONFIGS["trinity_nano_prefill_T8192"]
+    for key in ("hidden_size", "num_experts", "route_scale", "score_func"):
+        assert c3[key] == pc["trinity"][key], key
+    c5 = synth.CONFIGS["minimax_m3_prefill_T8192"]
+    m3 = pc["minimax_m3"]
+    assert (c5["hidden_size"], c5["num_experts"], c5["num_experts_per_tok"]) == (
+        m3["hidden_size"], m3["num_experts"], m3["num_experts_per_tok"])
+    assert c5["route_scale"] == m3["routed_scaling_factor"]
+    assert c5["shared_intermediate_size"] == m3["shared_intermediate_size"]
+    assert c5["shared_packed"] == 1 and c5["num_experts"] == m3["shared_slot"]
+    assert (c5["act_alpha"], c5["act_limit"], c5["act_beta"]) == (m3["alpha"], m3["limit"], m3["beta"])
