@@ -1,0 +1,247 @@
+"""Benchmark of the sparse-MoE feed-forward layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer (router GEMM, routing, grouping,
+gate/up + activation, down + combine, output cast) over one batch of seeded
+synthetic inputs that are resident in HBM before timing starts. The stage
+entry points are called in order on one stream with HIP events around each
+call; the K timed steps are bracketed by device synchronisation.
+
+Prints ONE JSON line: tokens/s of the layer, its TFLOP/s (fraction of bf16
+MFMA peak) and GB/s (fraction of HBM peak), the roofline of the dominant
+kernel, and the float64 CPU oracle timed on a bounded sample of the same
+workload (a baseline, not the target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE-layer tokens/s + % bf16 MFMA peak (prefill) / % HBM GB/s (decode) "
+          "on 1 MI355X")
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "afmoe_default_T4096"
+
+
+def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
+    """FLOPs and HBM bytes the layer must move (not padded or re-read work).
+    F = T*(2HE + 6kHI + 6 S H Is); B = touched experts' weights + shared
+    weights + router + x + out."""
+    H, E, k = cfg["hidden_size"], cfg["num_experts"], cfg["num_experts_per_tok"]
+    I, S = cfg["moe_intermediate_size"], cfg["num_shared_experts"]
+    Is = cfg["shared_intermediate_size"] or I
+    bw = 2 if cfg["dtype"] == "bf16" else 4
+    flops = T * (2 * H * E + 6 * k * H * I + 6 * S * H * Is)
+    touched = E if idx is None else int(np.unique(idx).size)
+    bytes_ = touched * 3 * H * I * bw + S * 3 * H * Is * bw + 4 * E * H + 2 * T * H * bw + 4 * E
+    gate_up_flops = 4 * T * H * (k * I + S * Is)
+    gate_up_bytes = touched * 2 * H * I * bw + S * 2 * H * Is * bw + T * H * bw \
+        + (T * k * I + T * S * Is) * bw
+    return dict(flops=flops, bytes=bytes_, touched=touched, gate_up_flops=gate_up_flops,
+                gate_up_bytes=gate_up_bytes)
+
+
+def traffic_from_profile(kernel: str, src_sha: str, units: float):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
+    if the summary is missing or was taken on another version of the source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != src_sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
+    """The float64 oracle (as it stands) on the first `sample_tokens` tokens."""
+    from oracle import moe_oracle as O
+    from workloads import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sub = synth.MoeInputs(cfg=dict(cfg, T=sample_tokens), x=inp.x[:sample_tokens],
+                          w_router=inp.w_router, expert_bias=inp.expert_bias,
+                          w_gate=inp.w_gate, w_up=inp.w_up, w_down=inp.w_down,
+                          ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down)
+    t0 = time.perf_counter()
+    O.moe_forward(sub, cfg)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, whole layer on the first {sample_tokens} of "
+                      f"{cfg['T']} tokens of {name} ({dt:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens for the CPU oracle baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is described in the design notes, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_moe_transformer_amd as moe
+    from workloads import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    cfg = synth.config(args.workload)
+    keys = synth.layer_keys(cfg)
+    T = cfg["T"]
+    E, k, H, I = cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"], \
+        cfg["moe_intermediate_size"]
+    S = cfg["num_shared_experts"]
+    Is = cfg["shared_intermediate_size"] or I
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    inp = synth.generate(cfg)
+    d = moe.to_device
+    x, wr, b = d(inp.x), d(inp.w_router), d(inp.expert_bias)
+    wg, wu, wd = d(inp.w_gate), d(inp.w_up), d(inp.w_down)
+    sg, su, sd = d(inp.ws_gate), d(inp.ws_up), d(inp.ws_down)
+    dt = moe.torch_dtype(keys)
+    dev = x.device
+    ws = moe.alloc_workspace(keys, T)
+    f32, i32 = torch.float32, torch.int32
+    logits = torch.empty(T * E, dtype=f32, device=dev)
+    idx = torch.empty(T * k, dtype=i32, device=dev)
+    w = torch.empty(T * k, dtype=f32, device=dev)
+    offs = torch.empty(E + 1, dtype=i32, device=dev)
+    sr = torch.empty(T * k, dtype=i32, device=dev)
+    rp = torch.empty(T * k, dtype=i32, device=dev)
+    h = torch.empty(T * k * I, dtype=dt, device=dev)
+    hs = torch.empty(T * S * Is, dtype=dt, device=dev) if S else None
+    acc = torch.empty(T * H, dtype=f32, device=dev)
+    out = torch.empty(T * H, dtype=dt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    stages = ["router", "route", "permute", "gate_up", "down", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+
+    def step(events=None):
+        rec = (lambda i: events[i].record(stream)) if events else (lambda i: None)
+        rec(0)
+        moe.moe_router_logits(keys, T, x, wr, logits, stream)
+        rec(1)
+        moe.moe_route(keys, T, logits, b, idx, w, None, stream)
+        rec(2)
+        moe.moe_permute(keys, T, idx, offs, sr, rp, ws, stream)
+        rec(3)
+        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream)
+        rec(4)
+        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, None, ws, stream)
+        rec(5)
+        moe.moe_combine(keys, T, acc, None, rp, w, out, stream)
+        rec(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(stages)}
+
+    # the same layer through the single entry point, for a cross-check
+    for _ in range(2):
+        moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
+                              out, 0, ws, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
+                              out, 0, ws, stream)
+    torch.cuda.synchronize()
+    ms_lf = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    idx_h = idx.view(T, k).cpu().numpy()
+    alg = algorithmic(cfg, T, idx_h)
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+    peak_mm = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_MFMA_TFLOPS
+    ai = alg["flops"] / alg["bytes"]
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+    # roofline of the dominant kernel: the grouped gate/up GEMM + activation
+    gu_ms = stage_ms["gate_up"]
+    src = open(os.path.join(ROOT, "sparse_moe_transformer_amd", "csrc", "moe_gemm.hip"), "rb").read()
+    sha = hashlib.sha256(src).hexdigest()
+    gu_ai = alg["gate_up_flops"] / alg["gate_up_bytes"]
+    if gu_ai >= ridge:
+        roof = {"bound": "mfma", "achieved": alg["gate_up_flops"] / (gu_ms * 1e-3) / 1e12,
+                "peak": peak_mm, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profile("moe_gate_up_kernel", sha, 1.0)
+    roof["kernel"] = "moe_gate_up_kernel"
+    roof["ms_per_launch"] = gu_ms
+
+    sample = args.cpu_sample
+    if sample is None:
+        sample = T
+    cpu = cpu_baseline(args.workload, cfg, inp, sample) if sample > 0 else None
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes of the workload, random weights)",
+        "config": {"workload": args.workload, "tokens": T, "hidden_size": H, "num_experts": E,
+                   "num_experts_per_tok": k, "moe_intermediate_size": I,
+                   "num_shared_experts": S, "shared_intermediate_size": Is,
+                   "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"]},
+        "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
+                  "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],
+                  "bytes": alg["bytes"], "arith_intensity": ai,
+                  "bound": "mfma" if ai >= ridge else "hbm",
+                  "touched_experts": alg["touched"], "stage_ms": stage_ms,
+                  "ms_per_step_layer_forward": ms_lf},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

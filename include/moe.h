@@ -1,0 +1,194 @@
+/* moe.h - C ABI of libmoe.so, the sparse mixture-of-experts feed-forward
+ * layer of AFMoE (Arcee Trinity) and MiniMax-M3 on one AMD MI355X (gfx950).
+ *
+ * The layer (pages: mlxcel issue #845 "add Arcee AFMoE", "Routing detail" and
+ * "Checkpoint weight layout"; HF Transformers doc "AFMoE", AfmoeConfig and the
+ * expert-routing / shared-expert sections; mlxcel issue #763 "add MiniMax-M3",
+ * "Architecture specification", MoE and Activation bullets):
+ *
+ *   L    = x . W_r^T                         router logits, fp32
+ *   s    = sigmoid(L)                        scores
+ *   idx  = top-k of (s + expert_bias)        bias used for selection only;
+ *                                            ties -> lower expert index;
+ *                                            emitted in that order
+ *   w    = route_scale * s[idx] / sum s[idx] route_norm on (without the
+ *                                            division when off)
+ *   y_e  = W_d[e] . act(W_g[e] . x, W_u[e] . x)
+ *   out  = sum_j w_j * y_{idx_j} + sum_s y_shared_s(x)
+ *
+ * Conventions of every entry point:
+ *  - Pointers are DEVICE pointers unless marked "host". The caller owns all
+ *    memory. The library allocates nothing and keeps no state between calls;
+ *    work happens asynchronously on the given stream.
+ *  - Tensors are row-major and dense. Weights use the [out, in] layout of a
+ *    linear layer: gate/up [E_tot, I, H], down [E_tot, H, I], where
+ *    E_tot = E + 1 when the shared expert is packed as slot E, else E.
+ *  - "dtype" tensors (x, expert weights, h, out) are bf16 or fp32 as
+ *    moe_config.dtype says. The router weight and logits are always fp32.
+ *  - All argument checks run on the host before any launch; a call that
+ *    returns an error has launched nothing. Faults inside kernels surface at
+ *    the caller's next synchronisation. Values are not checked (no NaN/Inf
+ *    scan).
+ *  - T == 0 returns MOE_OK and launches nothing.
+ *  - Calls are reentrant. Concurrent calls need distinct workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t; NULL = null stream */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad size, null required pointer, bad flag */
+  MOE_ERR_UNSUPPORTED = 2, /* valid config outside what the kernels cover */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the query reports */
+  MOE_ERR_HIP = 4          /* a HIP launch or API call failed */
+} moe_status;
+
+/* Scoring function: sigmoid (mlxcel #845 "Routing detail"); the HF doc also
+ * names softmax scoring, which is not implemented (MOE_ERR_UNSUPPORTED). */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
+
+/* Expert activation: SiLU-SwiGLU (HF "AFMoE" doc, hidden_act "silu") or
+ * clamp-SwiGLU (mlxcel #763 Activation bullet, hidden_act "swigluoai"):
+ *   silu:      a = g * sigmoid(g) * u
+ *   swigluoai: a = g' * sigmoid(alpha*g') * (u' + beta),
+ *              g' = min(g, limit), u' = clamp(u, -limit, limit)
+ * with g the gate projection and u the up projection. */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLUOAI = 1 } moe_hidden_act;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer configuration (host struct, passed by const pointer). Field names
+ * follow the pages' config keys. */
+typedef struct {
+  int32_t hidden_size;              /* H; multiple of 64                         */
+  int32_t num_experts;              /* E routed experts, 1..1024                 */
+  int32_t num_experts_per_tok;      /* k, 1..min(E, 32)                          */
+  int32_t num_shared_experts;       /* S >= 0, always-on experts                 */
+  int32_t moe_intermediate_size;    /* I; multiple of 64                         */
+  int32_t shared_intermediate_size; /* I_s; 0 means I; multiple of 64            */
+  int32_t shared_packed;            /* 1: the shared expert is slot E of the
+                                       stacked tensors, with fixed weight 1.0;
+                                       needs S == 1 and I_s == I (mlxcel #763)   */
+  int32_t score_func;               /* moe_score_func                            */
+  int32_t route_norm;               /* 0/1: renormalise the k gathered scores    */
+  float route_scale;                /* route_scale / routed_scaling_factor;
+                                       multiplies routed weights only            */
+  int32_t hidden_act;               /* moe_hidden_act                            */
+  float act_alpha;                  /* swigluoai alpha (1.702)                   */
+  float act_limit;                  /* swigluoai limit (7.0)                     */
+  float act_beta;                   /* swigluoai beta  (1.0)                     */
+  int32_t dtype;                    /* moe_dtype of x, expert weights, h, out    */
+} moe_config;
+
+/* Bytes of device workspace that moe_layer_forward (and every stage entry
+ * point) needs for T tokens. bytes: host pointer. The workspace must be
+ * 256-byte aligned. */
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
+
+/* Router GEMM: logits[T,E] (fp32) = x[T,H] . w_router[E,H]^T (fp32 weights),
+ * fp32 accumulation. The router is a bias-free linear map (mlxcel #845
+ * "Checkpoint weight layout": mlp.router.gate). */
+moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
+                             const float* w_router, float* logits,
+                             moe_stream_t stream);
+
+/* Routing (mlxcel #845 "Routing detail"; mlxcel #763 MoE bullet): sigmoid
+ * scores, selection key s + expert_bias formed in fp64, top-k by (key desc,
+ * index asc), weights from the unbiased scores, route_norm, route_scale.
+ *   logits      [T,E] fp32
+ *   expert_bias [E] fp32, or NULL (no bias)
+ *   topk_idx    [T,k] int32 out, in selection order
+ *   topk_w      [T,k] fp32 out
+ *   expert_counts [E] int32 out or NULL: number of rows routed to each expert
+ *                 (the array is cleared and filled by this call). */
+moe_status moe_route(const moe_config* cfg, int64_t T, const float* logits,
+                     const float* expert_bias, int32_t* topk_idx,
+                     float* topk_w, int32_t* expert_counts,
+                     moe_stream_t stream);
+
+/* Grouping of the T*k (token, slot) rows r = t*k + j by expert: a stable
+ * counting sort.
+ *   expert_offsets [E+1] out: exclusive scan of the per-expert row counts
+ *   sorted_rows    [T*k] out: rows of expert 0 in ascending r, then expert 1..
+ *   row_pos        [T*k] out: inverse, row_pos[sorted_rows[p]] = p
+ *   ws, ws_bytes: workspace of at least moe_workspace_size bytes. */
+moe_status moe_permute(const moe_config* cfg, int64_t T,
+                       const int32_t* topk_idx, int32_t* expert_offsets,
+                       int32_t* sorted_rows, int32_t* row_pos, void* ws,
+                       size_t ws_bytes, moe_stream_t stream);
+
+/* Grouped gate/up projections with the activation fused (stacked expert
+ * tensors: mlxcel #845 "Checkpoint weight layout"):
+ *   h[p, :]        = act(x[t] . W_g[e]^T, x[t] . W_u[e]^T) for the p-th
+ *                    sorted row (t = sorted_rows[p] / k, e its expert)
+ *   h_shared[t, s*I_s:(s+1)*I_s] = act(x[t] . Ws_g[s]^T, x[t] . Ws_u[s]^T)
+ *   x [T,H]; w_gate, w_up [E_tot,I,H]; ws_gate, ws_up [S,I_s,H] (NULL when
+ *   S == 0 or the shared expert is packed: then slot E of w_gate/w_up is
+ *   used); h [T*k, I] out; h_shared [T, S*I_s] out (NULL iff S == 0). */
+moe_status moe_grouped_gate_up_swiglu(
+    const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
+    const void* w_up, const void* ws_gate, const void* ws_up,
+    const int32_t* expert_offsets, const int32_t* sorted_rows, void* h,
+    void* h_shared, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Grouped down projection with the combine:
+ *   acc[t, :]  = sum_s h_shared[t, s] . Ws_d[s]^T          (stored; zeros
+ *                                                            when S == 0)
+ *   then for every sorted row p (row r = sorted_rows[p], t = r / k):
+ *     y_perm == NULL:  acc[t, :] += topk_w[r] * (h[p] . W_d[e]^T)
+ *                      (fp32 atomics; summation order varies run to run)
+ *     y_perm != NULL:  y_perm[p, :] = h[p] . W_d[e]^T   (dtype, unweighted;
+ *                      moe_combine then sums in a fixed order)
+ *   h [T*k, I]; w_down [E_tot,H,I]; h_shared [T,S*I_s]; ws_down [S,H,I_s] or
+ *   NULL (packed or S == 0); topk_w [T,k]; acc [T,H] fp32 out. The shared
+ *   experts carry weight exactly 1 and no route_scale (HF "AFMoE" doc:
+ *   route_scale scales the routed experts; mlxcel #763: fixed score 1.0). */
+moe_status moe_grouped_down(const moe_config* cfg, int64_t T, const void* h,
+                            const void* w_down, const void* h_shared,
+                            const void* ws_down, const int32_t* expert_offsets,
+                            const int32_t* sorted_rows, const float* topk_w,
+                            float* acc, void* y_perm, void* ws,
+                            size_t ws_bytes, moe_stream_t stream);
+
+/* Finalise: out[t] = acc[t] (y_perm == NULL), or
+ *           out[t] = acc[t] + sum_j topk_w[t,j] * y_perm[row_pos[t*k+j]]
+ * summed in j order (y_perm != NULL), cast to dtype. out [T,H]. */
+moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
+                       const void* y_perm, const int32_t* row_pos,
+                       const float* topk_w, void* out, moe_stream_t stream);
+
+/* The whole layer: router GEMM, routing, grouping, gate/up + activation,
+ * down + combine, cast.
+ *   x [T,H] dtype; w_router [E,H] fp32; expert_bias [E] fp32 or NULL;
+ *   w_gate, w_up, w_down stacked experts; ws_* separate shared experts or
+ *   NULL; router_logits_in [T,E] or NULL (when given, the router GEMM is
+ *   skipped and these logits are routed); router_logits_out [T,E] or NULL;
+ *   topk_idx_out [T,k] / topk_w_out [T,k] or NULL; out [T,H] dtype.
+ *   deterministic: 0 = fp32 atomic combine, 1 = fixed-order combine. */
+moe_status moe_layer_forward(
+    const moe_config* cfg, int64_t T, const void* x, const float* w_router,
+    const float* expert_bias, const void* w_gate, const void* w_up,
+    const void* w_down, const void* ws_gate, const void* ws_up,
+    const void* ws_down, const float* router_logits_in,
+    float* router_logits_out, int32_t* topk_idx_out, float* topk_w_out,
+    void* out, int32_t deterministic, void* ws, size_t ws_bytes,
+    moe_stream_t stream);
+
+const char* moe_status_string(moe_status s);
+
+/* Library version and the GPU architecture the kernels were built for. */
+const char* moe_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -226,7 +226,8 @@ def moe_forward(inp, cfg: dict, logits: np.ndarray | None = None,
             h[offsets[e]:offsets[e + 1]] = he
         ye = mlp_out(he, as_f64(inp.w_down[e]))
         wr = w.reshape(-1)[rows]
-        np.add.at(out, toks, wr[:, None] * ye)
+        # a token selects an expert at most once, so `toks` has no repeats
+        out[toks] += wr[:, None] * ye
     hs_all = []
     for (wg, wu, wd) in _shared_weights(inp, cfg):
         hs = mlp_hidden(x, wg, wu, act)

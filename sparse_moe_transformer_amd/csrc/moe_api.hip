@@ -1,0 +1,351 @@
+// C ABI of libmoe: argument checks, workspace carving and kernel launches.
+// All checks run before the first launch of a call; nothing here allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+struct Dims {
+  int64_t T;
+  int H, E, k, S, I, Is, packed, dtype;
+  size_t es;  // element size of dtype tensors
+};
+
+constexpr int64_t kMaxTokens = 1 << 24;
+
+moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
+  if (!c || T < 0 || T > kMaxTokens) return MOE_ERR_INVALID_ARG;
+  if (c->hidden_size <= 0 || c->hidden_size % 64) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->num_experts > 1024) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts_per_tok < 1 || c->num_experts_per_tok > c->num_experts ||
+      c->num_experts_per_tok > 32)
+    return MOE_ERR_INVALID_ARG;
+  if (c->num_shared_experts < 0 || c->num_shared_experts > 64) return MOE_ERR_INVALID_ARG;
+  if (c->moe_intermediate_size <= 0 || c->moe_intermediate_size % 64) return MOE_ERR_INVALID_ARG;
+  const int Is = c->shared_intermediate_size == 0 ? c->moe_intermediate_size
+                                                  : c->shared_intermediate_size;
+  if (Is < 0 || Is % 64) return MOE_ERR_INVALID_ARG;
+  if (c->shared_packed != 0 && c->shared_packed != 1) return MOE_ERR_INVALID_ARG;
+  if (c->shared_packed && (c->num_shared_experts != 1 || Is != c->moe_intermediate_size))
+    return MOE_ERR_INVALID_ARG;
+  if (c->score_func != MOE_SCORE_SIGMOID && c->score_func != MOE_SCORE_SOFTMAX)
+    return MOE_ERR_INVALID_ARG;
+  if (c->route_norm != 0 && c->route_norm != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->route_scale)) return MOE_ERR_INVALID_ARG;
+  if (c->hidden_act != MOE_ACT_SILU && c->hidden_act != MOE_ACT_SWIGLUOAI)
+    return MOE_ERR_INVALID_ARG;
+  if (c->hidden_act == MOE_ACT_SWIGLUOAI &&
+      !(std::isfinite(c->act_alpha) && std::isfinite(c->act_limit) && std::isfinite(c->act_beta)))
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
+  if (c->score_func == MOE_SCORE_SOFTMAX) return MOE_ERR_UNSUPPORTED;
+  d->T = T;
+  d->H = c->hidden_size;
+  d->E = c->num_experts;
+  d->k = c->num_experts_per_tok;
+  d->S = c->num_shared_experts;
+  d->I = c->moe_intermediate_size;
+  d->Is = Is;
+  d->packed = c->shared_packed;
+  d->dtype = c->dtype;
+  d->es = c->dtype == MOE_BF16 ? 2 : 4;
+  return MOE_OK;
+}
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Workspace carving (every segment 256-byte aligned).
+struct Ws {
+  float* logits;
+  int32_t* idx;
+  float* w;
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* row_pos;
+  int32_t* local_rank;
+  int32_t* chunk_hist;
+  void* h;
+  void* h_shared;
+  float* acc;
+  void* y_perm;
+  size_t total;
+};
+
+Ws carve(const Dims& d, void* base) {
+  Ws w{};
+  const size_t rows = (size_t)d.T * d.k;
+  const size_t nch = (rows + permute_chunk_rows() - 1) / permute_chunk_rows();
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> void* {
+    void* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  w.logits = (float*)take((size_t)d.T * d.E * 4);
+  w.idx = (int32_t*)take(rows * 4);
+  w.w = (float*)take(rows * 4);
+  w.offsets = (int32_t*)take((size_t)(d.E + 1) * 4);
+  w.sorted_rows = (int32_t*)take(rows * 4);
+  w.row_pos = (int32_t*)take(rows * 4);
+  w.local_rank = (int32_t*)take(rows * 4);
+  w.chunk_hist = (int32_t*)take(nch * d.E * 4);
+  w.h = take(rows * d.I * d.es);
+  w.h_shared = take((size_t)d.T * d.S * d.Is * d.es);
+  w.acc = (float*)take((size_t)d.T * d.H * 4);
+  w.y_perm = take(rows * d.H * d.es);
+  w.total = off;
+  return w;
+}
+
+moe_status check_ws(const Dims& d, const void* ws, size_t ws_bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < carve(d, nullptr).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+inline moe_status hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    moe_status _s = (expr);            \
+    if (_s != MOE_OK) return _s;       \
+  } while (0)
+
+ActParams act_of(const moe_config* c) {
+  return ActParams{c->hidden_act, c->act_alpha, c->act_limit, c->act_beta};
+}
+
+GemmArgs base_args(const moe_config* c, const Dims& d) {
+  GemmArgs g{};
+  g.T = (int)d.T;
+  g.H = d.H;
+  g.I = d.I;
+  g.E = d.E;
+  g.k = d.k;
+  g.S = d.S;
+  g.Is = d.Is;
+  g.act = act_of(c);
+  return g;
+}
+
+const void* shared_slot(const void* stacked, const Dims& d, size_t per_expert_elems) {
+  return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.es;
+}
+
+// --- stages (arguments already checked) ---
+
+moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
+                      const void* w_up, const void* ws_gate, const void* ws_up,
+                      const int32_t* offsets, const int32_t* sorted_rows, void* h,
+                      void* h_shared, hipStream_t st) {
+  GemmArgs g = base_args(c, d);
+  const int BM = gemm_bm();
+  const int64_t rows = d.T * d.k;
+  g.a = x;
+  g.w0 = w_gate;
+  g.w1 = w_up;
+  if (d.packed) {
+    g.ws0 = shared_slot(w_gate, d, (size_t)d.I * d.H);
+    g.ws1 = shared_slot(w_up, d, (size_t)d.I * d.H);
+  } else {
+    g.ws0 = ws_gate;
+    g.ws1 = ws_up;
+  }
+  g.offsets = offsets;
+  g.sorted_rows = sorted_rows;
+  g.out = h;
+  g.out_shared = h_shared;
+  g.mt_routed = (int)((rows + BM - 1) / BM + (rows < d.E ? rows : d.E));
+  g.nt_routed = (d.I + 127) / 128;
+  g.mt_shared = d.S ? (int)((d.T + BM - 1) / BM) : 0;
+  g.nt_shared = d.S ? (d.S * d.Is + 127) / 128 : 0;
+  return hip_ok(launch_gate_up(g, d.dtype, st));
+}
+
+moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void* w_down,
+                   const void* h_shared, const void* ws_down, const int32_t* offsets,
+                   const int32_t* sorted_rows, const float* topk_w, float* acc, void* y_perm,
+                   hipStream_t st) {
+  GemmArgs g = base_args(c, d);
+  const int BM = gemm_bm();
+  const int64_t rows = d.T * d.k;
+  g.offsets = offsets;
+  g.sorted_rows = sorted_rows;
+  g.topk_w = topk_w;
+  g.out = acc;
+  g.y_perm = y_perm;
+  if (d.S) {
+    g.a = h_shared;
+    g.ws0 = d.packed ? shared_slot(w_down, d, (size_t)d.H * d.I) : ws_down;
+    g.mt_shared = (int)((d.T + BM - 1) / BM);
+    g.nt_shared = (d.H + 255) / 256;
+    MOE_TRY(hip_ok(launch_down_shared(g, d.dtype, st)));
+  } else {
+    MOE_TRY(hip_ok(launch_fill_zero(acc, (size_t)d.T * d.H * 4, st)));
+  }
+  g.a = h;
+  g.w0 = w_down;
+  g.mt_routed = (int)((rows + BM - 1) / BM + (rows < d.E ? rows : d.E));
+  g.nt_routed = (d.H + 255) / 256;
+  return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims d;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  *bytes = carve(d, nullptr).total;
+  return MOE_OK;
+}
+
+moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
+                             const float* w_router, float* logits, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  return hip_ok(launch_router_logits(x, w_router, logits, (int)T, d.H, d.E, d.dtype,
+                                     (hipStream_t)stream));
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t T, const float* logits,
+                     const float* expert_bias, int32_t* topk_idx, float* topk_w,
+                     int32_t* expert_counts, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) {
+    if (expert_counts) return hip_ok(launch_fill_zero(expert_counts, (size_t)d.E * 4, (hipStream_t)stream));
+    return MOE_OK;
+  }
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (expert_counts) MOE_TRY(hip_ok(launch_fill_zero(expert_counts, (size_t)d.E * 4, st)));
+  return hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
+                             cfg->route_scale, topk_idx, topk_w, expert_counts, st));
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
+                       int32_t* expert_offsets, int32_t* sorted_rows, int32_t* row_pos,
+                       void* ws, size_t ws_bytes, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return hip_ok(launch_fill_zero(expert_offsets, (size_t)(d.E + 1) * 4, (hipStream_t)stream));
+  if (!topk_idx || !sorted_rows || !row_pos) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  Ws w = carve(d, ws);
+  return hip_ok(launch_permute(topk_idx, (int)(T * d.k), d.E, expert_offsets, sorted_rows,
+                               row_pos, w.local_rank, w.chunk_hist, (hipStream_t)stream));
+}
+
+moe_status moe_grouped_gate_up_swiglu(const moe_config* cfg, int64_t T, const void* x,
+                                      const void* w_gate, const void* w_up, const void* ws_gate,
+                                      const void* ws_up, const int32_t* expert_offsets,
+                                      const int32_t* sorted_rows, void* h, void* h_shared,
+                                      void* ws, size_t ws_bytes, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !expert_offsets || !sorted_rows || !h) return MOE_ERR_INVALID_ARG;
+  if (d.S && !h_shared) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed && (!ws_gate || !ws_up)) return MOE_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;
+  return do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, expert_offsets, sorted_rows, h,
+                    h_shared, (hipStream_t)stream);
+}
+
+moe_status moe_grouped_down(const moe_config* cfg, int64_t T, const void* h, const void* w_down,
+                            const void* h_shared, const void* ws_down,
+                            const int32_t* expert_offsets, const int32_t* sorted_rows,
+                            const float* topk_w, float* acc, void* y_perm, void* ws,
+                            size_t ws_bytes, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) return MOE_OK;
+  if (!h || !w_down || !expert_offsets || !sorted_rows || !acc) return MOE_ERR_INVALID_ARG;
+  if (!y_perm && !topk_w) return MOE_ERR_INVALID_ARG;
+  if (d.S && !h_shared) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed && !ws_down) return MOE_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;
+  return do_down(cfg, d, h, w_down, h_shared, ws_down, expert_offsets, sorted_rows, topk_w, acc,
+                 y_perm, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc, const void* y_perm,
+                       const int32_t* row_pos, const float* topk_w, void* out,
+                       moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) return MOE_OK;
+  if (!acc || !out) return MOE_ERR_INVALID_ARG;
+  if (y_perm && (!row_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return hip_ok(launch_combine(acc, y_perm, row_pos, topk_w, out, (int)T, d.H, d.k, d.dtype,
+                               (hipStream_t)stream));
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
+                             const float* w_router, const float* expert_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, const void* ws_gate,
+                             const void* ws_up, const void* ws_down,
+                             const float* router_logits_in, float* router_logits_out,
+                             int32_t* topk_idx_out, float* topk_w_out, void* out,
+                             int32_t deterministic, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
+  if (!router_logits_in && !w_router) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  Ws w = carve(d, ws);
+  const float* logits = router_logits_in;
+  if (!logits) {
+    float* lo = router_logits_out ? router_logits_out : w.logits;
+    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, (int)T, d.H, d.E, d.dtype, st)));
+    logits = lo;
+  }
+  int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
+  float* tw = topk_w_out ? topk_w_out : w.w;
+  MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
+                              cfg->route_scale, idx, tw, nullptr, st)));
+  MOE_TRY(hip_ok(launch_permute(idx, (int)(T * d.k), d.E, w.offsets, w.sorted_rows, w.row_pos,
+                                w.local_rank, w.chunk_hist, st)));
+  MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,
+                     w.h_shared, st));
+  void* yp = deterministic ? w.y_perm : nullptr;
+  MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, w.offsets, w.sorted_rows, tw, w.acc,
+                  yp, st));
+  return hip_ok(launch_combine(w.acc, yp, w.row_pos, tw, out, (int)T, d.H, d.k, d.dtype, st));
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_build_info(void) { return "libmoe 0.1 gfx950 (bf16/fp32 MFMA)"; }
+
+}  // extern "C"

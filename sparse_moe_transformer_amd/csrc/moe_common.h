@@ -1,0 +1,66 @@
+// Device-side helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (round to nearest, ties to even; inputs here are finite)
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Expert activation on the fp32 accumulators (g = gate projection,
+// u = up projection). silu: g*sigmoid(g)*u. swigluoai: clamp g from above
+// and u on both sides at `limit`, then g*sigmoid(alpha*g)*(u+beta).
+
+struct ActParams {
+  int kind;  // moe_hidden_act
+  float alpha, limit, beta;
+};
+
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return 1.0f / (1.0f + __expf(-z));
+}
+
+__device__ __forceinline__ float act_apply(float g, float u, const ActParams& a) {
+  if (a.kind == MOE_ACT_SWIGLUOAI) {
+    float gc = fminf(g, a.limit);
+    float uc = fminf(fmaxf(u, -a.limit), a.limit);
+    return gc * sigmoid_f32(a.alpha * gc) * (uc + a.beta);
+  }
+  return g * sigmoid_f32(g) * u;
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware block remap. The hardware hands consecutive workgroup ids to the
+// 8 XCDs round-robin; remapping makes a run of consecutive *logical* tiles
+// land on one XCD, so tiles that share weights share that XCD's L2.
+
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  const uint32_t nx = 8;
+  uint32_t per = nblocks / nx;         // full rounds
+  uint32_t rem = nblocks % nx;
+  uint32_t xcd = bid % nx;
+  uint32_t slot = bid / nx;
+  // XCDs [0, rem) own per+1 logical blocks, the rest own per.
+  uint32_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + slot;
+}

@@ -1,0 +1,50 @@
+// Host-visible launch interface of the libmoe kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_common.h"
+
+// Arguments of the grouped expert GEMMs (passed by value to the kernels).
+struct GemmArgs {
+  const void* a;      // activations: x (gate/up), h (routed down), h_shared (shared down)
+  const void* w0;     // gate or down stacked weights [E_tot, ., .]
+  const void* w1;     // up stacked weights
+  const void* ws0;    // shared gate (or shared down) weights
+  const void* ws1;    // shared up weights
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted_rows;  // [T*k]
+  const float* topk_w;         // [T*k]
+  void* out;          // h (gate/up) or acc (down)
+  void* out_shared;   // h_shared (gate/up)
+  void* y_perm;       // unweighted routed rows (fixed-order combine)
+  int T, H, I, E, k, S, Is;
+  int mt_routed, nt_routed, mt_shared, nt_shared;
+  ActParams act;
+};
+
+size_t gemm_lds_bytes(int E);
+int gemm_bm();
+hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st);
+hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
+hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
+
+hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
+                                int H, int E, int dtype, hipStream_t st);
+
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
+                        int route_norm, float route_scale, int32_t* idx, float* w,
+                        int32_t* counts, hipStream_t st);
+
+// permutation scratch: chunk histograms and per-row ranks
+int permute_chunk_rows();
+hipError_t launch_permute(const int32_t* idx, int rows, int E, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_pos, int32_t* local_rank,
+                          int32_t* chunk_hist, hipStream_t st);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+hipError_t launch_combine(const float* acc, const void* y_perm, const int32_t* row_pos,
+                          const float* topk_w, void* out, int T, int H, int k, int dtype,
+                          hipStream_t st);

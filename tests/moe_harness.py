@@ -1,0 +1,83 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the layer through
+the C ABI, and compare with the float64 oracle at the layer's bar
+(bf16: max|err| <= 2e-2 * max|ref|; fp32: max|err| <= 1e-4 * max|ref|)."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+import sparse_moe_transformer_amd as moe
+from workloads import synth
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def custom(**kw):
+    """A small workload dict (for edge cases) in the generator's format."""
+    base = dict(T=64, hidden_size=256, num_experts=8, num_experts_per_tok=2,
+                moe_intermediate_size=128, num_shared_experts=1,
+                shared_intermediate_size=0, dtype="bf16", bias_limit=0.05)
+    base.update(kw)
+    c = synth._cfg(**base)
+    c["name"] = kw.get("name", "custom")
+    return c
+
+
+class Dev:
+    """Inputs of one workload on the GPU (torch tensors)."""
+
+    def __init__(self, inp: synth.MoeInputs, device="cuda"):
+        self.inp = inp
+        self.cfg = inp.cfg
+        self.keys = synth.layer_keys(inp.cfg)
+        self.T = inp.x.shape[0]
+        t = moe.to_device
+        self.x = t(inp.x, device)
+        self.w_router = t(inp.w_router, device)
+        self.expert_bias = t(inp.expert_bias, device)
+        self.w_gate = t(inp.w_gate, device)
+        self.w_up = t(inp.w_up, device)
+        self.w_down = t(inp.w_down, device)
+        self.ws_gate = t(inp.ws_gate, device)
+        self.ws_up = t(inp.ws_up, device)
+        self.ws_down = t(inp.ws_down, device)
+        self.ws = moe.alloc_workspace(self.keys, self.T, device)
+
+    def forward(self, deterministic=0, logits_in=None, want_logits=True):
+        import torch
+        T, c = self.T, self.keys
+        E, k, H = c["num_experts"], c["num_experts_per_tok"], c["hidden_size"]
+        dev = self.x.device
+        logits = torch.empty(T * E, dtype=torch.float32, device=dev) if want_logits else None
+        idx = torch.empty(T * k, dtype=torch.int32, device=dev)
+        w = torch.empty(T * k, dtype=torch.float32, device=dev)
+        out = torch.empty(T * H, dtype=moe.torch_dtype(c), device=dev)
+        moe.moe_layer_forward(c, T, self.x, self.w_router, self.expert_bias, self.w_gate,
+                              self.w_up, self.w_down, self.ws_gate, self.ws_up, self.ws_down,
+                              logits_in, logits, idx, w, out, deterministic, self.ws)
+        torch.cuda.synchronize()
+        res = dict(idx=idx.view(T, k).cpu().numpy(), w=w.view(T, k).cpu().numpy(),
+                   out=out.view(T, H).float().cpu().numpy().astype(np.float64))
+        if want_logits:
+            res["logits"] = logits.view(T, E).cpu().numpy()
+        return res
+
+
+@functools.lru_cache(maxsize=2)
+def generated(name: str, T: int | None = None):
+    say(f"[gen] {name} T={T}")
+    return synth.generate(synth.config(name), T=T)
+
+
+def rel_err(a, ref):
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return float(np.max(np.abs(a - ref))) / (scale if scale > 0 else 1.0)
