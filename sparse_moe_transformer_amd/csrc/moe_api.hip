@@ -167,6 +167,8 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
   g.nt_routed = (d.I + 127) / 128;
   g.mt_shared = d.S ? (int)((d.T + BM - 1) / BM) : 0;
   g.nt_shared = d.S ? (d.S * d.Is + 127) / 128 : 0;
+  g.gm_routed = 8;
+  g.gm_shared = 8;
   return hip_ok(launch_gate_up(g, d.dtype, st));
 }
 
@@ -187,6 +189,7 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
     g.ws0 = d.packed ? shared_slot(w_down, d, (size_t)d.H * d.I) : ws_down;
     g.mt_shared = (int)((d.T + BM - 1) / BM);
     g.nt_shared = (d.H + 255) / 256;
+    g.gm_shared = 4;
     MOE_TRY(hip_ok(launch_down_shared(g, d.dtype, st)));
   } else {
     MOE_TRY(hip_ok(launch_fill_zero(acc, (size_t)d.T * d.H * 4, st)));
@@ -195,6 +198,7 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   g.w0 = w_down;
   g.mt_routed = (int)((rows + BM - 1) / BM + (rows < d.E ? rows : d.E));
   g.nt_routed = (d.H + 255) / 256;
+  g.gm_routed = 4;
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 

@@ -21,6 +21,7 @@ struct GemmArgs {
   void* y_perm;       // unweighted routed rows (fixed-order combine)
   int T, H, I, E, k, S, Is;
   int mt_routed, nt_routed, mt_shared, nt_shared;
+  int gm_routed, gm_shared;  // m-slots per group of the tile order
   ActParams act;
 };
 

@@ -41,16 +41,22 @@ __global__ void __launch_bounds__(CH) permute_chunk_kernel(const int32_t* __rest
 __global__ void __launch_bounds__(1024) permute_scan_kernel(int nchunks, int E,
                                                             int32_t* __restrict__ chunk_hist,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int tot[1024];
   __shared__ int wsum[16];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      int* p = chunk_hist + (size_t)c * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    // 16 independent loads in flight per round trip
+    constexpr int B = 16;
+    for (int c0 = 0; c0 < nchunks; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        v[u] = (c0 + u < nchunks) ? chunk_hist[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (c0 + u < nchunks) chunk_hist[(size_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
   }
   // exclusive scan of run over experts (E <= 1024)
@@ -75,7 +81,6 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(int nchunks, int E,
   }
   __syncthreads();
   const int excl = incl - run + wsum[wave];
-  tot[threadIdx.x] = excl;
   if (e < E) offsets[e] = excl;
   if (e == E - 1) offsets[E] = excl + run;
 }
