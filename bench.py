@@ -148,7 +148,7 @@ def main():
     def step(events=None):
         rec = (lambda i: events[i].record(stream)) if events else (lambda i: None)
         rec(0)
-        moe.moe_router_logits(keys, T, x, wr, logits, stream)
+        moe.moe_router_logits(keys, T, x, wr, logits, ws, stream)
         rec(1)
         moe.moe_route(keys, T, logits, b, idx, w, None, stream)
         rec(2)

@@ -96,10 +96,12 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
 
 /* Router GEMM: logits[T,E] (fp32) = x[T,H] . w_router[E,H]^T (fp32 weights),
  * fp32 accumulation. The router is a bias-free linear map (mlxcel #845
- * "Checkpoint weight layout": mlp.router.gate). */
+ * "Checkpoint weight layout": mlp.router.gate). The result does not depend on
+ * timing, and identical router rows give bitwise identical logit columns.
+ * ws, ws_bytes: workspace of at least moe_workspace_size bytes (scratch). */
 moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
-                             const float* w_router, float* logits,
-                             moe_stream_t stream);
+                             const float* w_router, float* logits, void* ws,
+                             size_t ws_bytes, moe_stream_t stream);
 
 /* Routing (mlxcel #845 "Routing detail"; mlxcel #763 MoE bullet): sigmoid
  * scores, selection key s + expert_bias formed in fp64, top-k by (key desc,

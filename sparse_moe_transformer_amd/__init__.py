@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
         i64, sz, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
         sig = {
             "moe_workspace_size": [cp, i64, ctypes.POINTER(sz)],
-            "moe_router_logits": [cp, i64, _vp, _vp, _vp, _vp],
+            "moe_router_logits": [cp, i64, _vp, _vp, _vp, _vp, sz, _vp],
             "moe_route": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
             "moe_permute": [cp, i64, _vp, _vp, _vp, _vp, _vp, sz, _vp],
             "moe_grouped_gate_up_swiglu": [cp, i64] + [_vp] * 9 + [_vp, sz, _vp],
@@ -178,12 +178,12 @@ def moe_workspace_size(cfg, T: int) -> int:
     return n.value
 
 
-def moe_router_logits(cfg, T, x, w_router, logits, stream=None):
+def moe_router_logits(cfg, T, x, w_router, logits, ws, stream=None):
     c = make_config(cfg)
     _need(logits, T * c.num_experts, "logits")
     _need(x, T * c.hidden_size, "x")
     _call("moe_router_logits", ctypes.byref(c), int(T), _p(x), _p(w_router), _p(logits),
-          _stream(stream))
+          _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
 
 
 def moe_route(cfg, T, logits, expert_bias, topk_idx, topk_w, expert_counts=None, stream=None):

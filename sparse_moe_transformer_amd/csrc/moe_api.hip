@@ -63,6 +63,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Workspace carving (every segment 256-byte aligned).
 struct Ws {
+  void* router;  // router GEMM scratch
   float* logits;
   int32_t* idx;
   float* w;
@@ -89,6 +90,7 @@ Ws carve(const Dims& d, void* base) {
     off += align256(bytes);
     return p;
   };
+  w.router = take(router_ws_bytes(d.T, d.E, d.H, d.dtype));
   w.logits = (float*)take((size_t)d.T * d.E * 4);
   w.idx = (int32_t*)take(rows * 4);
   w.w = (float*)take(rows * 4);
@@ -215,12 +217,15 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
 }
 
 moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
-                             const float* w_router, float* logits, moe_stream_t stream) {
+                             const float* w_router, float* logits, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
   Dims d;
   MOE_TRY(check_cfg(cfg, T, &d));
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
-  return hip_ok(launch_router_logits(x, w_router, logits, (int)T, d.H, d.E, d.dtype,
+  MOE_TRY(check_ws(d, ws, ws_bytes));
+  Ws w = carve(d, ws);
+  return hip_ok(launch_router_logits(x, w_router, logits, (int)T, d.H, d.E, d.dtype, w.router,
                                      (hipStream_t)stream));
 }
 
@@ -322,7 +327,7 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   const float* logits = router_logits_in;
   if (!logits) {
     float* lo = router_logits_out ? router_logits_out : w.logits;
-    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, (int)T, d.H, d.E, d.dtype, st)));
+    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, (int)T, d.H, d.E, d.dtype, w.router, st)));
     logits = lo;
   }
   int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;

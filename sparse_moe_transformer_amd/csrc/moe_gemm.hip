@@ -132,6 +132,19 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][mb], fb[s & 1][nb],
                                                                 acc[mb][nb], 0, 0, 0);
     }
+    // schedule: the 6 fragment reads of sub-step s+1 are interleaved with the
+    // 8 MFMAs of sub-step s, so LDS latency hides behind matrix work
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // reads of sub-step 0
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   } else {
     // fp32: lane group q holds k = 16q..16q+15 (chunks 4q..4q+3); MFMA v of
     // the 16 32x32x2 steps takes slot v of both operands.

@@ -31,8 +31,11 @@ hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
 
+// router GEMM scratch: bf16 split planes of the router weight + K-chunk partials
+int router_kchunks(int64_t T, int E, int H, int dtype);
+size_t router_ws_bytes(int64_t T, int E, int H, int dtype);
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
-                                int H, int E, int dtype, hipStream_t st);
+                                int H, int E, int dtype, void* ws, hipStream_t st);
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int route_norm, float route_scale, int32_t* idx, float* w,

@@ -1,0 +1,85 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+that include/moe.h declares, and rejects bad arguments on the host before any
+launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_transformer_amd as moe
+from workloads import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = _declared()
+    assert "moe_layer_forward" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.ENTRY_POINTS)
+    assert "gfx950" in moe.moe_build_info()
+
+
+def _cfg(**kw):
+    c = synth.layer_keys(synth.config("afmoe_default_T4096"))
+    c.update(kw)
+    return c
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden_size=100), dict(hidden_size=0), dict(num_experts=0), dict(num_experts=2000),
+    dict(num_experts_per_tok=0), dict(num_experts_per_tok=65), dict(num_experts=8, num_experts_per_tok=9),
+    dict(moe_intermediate_size=1400), dict(shared_intermediate_size=100),
+    dict(shared_packed=1),                       # needs S == 1 and I_s == I
+    dict(shared_packed=2), dict(route_norm=3), dict(hidden_act=7), dict(dtype=5),
+    dict(route_scale=float("nan")),
+])
+def test_invalid_config_rejected(bad):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(_cfg(**bad), 16)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_softmax_is_unsupported():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(_cfg(score_func="softmax"), 16)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_grows_with_tokens():
+    c = _cfg()
+    sizes = [moe.moe_workspace_size(c, t) for t in (1, 64, 4096, 8192)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:]))
+    assert all(s % 256 == 0 for s in sizes)
+
+
+def _raw_forward(cfg, T, ptr=0x1000, ws=0x100000, ws_bytes=1 << 40, x=True):
+    """moe_layer_forward with fake (never dereferenced) device addresses."""
+    L = moe.lib()
+    c = moe.make_config(cfg)
+    p = ptr if x else None
+    return L.moe_layer_forward(ctypes.byref(c), T, p, ptr, None, ptr, ptr, ptr, ptr, ptr, ptr,
+                               None, None, None, None, ptr, 0, ws, ws_bytes, None)
+
+
+def test_host_checks_run_before_any_launch():
+    c = _cfg()
+    assert _raw_forward(c, 0) == moe.MOE_OK                      # T == 0: nothing to do
+    assert _raw_forward(c, 8, x=False) == moe.MOE_ERR_INVALID_ARG
+    assert _raw_forward(c, 8, ws_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert _raw_forward(c, 8, ws=0x100010) == moe.MOE_ERR_INVALID_ARG   # misaligned
+    assert _raw_forward(c, -1) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for code in range(5):
+        assert moe.status_string(code).startswith("MOE_")

@@ -1,0 +1,47 @@
+"""The seeded generator: deterministic, per-block streams (a smaller T is a
+prefix of a larger one), bf16 rounding to nearest-even (checked against
+torch's float32 -> bfloat16 conversion), and the skewed workload's stored
+parameters."""
+import numpy as np
+import torch
+
+from workloads import synth
+
+
+def test_generation_is_deterministic_and_prefix_stable():
+    cfg = synth.config("trinity_nano_decode_T32")
+    a = synth.generate(cfg, experts=False)
+    b = synth.generate(cfg, experts=False)
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.w_router, b.w_router)
+    big = synth.generate(cfg, T=300, experts=False)
+    assert np.array_equal(big.x[:32], a.x)
+
+
+def test_bf16_rounding_matches_torch():
+    v = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 37.0
+    v[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]   # exact ties
+    ours = synth.f32_to_bf16_bits(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_value_ranges():
+    cfg = synth.config("tiny_fp32_T64")
+    inp = synth.generate(cfg)
+    assert np.all(np.abs(inp.expert_bias) <= 0.1)
+    assert abs(float(inp.w_gate.std()) - 0.02) < 0.002
+    assert abs(float(inp.x.std()) - 1.0) < 0.05
+
+
+def test_skew_parameters_are_applied():
+    cfg = synth.config("skewed_afmoe_T8192")
+    sk = synth.load_skew(cfg["skew"])
+    base = synth.generate(cfg, T=256, experts=False, apply_skew=False)
+    inp = synth.generate(cfg, T=256, experts=False)
+    a, c = sk["tie_pair"]
+    assert np.array_equal(inp.w_router[c], inp.w_router[a])
+    assert inp.expert_bias[c] == inp.expert_bias[a]
+    hot = np.array(sk["hot_experts"])
+    assert np.all(inp.expert_bias[hot] > base.expert_bias[hot])
+    assert abs(sk["hot_share"] - 0.60) <= 0.01
+    assert 0.03 <= sk["tie_straddle_rate"] <= 0.07
