@@ -97,7 +97,19 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (3 times): the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the layer's multi-GPU sharding is described in the design notes, not built)",
