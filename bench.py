@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--combine", choices=["atomic", "ordered"], default="ordered",
+                    help="down-projection combine: fp32 atomics into the output rows, or "
+                         "per-row expert outputs summed in a fixed order by moe_combine")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -151,6 +154,8 @@ def main():
     hs = torch.empty(T * S * Is, dtype=dt, device=dev) if S else None
     acc = torch.empty(T * H, dtype=f32, device=dev)
     out = torch.empty(T * H, dtype=dt, device=dev)
+    ordered = args.combine == "ordered"
+    yp = torch.empty(T * k * H, dtype=dt, device=dev) if ordered else None
     stream = torch.cuda.current_stream()
 
     stages = ["router", "route", "permute", "gate_up", "down", "combine"]
@@ -168,9 +173,9 @@ def main():
         rec(3)
         moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream)
         rec(4)
-        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, None, ws, stream)
+        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, stream)
         rec(5)
-        moe.moe_combine(keys, T, acc, None, rp, w, out, stream)
+        moe.moe_combine(keys, T, acc, yp, rp, w, out, stream)
         rec(6)
 
     for _ in range(args.warmup):
@@ -188,12 +193,12 @@ def main():
     # the same layer through the single entry point, for a cross-check
     for _ in range(2):
         moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
-                              out, 0, ws, stream)
+                              out, int(ordered), ws, stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
         moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
-                              out, 0, ws, stream)
+                              out, int(ordered), ws, stream)
     torch.cuda.synchronize()
     ms_lf = (time.perf_counter() - t1) * 1e3 / args.steps
 
@@ -242,7 +247,8 @@ def main():
         "config": {"workload": args.workload, "tokens": T, "hidden_size": H, "num_experts": E,
                    "num_experts_per_tok": k, "moe_intermediate_size": I,
                    "num_shared_experts": S, "shared_intermediate_size": Is,
-                   "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"]},
+                   "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"],
+                   "combine": args.combine},
         "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],
                   "bytes": alg["bytes"], "arith_intensity": ai,

@@ -36,8 +36,10 @@ struct ActParams {
   float alpha, limit, beta;
 };
 
+// 1 / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each);
+// e^-z overflows to +inf for very negative z, and rcp(inf) = 0, as wanted.
 __device__ __forceinline__ float sigmoid_f32(float z) {
-  return 1.0f / (1.0f + __expf(-z));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 __device__ __forceinline__ float act_apply(float g, float u, const ActParams& a) {

@@ -5,22 +5,34 @@
 // experts.{gate,up,down}_proj), and the activations are [rows, in], so both
 // MFMA operands are read along K in 16-byte chunks.
 //
-// Workgroup tile: 128 activation rows x 256 weight rows; K-step of 128 bytes
-// per row (64 bf16 or 32 fp32). Four waves in a 2x2 arrangement; each wave
-// owns 64 rows x 128 weight rows = 2 x 4 MFMA blocks of 32x32.
+// Tile: 128 activation rows x 256 weight rows; K-step of 128 bytes per row
+// (64 bf16 or 32 fp32). Four waves in a 2x2 arrangement; each wave owns 64
+// rows x 128 weight rows = 2 x 4 MFMA blocks of 32x32.
 //   gate/up: weight rows 0..127 are gate rows n0.., 128..255 the up rows of
 //            the same columns, so each wave holds matching gate and up
 //            accumulators and applies the activation in registers.
 //   down:    weight rows 0..255 are 256 output columns.
+//
+// Persistent schedule: one workgroup per compute unit walks a fixed list of
+// tiles. Tiles are numbered in a grouped order (m fastest inside groups of
+// m-slots) and every XCD owns a contiguous range of them, so the ~32
+// workgroups an XCD runs at once share activation and weight tiles in L2.
+//
 // Pipeline: three LDS stages filled by direct global->LDS loads
-// (global_load_lds_dwordx4, no staging registers); loads run two K-steps
-// ahead of the MFMAs; one barrier per K-step. LDS rows are 8 chunks of 16 B
-// with chunk c of row r stored at c ^ ((r >> 1) & 7), which keeps the 32x32
-// fragment reads free of bank conflicts on gfx950. Each wave's load
-// instruction fills 1 KB of LDS (8 rows); lane i supplies physical chunk
-// i % 8 of row i / 8, so it fetches the logical chunk that lands there.
-// Rows past the end of a tile (activation rows beyond the segment, weight
-// rows beyond N) load a valid clamped row; their results are never stored.
+// (global_load_lds_dwordx4, no staging registers), two K-steps ahead of the
+// MFMAs, one barrier per step. The load stream runs on across tiles: the last
+// two steps of a tile load the first two stages of the next tile, so they are
+// in flight during this tile's epilogue. Each tile's step count is padded to
+// a multiple of three with loads of a zero line (they add exactly zero), so
+// the LDS stage of every step is known at compile time. The three stages are
+// distinct __shared__ arrays and the barrier is a raw s_barrier, so the
+// compiler does not drain all loads before each LDS read. Nothing that a later
+// step must wait for is loaded after the look-ahead loads of a step (vector
+// memory counts complete in order), so no wait drains the pipeline. LDS rows
+// are 8 chunks of 16 B with chunk c of row r stored at c ^ ((r >> 1) & 7): no
+// bank conflicts for the 32x32 fragment reads (measured on gfx950). Rows past
+// the end of a tile (activation rows beyond the segment, weight rows beyond
+// N) load a valid clamped row; their results are never stored.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -28,11 +40,18 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int BM = 128;    // activation rows per workgroup
-constexpr int BR = 256;    // weight rows per workgroup
+constexpr int BM = 128;    // activation rows per tile
+constexpr int BR = 256;    // weight rows per tile
 constexpr int NCH = 8;     // 16-byte chunks per LDS row per K-step
+constexpr int KSB = NCH * 16;  // bytes per row per K-step
 constexpr int NTHR = 256;
 constexpr int MAX_EXPERTS = 1024;
+constexpr int LOADS_PER_STAGE = 12;  // per thread: 4 activation + 8 weight
+
+enum Kind { GATE_UP = 0, DOWN_SHARED = 1, DOWN_ROUTED = 2 };
+
+// A 128-byte line of zeros: the source of the padding steps.
+__device__ __align__(128) uint32_t g_zero_line[32] = {};
 
 template <typename T>
 struct Elem;
@@ -47,9 +66,6 @@ struct Elem<float> {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// The three LDS stages live in distinct __shared__ arrays so that the
-// compiler can tell a load into one stage from a read of another and does not
-// wait for every outstanding load before each LDS read.
 #define MOE_LDS_STAGES                              \
   __shared__ __align__(16) u32x4_t lds_a0[BM * NCH]; \
   __shared__ __align__(16) u32x4_t lds_a1[BM * NCH]; \
@@ -58,42 +74,52 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
   __shared__ __align__(16) u32x4_t lds_b1[BR * NCH]; \
   __shared__ __align__(16) u32x4_t lds_b2[BR * NCH];
 
-constexpr int LOADS_PER_STAGE = 12;  // per thread: 4 activation + 8 weight
-
-// Per-thread sources of its 12 load instructions per stage. Instruction j of
-// wave w fills activation rows 32w+8j .. +7 (j < 4) or weight rows
-// 64w+8j .. +7 (j < 8); the lane's row is that base + lane/8.
-template <typename T>
-struct Src {
-  const T* a[4];  // row pointer + logical chunk offset (elements)
-  const T* b[8];
-  int kseg;       // weight K segment length (elements); K-split for shared down
-  long bstride;   // elements between weight K segments
-};
-
+// Load instruction j of wave w fills activation rows 32w+8j .. +7 (j < 4) or
+// weight rows 64w+8j .. +7 (j < 8); the lane's row is that base + lane/8 and
+// it fetches the logical chunk that lands at physical chunk lane % 8.
 __device__ __forceinline__ int a_row(int j) { return (threadIdx.x >> 6) * 32 + 8 * j + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int b_row(int j) { return (threadIdx.x >> 6) * 64 + 8 * j + ((threadIdx.x & 63) >> 3); }
-// logical chunk fetched by this lane for a row
 __device__ __forceinline__ int lane_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
 
-__device__ __forceinline__ void dma16(const void* g, u32x4_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+// vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <typename T>
-__device__ __forceinline__ void load_stage(const Src<T>& s, int kk, long bseg, int koff,
-                                           u32x4_t* la, u32x4_t* lb) {
+// One tile: where its rows and weights are and how many K-steps it has.
+struct Tile {
+  const char* a[4];  // activation row pointers (+ lane chunk offset), bytes
+  const char* b[8];  // weight row pointers (+ lane chunk offset), bytes
+  int nk;            // real K-steps
+  int nk3;           // steps padded to a multiple of 3
+  int kseg;          // weight K segment length in bytes (K-split of shared down)
+  int bstride_kb;    // KiB between weight K segments
+  int shared, e, row0, nrows, n0, N;
+};
+
+// Load the 12 chunks of this lane for step j of tile t into LDS stage (la, lb)
+// (the zero line for padding steps j >= nk).
+__device__ __forceinline__ void issue_stage(const Tile& t, int j, u32x4_t* la, u32x4_t* lb) {
+  const bool real = j < t.nk;
+  const int kb = j * KSB;
+  const int seg = kb / t.kseg;
+  const long boff = (long)seg * t.bstride_kb * 1024 + (kb - seg * t.kseg);
+  const char* z = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 7) * 16;
   const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(s.a[j] + kk, la + (w * 4 + j) * 64);
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_global_load_lds(real ? t.a[q] + kb : z, la + (w * 4 + q) * 64, 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(s.b[j] + bseg + koff, lb + (w * 8 + j) * 64);
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + (w * 8 + q) * 64, 16, 0, 0);
 }
 
 // First weight row (within the 256-row tile) of block nb (0..3) of wave wn.
-template <bool GATE_UP>
+template <int KIND>
 __device__ __forceinline__ int wrow(int wn, int nb) {
-  if (GATE_UP) return nb < 2 ? wn * 64 + nb * 32 : 128 + wn * 64 + (nb - 2) * 32;
+  if (KIND == GATE_UP) return nb < 2 ? wn * 64 + nb * 32 : 128 + wn * 64 + (nb - 2) * 32;
   return wn * 128 + nb * 32;
 }
 
@@ -101,7 +127,7 @@ typedef floatx16_t Acc[2][4];
 
 // One K-step from one LDS stage.
 // bf16: 4 sub-steps of K=16; lane l reads row l%32, chunk 2*s + l/32.
-template <typename T, bool GATE_UP>
+template <typename T, int KIND>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -117,7 +143,7 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int row = wrow<GATE_UP>(wn, nb) + r;
+        const int row = wrow<KIND>(wn, nb) + r;
         fb[slot][nb] = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
       }
     };
@@ -160,7 +186,7 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int brw = wrow<GATE_UP>(wn, nb) + r;
+        const int brw = wrow<KIND>(wn, nb) + r;
         float bv[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -176,74 +202,21 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
   }
 }
 
-// vmcnt(n) with the other counters left alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+// Grouped tile order: logical index b -> (m-slot, n-tile) with groups of gm
+// m-slots; inside a group the m-slot varies fastest.
+__device__ __forceinline__ void grouped_order(int b, int mt, int nt, int gm, int* m, int* n) {
+  const int per_group = gm * nt;
+  const int g = b / per_group;
+  const int first = g * gm;
+  const int gsize = min(gm, mt - first);
+  const int local = b - g * per_group;
+  *m = first + local % gsize;
+  *n = local / gsize;
 }
 
-// Main loop: acc = A[128 x K] . B[256 x K]^T over the whole K (K % KS == 0).
-// Stage i lives in LDS set i % 3. Step i: wait for this wave's loads of
-// stage i (stage i+1 may stay in flight), barrier (all waves' loads of stage
-// i are in LDS and every wave is done with set (i+2) % 3), issue the loads of
-// stage i+2 into that set, compute stage i. The look-ahead loads are issued
-// on every step (past the end they re-read the last stage) so the compiler
-// sees the same number of loads in flight on every path.
-#define MOE_STEP(I, LA, LB, NA, NB)                                   \
-  {                                                                   \
-    wait_vmcnt<LOADS_PER_STAGE>();                                    \
-    __builtin_amdgcn_s_barrier();                                     \
-    if ((I) + 2 < nk) advance();                                      \
-    load_stage<T>(s, min((I) + 2, nk - 1) * KS, bseg, koff, NA, NB); \
-    compute_stage<T, GATE_UP>(LA, LB, acc);                           \
-  }
-
-template <typename T, bool GATE_UP>
-__device__ __forceinline__ void mainloop(u32x4_t* lds_a0, u32x4_t* lds_a1, u32x4_t* lds_a2,
-                                         u32x4_t* lds_b0, u32x4_t* lds_b1, u32x4_t* lds_b2,
-                                         const Src<T>& s, int K, Acc& acc) {
-  constexpr int KS = NCH * Elem<T>::EPC;  // elements per K-step
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-
-  const int nk = K / KS;
-  // weight K position of the most recently issued stage
-  long bseg = 0;
-  int koff = 0;
-  auto advance = [&]() {
-    koff += KS;
-    if (koff == s.kseg) {
-      koff = 0;
-      bseg += s.bstride;
-    }
-  };
-  load_stage<T>(s, 0, bseg, koff, lds_a0, lds_b0);
-  if (nk > 1) advance();
-  load_stage<T>(s, min(1, nk - 1) * KS, bseg, koff, lds_a1, lds_b1);
-  int it = 0;
-  for (; it + 3 <= nk; it += 3) {
-    MOE_STEP(it, lds_a0, lds_b0, lds_a2, lds_b2)
-    MOE_STEP(it + 1, lds_a1, lds_b1, lds_a0, lds_b0)
-    MOE_STEP(it + 2, lds_a2, lds_b2, lds_a1, lds_b1)
-  }
-  if (it < nk) MOE_STEP(it, lds_a0, lds_b0, lds_a2, lds_b2)
-  if (it + 1 < nk) MOE_STEP(it + 1, lds_a1, lds_b1, lds_a0, lds_b0)
-  // drain the look-ahead loads before the stages' LDS can be reused
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-}
-#undef MOE_STEP
-
-// Find which expert (and m-tile within it) routed m-slot `slot` belongs to.
-// Returns false if the slot is past the last tile. Uses `cum` (E+1 ints of
-// LDS): cum[e] = sum_{e'<e} ceil(n_e'/BM).
-__device__ bool locate_tile(const int32_t* __restrict__ offsets, int E, int slot, int* cum,
-                            int* e_out, int* mt_out) {
+// offs <- expert_offsets (E+1 ints); cum[e] = sum_{e'<e} ceil(n_e'/BM), e <= E
+__device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int* offs, int* cum) {
+  for (int e = threadIdx.x; e <= E; e += NTHR) offs[e] = offsets[e];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 63) / 64;
@@ -269,33 +242,18 @@ __device__ bool locate_tile(const int32_t* __restrict__ offsets, int E, int slot
     }
     if (lane == 63) cum[E] = incl;
   }
-  __syncthreads();
-  if (slot >= cum[E]) return false;
-  // the owner is the largest e with cum[e] <= slot (it has cum[e+1] > slot,
-  // so it is not empty)
+}
+
+// the expert that owns routed m-slot `slot` (largest e with cum[e] <= slot;
+// it has cum[e+1] > slot, so it is not empty)
+__device__ __forceinline__ int owner(const int* cum, int E, int slot) {
   int lo = 0, hi = E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (cum[mid] <= slot) lo = mid;
     else hi = mid - 1;
   }
-  *e_out = lo;
-  *mt_out = slot - cum[lo];
-  return true;
-}
-
-// Grouped tile order: logical block b -> (m-slot, n-tile) with groups of gm
-// m-slots; inside a group the m-slot varies fastest. The ~32 workgroups that
-// an XCD runs at once then cover a compact gm x (32/gm) patch, so both the
-// activation tiles and the weight tiles they read are shared through L2.
-__device__ __forceinline__ void grouped_order(uint32_t b, int mt, int nt, int gm, int* m, int* n) {
-  const uint32_t per_group = (uint32_t)gm * nt;
-  const int g = b / per_group;
-  const int first = g * gm;
-  const int gsize = min(gm, mt - first);
-  const int local = b - g * per_group;
-  *m = first + local % gsize;
-  *n = local / gsize;
+  return lo;
 }
 
 template <typename T>
@@ -315,268 +273,370 @@ __device__ __forceinline__ int acc_row(int mb, int v, int q) {
   return mb * 32 + (v >> 2) * 8 + q * 4 + (v & 3);
 }
 
+template <int KIND>
+__device__ __forceinline__ int tile_count(const GemmArgs& g, const int* cum) {
+  if (KIND == GATE_UP) return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
+  if (KIND == DOWN_SHARED) return g.mt_shared * g.nt_shared;
+  return cum[g.E] * g.nt_routed;
+}
+
+// Where tile `idx` is (no global memory reads: offsets and prefix are in LDS).
+template <int KIND>
+__device__ __forceinline__ void tile_place(const GemmArgs& g, const int* offs, const int* cum,
+                                           int idx, int* shared, int* e, int* row0, int* nrows,
+                                           int* nt) {
+  const int nshared = KIND == DOWN_ROUTED ? 0 : g.mt_shared * g.nt_shared;
+  int mt;
+  *e = 0;
+  if (idx < nshared) {
+    *shared = 1;
+    grouped_order(idx, g.mt_shared, g.nt_shared, g.gm_shared, &mt, nt);
+    *row0 = mt * BM;
+    *nrows = min(BM, g.T - *row0);
+  } else {
+    // routed tiles are expert-major: expert e owns tiles
+    // [cum[e] * nt_routed, cum[e+1] * nt_routed), so concurrent tiles share
+    // one expert's weights; inside an expert, groups of gm m-slots with the
+    // m-slot varying fastest
+    *shared = 0;
+    const int t = idx - nshared;
+    *e = owner(cum, g.E, t / g.nt_routed);
+    const int ms = cum[*e + 1] - cum[*e];
+    int m;
+    grouped_order(t - cum[*e] * g.nt_routed, ms, g.nt_routed, g.gm_routed, &m, nt);
+    *row0 = offs[*e] + m * BM;
+    *nrows = min(BM, offs[*e + 1] - *row0);
+  }
+}
+
+// Tokens of this lane's 4 activation rows of routed gate/up tile idx (global
+// loads; shared tiles need none).
+template <int KIND>
+__device__ __forceinline__ void load_tokens(const GemmArgs& g, const int* offs, const int* cum,
+                                            int idx, int (&tok)[4]) {
+  if (KIND != GATE_UP) return;
+  int shared, e, row0, nrows, nt;
+  tile_place<KIND>(g, offs, cum, idx, &shared, &e, &row0, &nrows, &nt);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = min(a_row(j), nrows - 1);
+    tok[j] = shared ? row0 + R : g.sorted_rows[row0 + R];
+  }
+}
+
+template <typename T, int KIND>
+__device__ void make_tile(const GemmArgs& g, const int* offs, const int* cum, int idx,
+                          const int (&tok)[4], Tile& t) {
+  constexpr int EPC = Elem<T>::EPC;
+  const int H = g.H;
+  int nt;
+  tile_place<KIND>(g, offs, cum, idx, &t.shared, &t.e, &t.row0, &t.nrows, &nt);
+  if (KIND == GATE_UP) {
+    const T* x = static_cast<const T*>(g.a);
+    t.n0 = nt * 128;
+    t.N = t.shared ? g.S * g.Is : g.I;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = a_row(j);
+      const int token = t.shared ? tok[j] : tok[j] / g.k;
+      t.a[j] = reinterpret_cast<const char*>(x + (size_t)token * H + lane_chunk(row) * EPC);
+    }
+    const T* wg = static_cast<const T*>(t.shared ? g.ws0 : g.w0);
+    const T* wu = static_cast<const T*>(t.shared ? g.ws1 : g.w1);
+    const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * H;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = b_row(j);
+      const int n = min(t.n0 + (row & 127), t.N - 1);
+      t.b[j] = reinterpret_cast<const char*>((row < 128 ? wg : wu) + ebase + (size_t)n * H +
+                                             lane_chunk(row) * EPC);
+    }
+    t.nk = H / (NCH * EPC);
+    t.kseg = H * (int)sizeof(T);
+    t.bstride_kb = 0;
+  } else if (KIND == DOWN_SHARED) {
+    const int Ks = g.S * g.Is;
+    const T* hs = static_cast<const T*>(g.a);
+    const T* wd = static_cast<const T*>(g.ws0);
+    t.n0 = nt * BR;
+    t.N = H;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = a_row(j);
+      t.a[j] = reinterpret_cast<const char*>(hs + (size_t)(t.row0 + min(row, t.nrows - 1)) * Ks +
+                                             lane_chunk(row) * EPC);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = b_row(j);
+      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * g.Is +
+                                             lane_chunk(row) * EPC);
+    }
+    t.nk = Ks / (NCH * EPC);
+    t.kseg = g.Is * (int)sizeof(T);  // shared expert s: K in [s*Is, (s+1)*Is) ...
+    t.bstride_kb = (int)(((long)H * g.Is * (long)sizeof(T)) >> 10);  // ... at ws_down + s*H*Is
+  } else {
+    const int I = g.I;
+    const T* h = static_cast<const T*>(g.a);
+    const T* wd = static_cast<const T*>(g.w0) + (size_t)t.e * H * I;
+    t.n0 = nt * BR;
+    t.N = H;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = a_row(j);
+      t.a[j] = reinterpret_cast<const char*>(h + (size_t)(t.row0 + min(row, t.nrows - 1)) * I +
+                                             lane_chunk(row) * EPC);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = b_row(j);
+      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * I +
+                                             lane_chunk(row) * EPC);
+    }
+    t.nk = I / (NCH * EPC);
+    t.kseg = I * (int)sizeof(T);
+    t.bstride_kb = 0;
+  }
+  t.nk3 = (t.nk + 2) / 3 * 3;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// gate/up + activation. Grid = shared blocks (mt_s x nt_s) + routed blocks
-// (mt_r x nt_r), both in grouped order.
+// The persistent kernel. Grid: one workgroup per compute unit (or fewer).
+// Step j of a tile: wait for this wave's loads of stage j (only the next
+// stage's loads are younger), barrier (all waves' loads of stage j are in LDS
+// and every wave is done with stage j-1's set), issue the loads of the stage
+// two ahead into that set, compute stage j.
+#define MOE_STEP(TL, J, LA, LB, NA, NB)          \
+  {                                              \
+    wait_vmcnt<LOADS_PER_STAGE>();               \
+    __builtin_amdgcn_s_barrier();                \
+    issue_stage(TL, J, NA, NB);                  \
+    compute_stage<T, KIND>(LA, LB, acc);         \
+  }
+
+template <typename T, int KIND, bool ATOMIC>
+__device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
+  MOE_LDS_STAGES
+  __shared__ int offs[MAX_EXPERTS + 1];
+  __shared__ int cum[MAX_EXPERTS + 1];
+  __shared__ int ep_tok[BM];   // routed down epilogue: token and weight of each row
+  __shared__ float ep_w[BM];
+
+  if (KIND != DOWN_SHARED) build_tile_prefix(g.offsets, g.E, offs, cum);
+  __syncthreads();
+  const int ntiles = tile_count<KIND>(g, cum);
+  // this workgroup's tiles: its XCD's contiguous range, walked with a stride
+  // of the number of workgroups on that XCD. Workgroups go to the nx XCDs
+  // round-robin; each XCD's range is proportional to its workgroup count, so
+  // the ranges cover every tile for any grid size.
+  const int G = gridDim.x, b = blockIdx.x;
+  const int nx = G < 8 ? G : 8;
+  const int x = b % nx, slot = b / nx;
+  const int gx = G / nx + (x < G % nx ? 1 : 0);
+  const int before = x * (G / nx) + min(x, G % nx);  // workgroups on XCDs < x
+  const int lo = (int)((long)ntiles * before / G);
+  const int hi = (int)((long)ntiles * (before + gx) / G);
+  int idx = lo + slot;
+  if (idx >= hi) return;
+
+  // Row ids are loaded one tile ahead, just before the first stage loads of
+  // the tile before theirs: the wait of that tile's first step then covers
+  // them (loads complete in order), so using them never drains the pipeline.
+  int tok[4] = {0, 0, 0, 0};
+  load_tokens<KIND>(g, offs, cum, idx, tok);
+  Tile cur, nxt;
+  make_tile<T, KIND>(g, offs, cum, idx, tok, cur);
+  int nidx = idx + gx < hi ? idx + gx : idx;  // the last tile repeats itself
+  load_tokens<KIND>(g, offs, cum, nidx, tok);
+  int ep_r = 0;  // routed down epilogue: the sorted row id of row threadIdx.x
+  if (KIND == DOWN_ROUTED && threadIdx.x < BM)
+    ep_r = g.sorted_rows[cur.row0 + min((int)threadIdx.x, cur.nrows - 1)];
+  issue_stage(cur, 0, lds_a0, lds_b0);
+  issue_stage(cur, 1, lds_a1, lds_b1);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
+
+  for (;;) {
+    const bool has_next = idx + gx < hi;
+    Acc acc;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+
+    const int nk3 = cur.nk3;
+    int j = 0;
+    for (; j + 3 < nk3; j += 3) {
+      MOE_STEP(cur, j + 2, lds_a0, lds_b0, lds_a2, lds_b2)
+      MOE_STEP(cur, j + 3, lds_a1, lds_b1, lds_a0, lds_b0)
+      MOE_STEP(cur, j + 4, lds_a2, lds_b2, lds_a1, lds_b1)
+    }
+    // last three steps: the look-ahead loads are the next tile's first stages
+    MOE_STEP(cur, j + 2, lds_a0, lds_b0, lds_a2, lds_b2)
+    int ep_t = 0;
+    float ep_wt = 0.f;
+    if (KIND == DOWN_ROUTED && threadIdx.x < BM) {
+      if (ATOMIC) ep_wt = g.topk_w[ep_r];
+      ep_t = ep_r / g.k;
+    }
+    make_tile<T, KIND>(g, offs, cum, nidx, tok, nxt);
+    // ids of the tile after next, then (below) the next tile's first stages
+    const int nnidx = nidx + gx < hi ? nidx + gx : nidx;
+    load_tokens<KIND>(g, offs, cum, nnidx, tok);
+    if (KIND == DOWN_ROUTED && threadIdx.x < BM)
+      ep_r = g.sorted_rows[nxt.row0 + min((int)threadIdx.x, nxt.nrows - 1)];
+    const int s0 = has_next ? 0 : nxt.nk3;  // nothing to load after the last tile
+    MOE_STEP(nxt, s0, lds_a1, lds_b1, lds_a0, lds_b0)
+    MOE_STEP(nxt, s0 + 1, lds_a2, lds_b2, lds_a1, lds_b1)
+
+    // ---- epilogue of the current tile (next tile's first stages in flight)
+    if (KIND == GATE_UP) {
+      T* dst = static_cast<T*>(cur.shared ? g.out_shared : g.out);
+      const int ld = cur.shared ? g.S * g.Is : g.I;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = wm * 64 + acc_row(mb, v, q);
+          if (m >= cur.nrows) continue;
+          T* drow = dst + (size_t)(cur.row0 + m) * ld;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = cur.n0 + wn * 64 + nb * 32 + r;
+            if (col < cur.N)
+              store_out<T>(drow + col, act_apply(acc[mb][nb][v], acc[mb][nb + 2][v], g.act));
+          }
+        }
+    } else if (KIND == DOWN_SHARED) {
+      float* out = static_cast<float*>(g.out);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = wm * 64 + acc_row(mb, v, q);
+          if (m >= cur.nrows) continue;
+          float* orow = out + (size_t)(cur.row0 + m) * g.H;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int col = cur.n0 + wn * 128 + nb * 32 + r;
+            if (col < cur.N) orow[col] = acc[mb][nb][v];
+          }
+        }
+    } else {
+      if (threadIdx.x < BM) {
+        ep_tok[threadIdx.x] = ep_t;
+        ep_w[threadIdx.x] = ep_wt;
+      }
+      // raw barrier: only the LDS writes above must be complete
+      __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = wm * 64 + acc_row(mb, v, q);
+          if (m >= cur.nrows) continue;
+          if (ATOMIC) {
+            float* orow = static_cast<float*>(g.out) + (size_t)ep_tok[m] * g.H;
+            const float wt = ep_w[m];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int col = cur.n0 + wn * 128 + nb * 32 + r;
+              if (col < cur.N) unsafeAtomicAdd(orow + col, wt * acc[mb][nb][v]);
+            }
+          } else {
+            T* yrow = static_cast<T*>(g.y_perm) + (size_t)(cur.row0 + m) * g.H;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int col = cur.n0 + wn * 128 + nb * 32 + r;
+              if (col < cur.N) store_out<T>(yrow + col, acc[mb][nb][v]);
+            }
+          }
+        }
+      // ep_tok/ep_w are rewritten by the next tile only after its steps'
+      // barriers
+    }
+    if (!has_next) break;
+    idx = nidx;
+    nidx = nnidx;
+    cur = nxt;
+  }
+  // the look-ahead loads after the last tile are not used: let them land
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+}
+#undef MOE_STEP
+
+// one entry per kind, so that profiles name them
 template <typename T>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_kernel(GemmArgs g) {
-  MOE_LDS_STAGES
-  __shared__ int cum[MAX_EXPERTS + 1];
-
-  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t nshared = (uint32_t)g.mt_shared * g.nt_shared;
-  const T* x = static_cast<const T*>(g.a);
-  const int H = g.H;
-  bool shared;
-  int n0, row0, nrows, e = 0, N;
-  if (lb < nshared) {
-    shared = true;
-    int nt, mt;
-    grouped_order(lb, g.mt_shared, g.nt_shared, g.gm_shared, &mt, &nt);
-    n0 = nt * 128;
-    row0 = mt * BM;
-    nrows = min(BM, g.T - row0);
-    N = g.S * g.Is;
-  } else {
-    shared = false;
-    int nt, slot, mt;
-    grouped_order(lb - nshared, g.mt_routed, g.nt_routed, g.gm_routed, &slot, &nt);
-    if (!locate_tile(g.offsets, g.E, slot, cum, &e, &mt)) return;
-    n0 = nt * 128;
-    row0 = g.offsets[e] + mt * BM;
-    nrows = min(BM, g.offsets[e + 1] - row0);
-    N = g.I;
-  }
-
-  constexpr int EPC = Elem<T>::EPC;
-  Src<T> s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = a_row(j);
-    const int R = min(row, nrows - 1);
-    const int tok = shared ? row0 + R : g.sorted_rows[row0 + R] / g.k;
-    s.a[j] = x + (size_t)tok * H + lane_chunk(row) * EPC;
-  }
-  const T* wg = static_cast<const T*>(shared ? g.ws0 : g.w0);
-  const T* wu = static_cast<const T*>(shared ? g.ws1 : g.w1);
-  const size_t ebase = shared ? 0 : (size_t)e * g.I * H;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = b_row(j);
-    const int n = min(n0 + (row & 127), N - 1);
-    s.b[j] = (row < 128 ? wg : wu) + ebase + (size_t)n * H + lane_chunk(row) * EPC;
-  }
-  s.kseg = H;
-  s.bstride = 0;
-
-  Acc acc;
-  mainloop<T, true>(lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2, s, H, acc);
-
-  // epilogue: h = act(gate, up); gate block nb pairs with up block nb + 2
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
-  T* dst = static_cast<T*>(shared ? g.out_shared : g.out);
-  const int ld = shared ? g.S * g.Is : g.I;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = wm * 64 + acc_row(mb, v, q);
-      if (m >= nrows) continue;
-      T* drow = dst + (size_t)(row0 + m) * ld;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n0 + wn * 64 + nb * 32 + r;
-        if (col < N) store_out<T>(drow + col, act_apply(acc[mb][nb][v], acc[mb][nb + 2][v], g.act));
-      }
-    }
+  moe_gemm_body<T, GATE_UP, false>(g);
 }
-
-// ---------------------------------------------------------------------------
-// down projection of the shared experts: acc[t] = h_shared[t] . Wsd_cat^T,
-// stored (this launch runs before the routed one on the same stream).
 template <typename T>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_kernel(GemmArgs g) {
-  MOE_LDS_STAGES
-  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  int nt, mt;
-  grouped_order(lb, g.mt_shared, g.nt_shared, g.gm_shared, &mt, &nt);
-  const int n0 = nt * BR, row0 = mt * BM;
-  const int nrows = min(BM, g.T - row0);
-  const int H = g.H, Ks = g.S * g.Is;
-  const T* hs = static_cast<const T*>(g.a);
-  const T* wd = static_cast<const T*>(g.ws0);
-  constexpr int EPC = Elem<T>::EPC;
-  Src<T> s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = a_row(j);
-    s.a[j] = hs + (size_t)(row0 + min(row, nrows - 1)) * Ks + lane_chunk(row) * EPC;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = b_row(j);
-    s.b[j] = wd + (size_t)min(n0 + row, H - 1) * g.Is + lane_chunk(row) * EPC;
-  }
-  s.kseg = g.Is;               // shared expert s occupies K in [s*Is, (s+1)*Is)
-  s.bstride = (long)H * g.Is;  // ... and lives at ws_down + s*H*Is
-
-  Acc acc;
-  mainloop<T, false>(lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2, s, Ks, acc);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
-  float* out = static_cast<float*>(g.out);
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = wm * 64 + acc_row(mb, v, q);
-      if (m >= nrows) continue;
-      float* orow = out + (size_t)(row0 + m) * H;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = n0 + wn * 128 + nb * 32 + r;
-        if (col < H) orow[col] = acc[mb][nb][v];
-      }
-    }
+  moe_gemm_body<T, DOWN_SHARED, false>(g);
 }
-
-// ---------------------------------------------------------------------------
-// down projection of the routed experts, fused with the weighted combine:
-// ATOMIC: acc[t] += w * y (fp32 atomics); else y_perm[p] = y (dtype).
 template <typename T, bool ATOMIC>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_kernel(GemmArgs g) {
-  MOE_LDS_STAGES
-  __shared__ int cum[MAX_EXPERTS + 1];
-  __shared__ int etok[BM];
-  __shared__ float ew[BM];
-
-  const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-  int nt, slot;
-  grouped_order(lb, g.mt_routed, g.nt_routed, g.gm_routed, &slot, &nt);
-  int e, mt;
-  if (!locate_tile(g.offsets, g.E, slot, cum, &e, &mt)) return;
-  const int n0 = nt * BR;
-  const int row0 = g.offsets[e] + mt * BM;
-  const int nrows = min(BM, g.offsets[e + 1] - row0);
-  const int H = g.H, I = g.I;
-  const T* h = static_cast<const T*>(g.a);
-  const T* wd = static_cast<const T*>(g.w0) + (size_t)e * H * I;
-
-  if (ATOMIC && threadIdx.x < BM) {
-    const int m = threadIdx.x;
-    if (m < nrows) {
-      const int rr = g.sorted_rows[row0 + m];
-      etok[m] = rr / g.k;
-      ew[m] = g.topk_w[rr];
-    }
-  }
-
-  constexpr int EPC = Elem<T>::EPC;
-  Src<T> s;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = a_row(j);
-    s.a[j] = h + (size_t)(row0 + min(row, nrows - 1)) * I + lane_chunk(row) * EPC;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = b_row(j);
-    s.b[j] = wd + (size_t)min(n0 + row, H - 1) * I + lane_chunk(row) * EPC;
-  }
-  s.kseg = I;
-  s.bstride = 0;
-  // etok/ew are written before the first barrier of the main loop
-  __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0): LDS writes done
-
-  Acc acc;
-  mainloop<T, false>(lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2, s, I, acc);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = wm * 64 + acc_row(mb, v, q);
-      if (m >= nrows) continue;
-      if (ATOMIC) {
-        float* orow = static_cast<float*>(g.out) + (size_t)etok[m] * H;
-        const float wt = ew[m];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = n0 + wn * 128 + nb * 32 + r;
-          if (col < H) unsafeAtomicAdd(orow + col, wt * acc[mb][nb][v]);
-        }
-      } else {
-        T* yrow = static_cast<T*>(g.y_perm) + (size_t)(row0 + m) * H;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = n0 + wn * 128 + nb * 32 + r;
-          if (col < H) store_out<T>(yrow + col, acc[mb][nb][v]);
-        }
-      }
-    }
+  moe_gemm_body<T, DOWN_ROUTED, ATOMIC>(g);
 }
 
 // ---------------------------------------------------------------------------
 // host-side launchers
 
 size_t gemm_lds_bytes(int) { return 0; }
-
 int gemm_bm() { return BM; }
 
-static hipError_t set_lds(const void*, size_t) { return hipSuccess; }
+static int g_num_cus = 0;
+static int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+static int grid_for(long max_tiles) { return (int)(max_tiles < num_cus() ? max_tiles : num_cus()); }
 
 hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st) {
-  const size_t lds = gemm_lds_bytes(g.E);
-  const uint32_t nblk = (uint32_t)g.mt_shared * g.nt_shared + (uint32_t)g.mt_routed * g.nt_routed;
-  if (nblk == 0) return hipSuccess;
-  if (dtype == MOE_BF16) {
-    hipError_t e = set_lds((const void*)moe_gate_up_kernel<bf16_t>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_gate_up_kernel<bf16_t>, dim3(nblk), dim3(NTHR), lds, st, g);
-  } else {
-    hipError_t e = set_lds((const void*)moe_gate_up_kernel<float>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_gate_up_kernel<float>, dim3(nblk), dim3(NTHR), lds, st, g);
-  }
+  const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
+  if (n <= 0) return hipSuccess;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(moe_gate_up_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else
+    hipLaunchKernelGGL(moe_gate_up_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st) {
-  const size_t lds = gemm_lds_bytes(g.E);
-  const uint32_t nblk = (uint32_t)g.mt_shared * g.nt_shared;
-  if (nblk == 0) return hipSuccess;
-  if (dtype == MOE_BF16) {
-    hipError_t e = set_lds((const void*)moe_down_shared_kernel<bf16_t>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_down_shared_kernel<bf16_t>, dim3(nblk), dim3(NTHR), lds, st, g);
-  } else {
-    hipError_t e = set_lds((const void*)moe_down_shared_kernel<float>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_down_shared_kernel<float>, dim3(nblk), dim3(NTHR), lds, st, g);
-  }
+  const long n = (long)g.mt_shared * g.nt_shared;
+  if (n <= 0) return hipSuccess;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(moe_down_shared_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else
+    hipLaunchKernelGGL(moe_down_shared_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st) {
-  const size_t lds = gemm_lds_bytes(g.E);
-  const uint32_t nblk = (uint32_t)g.mt_routed * g.nt_routed;
-  if (nblk == 0) return hipSuccess;
-  hipError_t e;
-#define MOE_LAUNCH_DOWN(TT, AT)                                                        \
-  e = set_lds((const void*)moe_down_routed_kernel<TT, AT>, lds);                       \
-  if (e != hipSuccess) return e;                                                       \
-  hipLaunchKernelGGL((moe_down_routed_kernel<TT, AT>), dim3(nblk), dim3(NTHR), lds, st, g);
+  const long n = (long)g.mt_routed * g.nt_routed;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(grid_for(n));
   if (dtype == MOE_BF16) {
-    if (atomic) { MOE_LAUNCH_DOWN(bf16_t, true) } else { MOE_LAUNCH_DOWN(bf16_t, false) }
+    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true>), grid, dim3(NTHR), 0, st, g);
+    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false>), grid, dim3(NTHR), 0, st, g);
   } else {
-    if (atomic) { MOE_LAUNCH_DOWN(float, true) } else { MOE_LAUNCH_DOWN(float, false) }
+    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<float, true>), grid, dim3(NTHR), 0, st, g);
+    else hipLaunchKernelGGL((moe_down_routed_kernel<float, false>), grid, dim3(NTHR), 0, st, g);
   }
-#undef MOE_LAUNCH_DOWN
   return hipGetLastError();
 }
