@@ -2,6 +2,7 @@
 // All checks run before the first launch of a call; nothing here allocates.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -132,6 +133,7 @@ GemmArgs base_args(const moe_config* c, const Dims& d) {
   g.I = d.I;
   g.E = d.E;
   g.k = d.k;
+  g.kmagic = (uint32_t)std::min<uint64_t>((1ull << 32) / (uint64_t)d.k, 0xFFFFFFFFull);
   g.S = d.S;
   g.Is = d.Is;
   g.act = act_of(c);

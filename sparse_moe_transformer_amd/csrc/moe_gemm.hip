@@ -158,19 +158,21 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][mb], fb[s & 1][nb],
                                                                 acc[mb][nb], 0, 0, 0);
     }
-    // schedule: the 6 fragment reads of sub-step s+1 are interleaved with the
-    // 8 MFMAs of sub-step s, so LDS latency hides behind matrix work
+    // schedule: the 6 fragment reads of sub-step s+1 and 3 of the step's 12
+    // global->LDS loads are interleaved with the 8 MFMAs of sub-step s. Issued
+    // back to back, the loads would stall the wave on a full memory queue
+    // with its MFMAs waiting behind them (measured: 1768 -> 1423 cycles per
+    // step with L2-resident data).
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // reads of sub-step 0
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (s < 3 && i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i == 1 || i == 4 || i == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   } else {
     // fp32: lane group q holds k = 16q..16q+15 (chunks 4q..4q+3); MFMA v of
     // the 16 32x32x2 steps takes slot v of both operands.
@@ -309,14 +311,33 @@ __device__ __forceinline__ void tile_place(const GemmArgs& g, const int* offs, c
   }
 }
 
-// Tokens of this lane's 4 activation rows of routed gate/up tile idx (global
-// loads; shared tiles need none).
+// A tile's place: row0 (x), nrows | shared << 16 (y), expert (z), n-tile (w).
+// A workgroup computes the places of its first MAX_WG_TILES tiles once, in
+// parallel, into LDS; later tiles (very large batches) are placed on the fly.
+constexpr int MAX_WG_TILES = 256;
+
 template <int KIND>
-__device__ __forceinline__ void load_tokens(const GemmArgs& g, const int* offs, const int* cum,
-                                            int idx, int (&tok)[4]) {
-  if (KIND != GATE_UP) return;
+__device__ __forceinline__ int4 place_of(const GemmArgs& g, const int* offs, const int* cum,
+                                         int idx) {
   int shared, e, row0, nrows, nt;
   tile_place<KIND>(g, offs, cum, idx, &shared, &e, &row0, &nrows, &nt);
+  return make_int4(row0, nrows | (shared << 16), e, nt);
+}
+
+// row / k for row ids (0 <= row < 2^31): multiply-high by floor(2^32 / k)
+// falls short by at most one, which the fix-up restores
+__device__ __forceinline__ int div_k(int row, int k, uint32_t kmagic) {
+  int t = (int)__umulhi((uint32_t)row, kmagic);
+  if ((t + 1) * k <= row) ++t;
+  return t;
+}
+
+// Tokens of this lane's 4 activation rows of routed gate/up tile p (global
+// loads; shared tiles need none).
+template <int KIND>
+__device__ __forceinline__ void load_tokens(const GemmArgs& g, int4 p, int (&tok)[4]) {
+  if (KIND != GATE_UP) return;
+  const int row0 = p.x, nrows = p.y & 0xFFFF, shared = p.y >> 16;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int R = min(a_row(j), nrows - 1);
@@ -325,12 +346,14 @@ __device__ __forceinline__ void load_tokens(const GemmArgs& g, const int* offs, 
 }
 
 template <typename T, int KIND>
-__device__ void make_tile(const GemmArgs& g, const int* offs, const int* cum, int idx,
-                          const int (&tok)[4], Tile& t) {
+__device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& t) {
   constexpr int EPC = Elem<T>::EPC;
   const int H = g.H;
-  int nt;
-  tile_place<KIND>(g, offs, cum, idx, &t.shared, &t.e, &t.row0, &t.nrows, &nt);
+  t.row0 = p.x;
+  t.nrows = p.y & 0xFFFF;
+  t.shared = p.y >> 16;
+  t.e = p.z;
+  const int nt = p.w;
   if (KIND == GATE_UP) {
     const T* x = static_cast<const T*>(g.a);
     t.n0 = nt * 128;
@@ -338,7 +361,7 @@ __device__ void make_tile(const GemmArgs& g, const int* offs, const int* cum, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = a_row(j);
-      const int token = t.shared ? tok[j] : tok[j] / g.k;
+      const int token = t.shared ? tok[j] : div_k(tok[j], g.k, g.kmagic);
       t.a[j] = reinterpret_cast<const char*>(x + (size_t)token * H + lane_chunk(row) * EPC);
     }
     const T* wg = static_cast<const T*>(t.shared ? g.ws0 : g.w0);
@@ -423,6 +446,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   __shared__ int cum[MAX_EXPERTS + 1];
   __shared__ int ep_tok[BM];   // routed down epilogue: token and weight of each row
   __shared__ float ep_w[BM];
+  __shared__ int4 places[MAX_WG_TILES];
 
   if (KIND != DOWN_SHARED) build_tile_prefix(g.offsets, g.E, offs, cum);
   __syncthreads();
@@ -438,18 +462,27 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   const int before = x * (G / nx) + min(x, G % nx);  // workgroups on XCDs < x
   const int lo = (int)((long)ntiles * before / G);
   const int hi = (int)((long)ntiles * (before + gx) / G);
-  int idx = lo + slot;
-  if (idx >= hi) return;
+  if (lo + slot >= hi) return;
+  // this workgroup's tiles are lo + slot + i * gx, i < n_my
+  const int n_my = (hi - lo - slot + gx - 1) / gx;
+  for (int i = threadIdx.x; i < min(n_my, MAX_WG_TILES); i += NTHR)
+    places[i] = place_of<KIND>(g, offs, cum, lo + slot + i * gx);
+  __syncthreads();
+  // the place of tile i (the last tile stands in for any i past the end)
+  auto place = [&](int i) -> int4 {
+    i = min(i, n_my - 1);
+    return i < MAX_WG_TILES ? places[i] : place_of<KIND>(g, offs, cum, lo + slot + i * gx);
+  };
 
   // Row ids are loaded one tile ahead, just before the first stage loads of
   // the tile before theirs: the wait of that tile's first step then covers
   // them (loads complete in order), so using them never drains the pipeline.
+  int li = 0;  // local index of the current tile
   int tok[4] = {0, 0, 0, 0};
-  load_tokens<KIND>(g, offs, cum, idx, tok);
+  load_tokens<KIND>(g, place(0), tok);
   Tile cur, nxt;
-  make_tile<T, KIND>(g, offs, cum, idx, tok, cur);
-  int nidx = idx + gx < hi ? idx + gx : idx;  // the last tile repeats itself
-  load_tokens<KIND>(g, offs, cum, nidx, tok);
+  make_tile<T, KIND>(g, place(0), tok, cur);
+  load_tokens<KIND>(g, place(1), tok);
   int ep_r = 0;  // routed down epilogue: the sorted row id of row threadIdx.x
   if (KIND == DOWN_ROUTED && threadIdx.x < BM)
     ep_r = g.sorted_rows[cur.row0 + min((int)threadIdx.x, cur.nrows - 1)];
@@ -460,7 +493,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
 
   for (;;) {
-    const bool has_next = idx + gx < hi;
+    const bool has_next = li + 1 < n_my;
     Acc acc;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -482,51 +515,77 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
     float ep_wt = 0.f;
     if (KIND == DOWN_ROUTED && threadIdx.x < BM) {
       if (ATOMIC) ep_wt = g.topk_w[ep_r];
-      ep_t = ep_r / g.k;
+      ep_t = div_k(ep_r, g.k, g.kmagic);
     }
-    make_tile<T, KIND>(g, offs, cum, nidx, tok, nxt);
+    make_tile<T, KIND>(g, place(li + 1), tok, nxt);
     // ids of the tile after next, then (below) the next tile's first stages
-    const int nnidx = nidx + gx < hi ? nidx + gx : nidx;
-    load_tokens<KIND>(g, offs, cum, nnidx, tok);
+    load_tokens<KIND>(g, place(li + 2), tok);
     if (KIND == DOWN_ROUTED && threadIdx.x < BM)
       ep_r = g.sorted_rows[nxt.row0 + min((int)threadIdx.x, nxt.nrows - 1)];
     const int s0 = has_next ? 0 : nxt.nk3;  // nothing to load after the last tile
     MOE_STEP(nxt, s0, lds_a1, lds_b1, lds_a0, lds_b0)
     MOE_STEP(nxt, s0 + 1, lds_a2, lds_b2, lds_a1, lds_b1)
 
-    // ---- epilogue of the current tile (next tile's first stages in flight)
+    // ---- epilogue of the current tile (next tile's first stages in flight).
+    // Full tiles (all rows present, all columns inside N) take a path with no
+    // per-element bounds checks: lane (q, r) of wave (wm, wn) writes rows
+    // base + acc_row(mb, v, q) of column r of each 32-column block.
+    const bool full_rows = cur.nrows == BM;
     if (KIND == GATE_UP) {
       T* dst = static_cast<T*>(cur.shared ? g.out_shared : g.out);
       const int ld = cur.shared ? g.S * g.Is : g.I;
+      T* base = dst + (size_t)(cur.row0 + wm * 64) * ld + cur.n0 + wn * 64 + r;
+      if (full_rows && cur.n0 + 128 <= cur.N) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = wm * 64 + acc_row(mb, v, q);
-          if (m >= cur.nrows) continue;
-          T* drow = dst + (size_t)(cur.row0 + m) * ld;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int col = cur.n0 + wn * 64 + nb * 32 + r;
-            if (col < cur.N)
-              store_out<T>(drow + col, act_apply(acc[mb][nb][v], acc[mb][nb + 2][v], g.act));
+          for (int v = 0; v < 16; ++v) {
+            T* p = base + (size_t)acc_row(mb, v, q) * ld;
+            store_out<T>(p, act_apply(acc[mb][0][v], acc[mb][2][v], g.act));
+            store_out<T>(p + 32, act_apply(acc[mb][1][v], acc[mb][3][v], g.act));
           }
-        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = wm * 64 + acc_row(mb, v, q);
+            if (m >= cur.nrows) continue;
+            T* p = base + (size_t)acc_row(mb, v, q) * ld;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const int col = cur.n0 + wn * 64 + nb * 32 + r;
+              if (col < cur.N) store_out<T>(p + nb * 32, act_apply(acc[mb][nb][v], acc[mb][nb + 2][v], g.act));
+            }
+          }
+      }
     } else if (KIND == DOWN_SHARED) {
-      float* out = static_cast<float*>(g.out);
+      float* base = static_cast<float*>(g.out) + (size_t)(cur.row0 + wm * 64) * g.H + cur.n0 +
+                    wn * 128 + r;
+      if (full_rows && cur.n0 + BR <= cur.N) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = wm * 64 + acc_row(mb, v, q);
-          if (m >= cur.nrows) continue;
-          float* orow = out + (size_t)(cur.row0 + m) * g.H;
+          for (int v = 0; v < 16; ++v) {
+            float* p = base + (size_t)acc_row(mb, v, q) * g.H;
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int col = cur.n0 + wn * 128 + nb * 32 + r;
-            if (col < cur.N) orow[col] = acc[mb][nb][v];
+            for (int nb = 0; nb < 4; ++nb) p[nb * 32] = acc[mb][nb][v];
           }
-        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = wm * 64 + acc_row(mb, v, q);
+            if (m >= cur.nrows) continue;
+            float* p = base + (size_t)acc_row(mb, v, q) * g.H;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int col = cur.n0 + wn * 128 + nb * 32 + r;
+              if (col < cur.N) p[nb * 32] = acc[mb][nb][v];
+            }
+          }
+      }
     } else {
       if (threadIdx.x < BM) {
         ep_tok[threadIdx.x] = ep_t;
@@ -535,35 +594,52 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
       // raw barrier: only the LDS writes above must be complete
       __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
+      const bool full = full_rows && cur.n0 + BR <= cur.N;
+      if (ATOMIC) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = wm * 64 + acc_row(mb, v, q);
-          if (m >= cur.nrows) continue;
-          if (ATOMIC) {
-            float* orow = static_cast<float*>(g.out) + (size_t)ep_tok[m] * g.H;
+          for (int v = 0; v < 16; ++v) {
+            const int m = wm * 64 + acc_row(mb, v, q);
+            if (!full && m >= cur.nrows) continue;
+            float* orow = static_cast<float*>(g.out) + (size_t)ep_tok[m] * g.H + cur.n0 + wn * 128 + r;
             const float wt = ep_w[m];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const int col = cur.n0 + wn * 128 + nb * 32 + r;
-              if (col < cur.N) unsafeAtomicAdd(orow + col, wt * acc[mb][nb][v]);
-            }
-          } else {
-            T* yrow = static_cast<T*>(g.y_perm) + (size_t)(cur.row0 + m) * g.H;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const int col = cur.n0 + wn * 128 + nb * 32 + r;
-              if (col < cur.N) store_out<T>(yrow + col, acc[mb][nb][v]);
-            }
+            for (int nb = 0; nb < 4; ++nb)
+              if (full || cur.n0 + wn * 128 + nb * 32 + r < cur.N)
+                unsafeAtomicAdd(orow + nb * 32, wt * acc[mb][nb][v]);
           }
+      } else {
+        T* base = static_cast<T*>(g.y_perm) + (size_t)(cur.row0 + wm * 64) * g.H + cur.n0 +
+                  wn * 128 + r;
+        if (full) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              T* p = base + (size_t)acc_row(mb, v, q) * g.H;
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb) store_out<T>(p + nb * 32, acc[mb][nb][v]);
+            }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int m = wm * 64 + acc_row(mb, v, q);
+              if (m >= cur.nrows) continue;
+              T* p = base + (size_t)acc_row(mb, v, q) * g.H;
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb)
+                if (cur.n0 + wn * 128 + nb * 32 + r < cur.N) store_out<T>(p + nb * 32, acc[mb][nb][v]);
+            }
         }
+      }
       // ep_tok/ep_w are rewritten by the next tile only after its steps'
       // barriers
     }
     if (!has_next) break;
-    idx = nidx;
-    nidx = nnidx;
+    ++li;
     cur = nxt;
   }
   // the look-ahead loads after the last tile are not used: let them land

@@ -20,6 +20,7 @@ struct GemmArgs {
   void* out_shared;   // h_shared (gate/up)
   void* y_perm;       // unweighted routed rows (fixed-order combine)
   int T, H, I, E, k, S, Is;
+  uint32_t kmagic;    // min(floor(2^32 / k), 2^32 - 1): row / k by multiply-high + one fix-up
   int mt_routed, nt_routed, mt_shared, nt_shared;
   int gm_routed, gm_shared;  // m-slots per group of the tile order
   ActParams act;
