@@ -177,6 +177,147 @@ __global__ void __launch_bounds__(256) router_f32_kernel(const float* __restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled bf16 router for prefill-sized batches: workgroup tile 128 tokens x 64
+// experts; the three weight planes are 192 weight rows of the tile. K-steps of
+// 64 elements (128 bytes per row), three LDS stages filled by direct
+// global->LDS loads two steps ahead (the grouped-GEMM pipeline), so each
+// plane row is read once per 128 tokens instead of once per 32. Stage rows:
+// 0..127 tokens, 128 + 64p + j plane p of expert j; chunk c of row r at
+// c ^ ((r >> 1) & 7). Four waves (2x2): wave (wm, wn) owns tokens 64wm..+63 x
+// experts 32wn..+31, two 32x32 blocks, three MFMAs (lo, mid, hi) per block and
+// sub-step. A workgroup covers K-chunk blockIdx.z; chunks are summed in order.
+constexpr int RTT_M = 128, RTT_N = 64, RTT_ROWS = RTT_M + 3 * RTT_N;  // 320
+constexpr int RTT_LOADS = RTT_ROWS / 32;  // 10 loads per lane per stage
+
+__device__ __align__(128) uint32_t g_router_zero[32] = {};
+
+__device__ __forceinline__ int rswz(int row) { return (row >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void r_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct RTile {
+  const char* p[RTT_LOADS];  // this lane's row pointers (+ chunk offset)
+  int nk;                    // real K-steps of the chunk
+};
+
+__device__ __forceinline__ void rt_issue(const RTile& t, int j, u32x4_t* st) {
+  const bool real = j < t.nk;
+  const int kb = j * 128;
+  const char* z = reinterpret_cast<const char*>(g_router_zero) + (threadIdx.x & 7) * 16;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < RTT_LOADS; ++i)
+    __builtin_amdgcn_global_load_lds(real ? t.p[i] + kb : z, st + (w * RTT_LOADS * 8 + i * 8) * 8,
+                                     16, 0, 0);
+}
+
+__device__ __forceinline__ void rt_compute(const u32x4_t* st, floatx16_t (&acc)[2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
+  bf16x8_t fa[2][2], fb[2][3];
+  auto read = [&](int s, int slot) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = wm * 64 + mb * 32 + r;
+      fa[slot][mb] = __builtin_bit_cast(bf16x8_t, st[row * 8 + ((2 * s + q) ^ rswz(row))]);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int row = RTT_M + p * RTT_N + wn * 32 + r;
+      fb[slot][p] = __builtin_bit_cast(bf16x8_t, st[row * 8 + ((2 * s + q) ^ rswz(row))]);
+    }
+  };
+  read(0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < 3) read(s + 1, (s + 1) & 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int p = 2; p >= 0; --p)  // smallest terms first
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][mb], fb[s & 1][p], acc[mb],
+                                                          0, 0, 0);
+  }
+  // per sub-step: 6 MFMAs carry the next sub-step's 5 fragment reads and
+  // 2-3 of the step's 10 global->LDS loads
+  __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s < 3 && i < 5) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if ((i == 1 || i == 4) || (i == 5 && s < 2)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+}
+
+#define RT_STEP(J, SC, SD)                   \
+  {                                          \
+    r_wait_vmcnt<RTT_LOADS>();               \
+    __builtin_amdgcn_s_barrier();            \
+    rt_issue(t, J, SD);                      \
+    rt_compute(SC, acc);                     \
+  }
+
+// grid (ceil(T/128), ceil(E/64), KC); kc_steps K-steps of 64 per chunk
+__global__ void __launch_bounds__(256) router_tile_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ planes,
+                                                          float* __restrict__ part, int T,
+                                                          int H, int E, int kc_steps) {
+  __shared__ __align__(16) u32x4_t st0[RTT_ROWS * 8];
+  __shared__ __align__(16) u32x4_t st1[RTT_ROWS * 8];
+  __shared__ __align__(16) u32x4_t st2[RTT_ROWS * 8];
+  const int t0 = blockIdx.x * RTT_M, e0 = blockIdx.y * RTT_N;
+  const int k0 = blockIdx.z * kc_steps * 64;
+  const size_t plane = (size_t)E * H;
+  RTile t;
+  t.nk = min(kc_steps, H / 64 - blockIdx.z * kc_steps);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < RTT_LOADS; ++i) {
+    const int row = w * RTT_LOADS * 8 + i * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ rswz(row);
+    const uint16_t* src;
+    if (row < RTT_M) {
+      src = x + (size_t)min(t0 + row, T - 1) * H;
+    } else {
+      const int pr = row - RTT_M, p = pr / RTT_N, j = pr % RTT_N;
+      src = planes + p * plane + (size_t)min(e0 + j, E - 1) * H;
+    }
+    t.p[i] = reinterpret_cast<const char*>(src + k0 + chunk * 8);
+  }
+  const int nk3 = (t.nk + 2) / 3 * 3;
+  floatx16_t acc[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[mb][v] = 0.f;
+  rt_issue(t, 0, st0);
+  rt_issue(t, 1, st1);
+  for (int j = 0; j < nk3; j += 3) {
+    RT_STEP(j + 2, st0, st2)
+    RT_STEP(j + 3, st1, st0)
+    RT_STEP(j + 4, st2, st1)
+  }
+  r_wait_vmcnt<0>();
+  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
+  float* out = part + (size_t)blockIdx.z * T * E;
+  const int e = e0 + wn * 32 + r;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tk = t0 + wm * 64 + mb * 32 + (v >> 2) * 8 + q * 4 + (v & 3);
+      if (tk < T && e < E) out[(size_t)tk * E + e] = acc[mb][v];
+    }
+}
+#undef RT_STEP
+
 inline int grid_blocks(size_t n) {
   size_t b = (n + 255) / 256;
   return (int)(b > 4096 ? 4096 : (b ? b : 1));
@@ -184,12 +325,22 @@ inline int grid_blocks(size_t n) {
 
 }  // namespace
 
-// K chunks of the bf16 router GEMM: enough workgroups to fill the chip, each
-// chunk a multiple of 64 elements that divides H.
+// The bf16 router plan: the tiled kernel for batches of at least 128 tokens
+// (else the per-wave kernel), and the number of K chunks: enough workgroups
+// to fill the chip, each chunk a whole number of 64-element steps (at least
+// three for the tiled kernel) that divides H.
+static bool router_tiled(int64_t T) { return T >= RTT_M; }
+
 int router_kchunks(int64_t T, int E, int H, int dtype) {
   if (dtype != MOE_BF16) return 1;
-  const int64_t tiles = ((T + RT_M - 1) / RT_M) * ((E + RT_N - 1) / RT_N);
   int kc = 1;
+  if (router_tiled(T)) {
+    const int64_t tiles = ((T + RTT_M - 1) / RTT_M) * ((E + RTT_N - 1) / RTT_N);
+    const int steps = H / 64;
+    while (tiles * kc * 2 <= 256 && steps % (2 * kc) == 0 && steps / (2 * kc) >= 3) kc *= 2;
+    return kc;
+  }
+  const int64_t tiles = ((T + RT_M - 1) / RT_M) * ((E + RT_N - 1) / RT_N);
   while (tiles * kc < 512 && H % (2 * kc * RT_KG) == 0) kc *= 2;
   return kc;
 }
@@ -216,9 +367,15 @@ hipError_t launch_router_logits(const void* x, const float* w_router, float* log
                        : logits;
   hipLaunchKernelGGL(router_split_kernel, dim3(grid_blocks(n)), dim3(256), 0, st, w_router, n,
                      planes);
-  dim3 grid((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N, kc);
-  hipLaunchKernelGGL(router_partial_kernel, grid, dim3(256), 0, st,
-                     static_cast<const uint16_t*>(x), planes, part, T, H, E, H / kc);
+  if (router_tiled(T)) {
+    dim3 grid((T + RTT_M - 1) / RTT_M, (E + RTT_N - 1) / RTT_N, kc);
+    hipLaunchKernelGGL(router_tile_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), planes, part, T, H, E, H / 64 / kc);
+  } else {
+    dim3 grid((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N, kc);
+    hipLaunchKernelGGL(router_partial_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), planes, part, T, H, E, H / kc);
+  }
   if (kc > 1) {
     const size_t m = (size_t)T * E;
     hipLaunchKernelGGL(router_reduce_kernel, dim3(grid_blocks(m)), dim3(256), 0, st, part, kc, m,
