@@ -5,8 +5,10 @@
 A step is one pass of the whole layer (router GEMM, routing, grouping,
 gate/up + activation, down + combine, output cast) over one batch of seeded
 synthetic inputs that are resident in HBM before timing starts. The stage
-entry points are called in order on one stream with HIP events around each
-call; the K timed steps are bracketed by device synchronisation.
+entry points are called in order on one stream; the step is captured once in
+a HIP graph and the K timed steps are replays of it (--graph off: eager
+calls), bracketed by device synchronisation. The per-stage breakdown comes
+from an eager pass with HIP events around each call.
 
 Prints ONE JSON line: tokens/s of the layer, its TFLOP/s (fraction of bf16
 MFMA peak) and GB/s (fraction of HBM peak), the roofline of the dominant
@@ -100,6 +102,10 @@ def main():
     ap.add_argument("--combine", choices=["atomic", "ordered"], default="ordered",
                     help="down-projection combine: fp32 atomics into the output rows, or "
                          "per-row expert outputs summed in a fixed order by moe_combine")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="time replays of the layer step captured once in a HIP graph (on) or "
+                         "eager calls of the entry points (off); the per-stage breakdown always "
+                         "comes from an eager pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -163,32 +169,49 @@ def main():
           for _ in range(args.steps)]
 
     def step(events=None):
-        rec = (lambda i: events[i].record(stream)) if events else (lambda i: None)
+        # the stream current at call time: the capture stream inside graph capture
+        st = torch.cuda.current_stream()
+        rec = (lambda i: events[i].record(st)) if events else (lambda i: None)
         rec(0)
-        moe.moe_router_logits(keys, T, x, wr, logits, ws, stream)
+        moe.moe_router_logits(keys, T, x, wr, logits, ws, st)
         rec(1)
-        moe.moe_route(keys, T, logits, b, idx, w, None, stream)
+        moe.moe_route(keys, T, logits, b, idx, w, None, st)
         rec(2)
-        moe.moe_permute(keys, T, idx, offs, sr, rp, ws, stream)
+        moe.moe_permute(keys, T, idx, offs, sr, rp, ws, st)
         rec(3)
-        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream)
+        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, st)
         rec(4)
-        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, stream)
+        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, st)
         rec(5)
-        moe.moe_combine(keys, T, acc, yp, rp, w, out, stream)
+        moe.moe_combine(keys, T, acc, yp, rp, w, out, st)
         rec(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # eager pass: per-stage HIP events, and the eager step time
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, s in enumerate(stages)}
+    if args.graph == "on":
+        # one layer step captured once; every replay runs all of its kernels
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    else:
+        ms = ms_eager
 
     # the same layer through the single entry point, for a cross-check
     for _ in range(2):
@@ -259,13 +282,13 @@ def main():
                    "num_experts_per_tok": k, "moe_intermediate_size": I,
                    "num_shared_experts": S, "shared_intermediate_size": Is,
                    "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"],
-                   "combine": args.combine},
+                   "combine": args.combine, "graph": args.graph},
         "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],
                   "bytes": alg["bytes"], "arith_intensity": ai,
                   "bound": "mfma" if ai >= ridge else "hbm",
                   "touched_experts": alg["touched"], "stage_ms": stage_ms,
-                  "ms_per_step_layer_forward": ms_lf},
+                  "ms_per_step_eager": ms_eager, "ms_per_step_layer_forward": ms_lf},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

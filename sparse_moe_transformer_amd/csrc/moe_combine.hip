@@ -3,41 +3,53 @@
 //                                                      by the down projection)
 //   y_perm != NULL: out[t] = acc[t] + sum_j w[t,j] * y_perm[row_pos[t*k+j]]
 //                   summed in j order, so the result does not depend on timing.
-// Each thread handles 4 consecutive columns of one token (H % 64 == 0).
+// Each thread handles 8 consecutive columns of one token (H % 64 == 0). The
+// k gathered rows are fetched in groups of 8 slots whose loads are all in
+// flight together; the sum still runs slot by slot in j order.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace {
 
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float (&v)[4]);
-template <>
-__device__ __forceinline__ void load4<float>(const float* p, float (&v)[4]) {
-  floatx4_t u = *reinterpret_cast<const floatx4_t*>(p);
-  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-}
-template <>
-__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
-  uint2 u = *reinterpret_cast<const uint2*>(p);
-  v[0] = bf16_bits_to_f32((uint16_t)(u.x & 0xFFFF));
-  v[1] = bf16_bits_to_f32((uint16_t)(u.x >> 16));
-  v[2] = bf16_bits_to_f32((uint16_t)(u.y & 0xFFFF));
-  v[3] = bf16_bits_to_f32((uint16_t)(u.y >> 16));
-}
+constexpr int CW = 8;      // columns per thread
+constexpr int KGROUP = 8;  // gathered rows in flight per thread
 
 template <typename T>
-__device__ __forceinline__ void store4(T* p, const float (&v)[4]);
+struct Vec8;
 template <>
-__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
-  *reinterpret_cast<floatx4_t*>(p) = floatx4_t{v[0], v[1], v[2], v[3]};
-}
+struct Vec8<float> {
+  typedef floatx4_t raw[2];
+  static __device__ __forceinline__ void load(const float* p, float (&v)[CW]) {
+    const floatx4_t a = *reinterpret_cast<const floatx4_t*>(p);
+    const floatx4_t b = *reinterpret_cast<const floatx4_t*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[CW]) {
+    *reinterpret_cast<floatx4_t*>(p) = floatx4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<floatx4_t*>(p + 4) = floatx4_t{v[4], v[5], v[6], v[7]};
+  }
+};
 template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float (&v)[4]) {
-  uint2 u;
-  u.x = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-  u.y = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
-}
+struct Vec8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[CW]) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[CW]) {
+    u32x4_t u;
+    u.x = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    u.y = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    u.z = f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
+    u.w = f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  }
+};
 
 template <typename T, bool GATHER>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ acc,
@@ -45,24 +57,37 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ row_pos,
                                                       const float* __restrict__ topk_w,
                                                       T* __restrict__ out, int T_, int H, int k) {
-  const size_t nq = (size_t)T_ * (H / 4);
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq;
+  const int per_row = H / CW;
+  const size_t n = (size_t)T_ * per_row;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const size_t t = i / (H / 4);
-    const int c = (int)(i - t * (H / 4)) * 4;
-    float v[4];
-    load4<float>(acc + t * H + c, v);
+    const size_t t = i / per_row;
+    const int c = (int)(i - t * per_row) * CW;
+    float v[CW];
+    Vec8<float>::load(acc + t * H + c, v);
     if (GATHER) {
-      for (int j = 0; j < k; ++j) {
-        const float w = topk_w[t * k + j];
-        const int p = row_pos[t * k + j];
-        float y[4];
-        load4<T>(y_perm + (size_t)p * H + c, y);
+      for (int j0 = 0; j0 < k; j0 += KGROUP) {
+        const int m = min(KGROUP, k - j0);
+        int p[KGROUP];
+        float w[KGROUP];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] += w * y[u];
+        for (int j = 0; j < KGROUP; ++j) {
+          p[j] = j < m ? row_pos[t * k + j0 + j] : 0;
+          w[j] = j < m ? topk_w[t * k + j0 + j] : 0.f;
+        }
+        float y[KGROUP][CW];
+#pragma unroll
+        for (int j = 0; j < KGROUP; ++j)
+          if (j < m) Vec8<T>::load(y_perm + (size_t)p[j] * H + c, y[j]);
+#pragma unroll
+        for (int j = 0; j < KGROUP; ++j)
+          if (j < m) {
+#pragma unroll
+            for (int u = 0; u < CW; ++u) v[u] += w[j] * y[j][u];
+          }
       }
     }
-    store4<T>(out + t * H + c, v);
+    Vec8<T>::store(out + t * H + c, v);
   }
 }
 
@@ -71,8 +96,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* acc, const void* y_perm, const int32_t* row_pos,
                           const float* topk_w, void* out, int T, int H, int k, int dtype,
                           hipStream_t st) {
-  const size_t nq = (size_t)T * (H / 4);
-  size_t blocks = (nq + 255) / 256;
+  const size_t n = (size_t)T * (H / CW);
+  size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   dim3 grid((unsigned)blocks), block(256);
   if (dtype == MOE_BF16) {
