@@ -188,21 +188,31 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   g.topk_w = topk_w;
   g.out = acc;
   g.y_perm = y_perm;
+  g.mt_routed = (int)((rows + BM - 1) / BM + (rows < d.E ? rows : d.E));
+  g.nt_routed = (d.H + 255) / 256;
+  g.gm_routed = 4;
   if (d.S) {
-    g.a = h_shared;
     g.ws0 = d.packed ? shared_slot(w_down, d, (size_t)d.H * d.I) : ws_down;
     g.mt_shared = (int)((d.T + BM - 1) / BM);
     g.nt_shared = (d.H + 255) / 256;
     g.gm_shared = 4;
+    if (y_perm) {
+      // fixed-order combine: shared rows (to acc) and routed rows (to y_perm)
+      // do not touch the same memory, so one launch takes both
+      g.a = h;
+      g.a_shared = h_shared;
+      g.w0 = w_down;
+      return hip_ok(launch_down_both(g, d.dtype, st));
+    }
+    g.a = h_shared;
     MOE_TRY(hip_ok(launch_down_shared(g, d.dtype, st)));
   } else {
     MOE_TRY(hip_ok(launch_fill_zero(acc, (size_t)d.T * d.H * 4, st)));
   }
+  g.mt_shared = 0;
+  g.nt_shared = 0;
   g.a = h;
   g.w0 = w_down;
-  g.mt_routed = (int)((rows + BM - 1) / BM + (rows < d.E ? rows : d.E));
-  g.nt_routed = (d.H + 255) / 256;
-  g.gm_routed = 4;
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 

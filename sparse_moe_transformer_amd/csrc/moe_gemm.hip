@@ -48,7 +48,9 @@ constexpr int NTHR = 256;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int LOADS_PER_STAGE = 12;  // per thread: 4 activation + 8 weight
 
-enum Kind { GATE_UP = 0, DOWN_SHARED = 1, DOWN_ROUTED = 2 };
+// DOWN_BOTH: shared tiles (stored to acc) then routed tiles (unweighted rows
+// to y_perm) in one launch; used with the fixed-order combine
+enum Kind { GATE_UP = 0, DOWN_SHARED = 1, DOWN_ROUTED = 2, DOWN_BOTH = 3 };
 
 // A 128-byte line of zeros: the source of the padding steps.
 __device__ __align__(128) uint32_t g_zero_line[32] = {};
@@ -277,7 +279,7 @@ __device__ __forceinline__ int acc_row(int mb, int v, int q) {
 
 template <int KIND>
 __device__ __forceinline__ int tile_count(const GemmArgs& g, const int* cum) {
-  if (KIND == GATE_UP) return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
+  if (KIND == GATE_UP || KIND == DOWN_BOTH) return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
   if (KIND == DOWN_SHARED) return g.mt_shared * g.nt_shared;
   return cum[g.E] * g.nt_routed;
 }
@@ -377,48 +379,33 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
     t.nk = H / (NCH * EPC);
     t.kseg = H * (int)sizeof(T);
     t.bstride_kb = 0;
-  } else if (KIND == DOWN_SHARED) {
-    const int Ks = g.S * g.Is;
-    const T* hs = static_cast<const T*>(g.a);
-    const T* wd = static_cast<const T*>(g.ws0);
+  } else {
+    // down: shared tiles read h_shared [T, S*Is] against the S shared down
+    // matrices [H, Is] (K segment s at ws_down + s*H*Is); routed tiles read
+    // h [T*k, I] against expert e's down matrix [H, I]
+    const bool sh = KIND == DOWN_SHARED || (KIND == DOWN_BOTH && t.shared);
+    const int Ks = sh ? g.S * g.Is : g.I;  // row length of the activations
+    const int ldb = sh ? g.Is : g.I;       // row length of a weight K segment
+    const T* act = static_cast<const T*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
+    const T* wd = sh ? static_cast<const T*>(g.ws0)
+                     : static_cast<const T*>(g.w0) + (size_t)t.e * H * g.I;
     t.n0 = nt * BR;
     t.N = H;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = a_row(j);
-      t.a[j] = reinterpret_cast<const char*>(hs + (size_t)(t.row0 + min(row, t.nrows - 1)) * Ks +
+      t.a[j] = reinterpret_cast<const char*>(act + (size_t)(t.row0 + min(row, t.nrows - 1)) * Ks +
                                              lane_chunk(row) * EPC);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = b_row(j);
-      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * g.Is +
+      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * ldb +
                                              lane_chunk(row) * EPC);
     }
     t.nk = Ks / (NCH * EPC);
-    t.kseg = g.Is * (int)sizeof(T);  // shared expert s: K in [s*Is, (s+1)*Is) ...
-    t.bstride_kb = (int)(((long)H * g.Is * (long)sizeof(T)) >> 10);  // ... at ws_down + s*H*Is
-  } else {
-    const int I = g.I;
-    const T* h = static_cast<const T*>(g.a);
-    const T* wd = static_cast<const T*>(g.w0) + (size_t)t.e * H * I;
-    t.n0 = nt * BR;
-    t.N = H;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = a_row(j);
-      t.a[j] = reinterpret_cast<const char*>(h + (size_t)(t.row0 + min(row, t.nrows - 1)) * I +
-                                             lane_chunk(row) * EPC);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = b_row(j);
-      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * I +
-                                             lane_chunk(row) * EPC);
-    }
-    t.nk = I / (NCH * EPC);
-    t.kseg = I * (int)sizeof(T);
-    t.bstride_kb = 0;
+    t.kseg = ldb * (int)sizeof(T);
+    t.bstride_kb = sh ? (int)(((long)H * g.Is * (long)sizeof(T)) >> 10) : 0;
   }
   t.nk3 = (t.nk + 2) / 3 * 3;
 }
@@ -460,18 +447,31 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   const int x = b % nx, slot = b / nx;
   const int gx = G / nx + (x < G % nx ? 1 : 0);
   const int before = x * (G / nx) + min(x, G % nx);  // workgroups on XCDs < x
-  const int lo = (int)((long)ntiles * before / G);
-  const int hi = (int)((long)ntiles * (before + gx) / G);
-  if (lo + slot >= hi) return;
-  // this workgroup's tiles are lo + slot + i * gx, i < n_my
-  const int n_my = (hi - lo - slot + gx - 1) / gx;
+  // In the combined down launch the shared tiles (K = S*I_s) and the routed
+  // tiles (K = I) are split over the XCDs separately, so every XCD gets its
+  // share of each kind and the same amount of work.
+  const int nsh = KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0;
+  const int nrt = ntiles - nsh;
+  const int slo = (int)((long)nsh * before / G), shi = (int)((long)nsh * (before + gx) / G);
+  const int rlo = (int)((long)nrt * before / G), rhi = (int)((long)nrt * (before + gx) / G);
+  const int ns_x = shi - slo, n_x = ns_x + (rhi - rlo);  // this XCD's tile list
+  if (slot >= n_x) return;
+  // this workgroup's tiles are entries slot + i * gx, i < n_my, of that list
+  const int n_my = (n_x - slot + gx - 1) / gx;
+  auto gtile = [&](int i) {
+    const int L = slot + i * gx;
+    return L < ns_x ? slo + L : nsh + rlo + (L - ns_x);
+  };
   for (int i = threadIdx.x; i < min(n_my, MAX_WG_TILES); i += NTHR)
-    places[i] = place_of<KIND>(g, offs, cum, lo + slot + i * gx);
+    places[i] = place_of<KIND>(g, offs, cum, gtile(i));
   __syncthreads();
   // the place of tile i (the last tile stands in for any i past the end)
+  // (workgroup-uniform: moved to scalar registers)
   auto place = [&](int i) -> int4 {
     i = min(i, n_my - 1);
-    return i < MAX_WG_TILES ? places[i] : place_of<KIND>(g, offs, cum, lo + slot + i * gx);
+    const int4 p = i < MAX_WG_TILES ? places[i] : place_of<KIND>(g, offs, cum, gtile(i));
+    return make_int4(__builtin_amdgcn_readfirstlane(p.x), __builtin_amdgcn_readfirstlane(p.y),
+                     __builtin_amdgcn_readfirstlane(p.z), __builtin_amdgcn_readfirstlane(p.w));
   };
 
   // Row ids are loaded one tile ahead, just before the first stage loads of
@@ -559,7 +559,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
             }
           }
       }
-    } else if (KIND == DOWN_SHARED) {
+    } else if (KIND == DOWN_SHARED || (KIND == DOWN_BOTH && cur.shared)) {
       float* base = static_cast<float*>(g.out) + (size_t)(cur.row0 + wm * 64) * g.H + cur.n0 +
                     wn * 128 + r;
       if (full_rows && cur.n0 + BR <= cur.N) {
@@ -587,13 +587,15 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
           }
       }
     } else {
-      if (threadIdx.x < BM) {
-        ep_tok[threadIdx.x] = ep_t;
-        ep_w[threadIdx.x] = ep_wt;
+      if (ATOMIC) {
+        if (threadIdx.x < BM) {
+          ep_tok[threadIdx.x] = ep_t;
+          ep_w[threadIdx.x] = ep_wt;
+        }
+        // raw barrier: only the LDS writes above must be complete
+        __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
       }
-      // raw barrier: only the LDS writes above must be complete
-      __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
       const bool full = full_rows && cur.n0 + BR <= cur.N;
       if (ATOMIC) {
 #pragma unroll
@@ -661,6 +663,10 @@ template <typename T, bool ATOMIC>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_kernel(GemmArgs g) {
   moe_gemm_body<T, DOWN_ROUTED, ATOMIC>(g);
 }
+template <typename T>
+__global__ void __launch_bounds__(NTHR) moe_down_kernel(GemmArgs g) {
+  moe_gemm_body<T, DOWN_BOTH, false>(g);
+}
 
 // ---------------------------------------------------------------------------
 // host-side launchers
@@ -700,6 +706,16 @@ hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st) {
     hipLaunchKernelGGL(moe_down_shared_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   else
     hipLaunchKernelGGL(moe_down_shared_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st) {
+  const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
+  if (n <= 0) return hipSuccess;
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(moe_down_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else
+    hipLaunchKernelGGL(moe_down_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 // Arguments of the grouped expert GEMMs (passed by value to the kernels).
 struct GemmArgs {
   const void* a;      // activations: x (gate/up), h (routed down), h_shared (shared down)
+  const void* a_shared;  // h_shared when shared and routed down tiles share a launch
   const void* w0;     // gate or down stacked weights [E_tot, ., .]
   const void* w1;     // up stacked weights
   const void* ws0;    // shared gate (or shared down) weights
@@ -30,6 +31,8 @@ size_t gemm_lds_bytes(int E);
 int gemm_bm();
 hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
+// shared and routed down tiles in one launch (fixed-order combine only)
+hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
 
 // router GEMM scratch: bf16 split planes of the router weight + K-chunk partials

@@ -6,6 +6,7 @@
 //  2. scan pass (one workgroup): per expert, the running count over chunks
 //     (column scan) and the exclusive scan over experts -> expert_offsets;
 //  3. scatter pass: pos = offsets[e] + rows of e in earlier chunks + rank.
+// Up to 1024 rows (decode batches) the same sort runs in one workgroup.
 // Nothing returns to the host; the result does not depend on timing.
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -101,6 +102,63 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __r
   row_pos[r] = pos;
 }
 
+// The whole counting sort in one workgroup, for at most 1024 rows (decode
+// batches): row = thread. rank = earlier rows with the same expert; counts in
+// LDS; exclusive scan over experts (E <= 1024, expert = thread); scatter.
+__global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx,
+                                                             int rows, int E,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_rows,
+                                                             int32_t* __restrict__ row_pos) {
+  __shared__ int ex[1024];
+  __shared__ int cnt[1024];
+  __shared__ int wsum[16];
+  const int t = threadIdx.x;
+  cnt[t] = 0;
+  const int my = t < rows ? idx[t] : -1;
+  ex[t] = my;
+  __syncthreads();
+  int rank = 0;
+  if (my >= 0) {
+    for (int j = 0; j < t; ++j) rank += (ex[j] == my);
+    atomicAdd(&cnt[my], 1);
+  }
+  __syncthreads();
+  const int c = t < E ? cnt[t] : 0;
+  const int lane = t & 63, wave = t >> 6;
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (t < 64) {
+    const int v = t < 16 ? wsum[t] : 0;
+    int vi = v;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(vi, off);
+      if (t >= off) vi += o;
+    }
+    if (t < 16) wsum[t] = vi - v;
+  }
+  __syncthreads();
+  const int excl = incl - c + wsum[wave];
+  if (t < E) {
+    cnt[t] = excl;  // every read of cnt happened before the barriers above
+    offsets[t] = excl;
+    if (t == E - 1) offsets[E] = excl + c;
+  }
+  __syncthreads();
+  if (my >= 0) {
+    const int pos = cnt[my] + rank;
+    sorted_rows[pos] = t;
+    row_pos[t] = pos;
+  }
+}
+
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -114,6 +172,11 @@ int permute_chunk_rows() { return CH; }
 hipError_t launch_permute(const int32_t* idx, int rows, int E, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* row_pos, int32_t* local_rank,
                           int32_t* chunk_hist, hipStream_t st) {
+  if (rows <= 1024) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, st, idx, rows, E, offsets,
+                       sorted_rows, row_pos);
+    return hipGetLastError();
+  }
   const int nch = (rows + CH - 1) / CH;
   hipLaunchKernelGGL(permute_chunk_kernel, dim3(nch), dim3(CH), E * sizeof(int), st, idx, rows,
                      E, local_rank, chunk_hist);
