@@ -549,6 +549,8 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
+            // whole groups of 8 rows past the tile's rows: a uniform skip
+            if (wm * 64 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
             const int m = wm * 64 + acc_row(mb, v, q);
             if (m >= cur.nrows) continue;
             T* p = base + (size_t)acc_row(mb, v, q) * ld;
@@ -576,6 +578,8 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
+            // whole groups of 8 rows past the tile's rows: a uniform skip
+            if (wm * 64 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
             const int m = wm * 64 + acc_row(mb, v, q);
             if (m >= cur.nrows) continue;
             float* p = base + (size_t)acc_row(mb, v, q) * g.H;
@@ -602,6 +606,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
+            if (!full && wm * 64 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
             const int m = wm * 64 + acc_row(mb, v, q);
             if (!full && m >= cur.nrows) continue;
             float* orow = static_cast<float*>(g.out) + (size_t)ep_tok[m] * g.H + cur.n0 + wn * 128 + r;
@@ -628,6 +633,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
+              if (wm * 64 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
               const int m = wm * 64 + acc_row(mb, v, q);
               if (m >= cur.nrows) continue;
               T* p = base + (size_t)acc_row(mb, v, q) * g.H;

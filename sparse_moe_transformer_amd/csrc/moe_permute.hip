@@ -10,6 +10,7 @@
 // Nothing returns to the host; the result does not depend on timing.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "moe_small_sort.h"
 
 namespace {
 
@@ -103,8 +104,7 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __r
 }
 
 // The whole counting sort in one workgroup, for at most 1024 rows (decode
-// batches): row = thread. rank = earlier rows with the same expert; counts in
-// LDS; exclusive scan over experts (E <= 1024, expert = thread); scatter.
+// batches).
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx,
                                                              int rows, int E,
                                                              int32_t* __restrict__ offsets,
@@ -113,50 +113,8 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   __shared__ int ex[1024];
   __shared__ int cnt[1024];
   __shared__ int wsum[16];
-  const int t = threadIdx.x;
-  cnt[t] = 0;
-  const int my = t < rows ? idx[t] : -1;
-  ex[t] = my;
-  __syncthreads();
-  int rank = 0;
-  if (my >= 0) {
-    for (int j = 0; j < t; ++j) rank += (ex[j] == my);
-    atomicAdd(&cnt[my], 1);
-  }
-  __syncthreads();
-  const int c = t < E ? cnt[t] : 0;
-  const int lane = t & 63, wave = t >> 6;
-  int incl = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  if (t < 64) {
-    const int v = t < 16 ? wsum[t] : 0;
-    int vi = v;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int o = __shfl_up(vi, off);
-      if (t >= off) vi += o;
-    }
-    if (t < 16) wsum[t] = vi - v;
-  }
-  __syncthreads();
-  const int excl = incl - c + wsum[wave];
-  if (t < E) {
-    cnt[t] = excl;  // every read of cnt happened before the barriers above
-    offsets[t] = excl;
-    if (t == E - 1) offsets[E] = excl + c;
-  }
-  __syncthreads();
-  if (my >= 0) {
-    const int pos = cnt[my] + rank;
-    sorted_rows[pos] = t;
-    row_pos[t] = pos;
-  }
+  ex[threadIdx.x] = threadIdx.x < rows ? idx[threadIdx.x] : -1;
+  block_sort_rows_1024(ex, rows, E, cnt, wsum, offsets, sorted_rows, row_pos);
 }
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {

@@ -13,16 +13,140 @@
 // last-ulp differences of two exp implementations to matter). Ties go to the
 // lower expert index, and the k indices are emitted in selection order.
 //
-// Lane l holds experts l, l+64, ... (NPL per lane). Each of the k rounds takes
-// the lane-local best candidate and reduces (key desc, index asc) across the
-// wave with xor shuffles; the winning lane retires its candidate.
+// Lane l holds experts l, l+64, ... (NPL per lane). Each of the k rounds
+// takes the lane-local best live candidate, reduces (key desc, index asc)
+// within rows of 16 lanes by DPP exchanges (xor 1, xor 2, half-row mirror,
+// row mirror: each pairs lanes symmetrically, so every lane ends with its
+// row's best), then combines the four row winners read with readlane. The
+// winner's lane retires it. No LDS round trip is involved.
 #include <float.h>
 #include <limits.h>
 
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "moe_small_sort.h"
 
 namespace {
+
+// fp64 -> uint64 with the same order (finite values; -0 is never formed:
+// keys are normalised with + 0.0)
+__device__ __forceinline__ uint64_t ordered_bits(double d) {
+  const uint64_t u = __double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+struct Cand {
+  uint64_t k;  // ordered key; 0 = no candidate
+  int i;       // expert index; INT_MAX = no candidate
+};
+
+__device__ __forceinline__ bool better(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(Cand& c) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)c.k, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(c.k >> 32), CTRL, 0xF, 0xF, false);
+  const int pi = __builtin_amdgcn_update_dpp(0, c.i, CTRL, 0xF, 0xF, false);
+  const uint64_t pk = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+  if (better(pk, pi, c.k, c.i)) {
+    c.k = pk;
+    c.i = pi;
+  }
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Routes token row Lrow (one wavefront): writes its k indices and weights
+// (lanes < k, in selection order) and, if ex_row is given, the indices there.
+template <int NPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
+                                            const float* __restrict__ bias, int E, int k,
+                                            int route_norm, float route_scale,
+                                            int32_t* __restrict__ idx_row,
+                                            float* __restrict__ w_row, int* ex_row,
+                                            int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  double key[NPL], sc[NPL];
+  bool live[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    if (live[i]) {
+      const double s = 1.0 / (1.0 + exp(-(double)Lrow[e]));
+      sc[i] = s;
+      key[i] = (s + (bias ? (double)bias[e] : 0.0)) + 0.0;
+    } else {
+      sc[i] = 0.0;
+      key[i] = 0.0;
+    }
+  }
+  double gsum = 0.0, my_g = 0.0;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    Cand c{0ull, INT_MAX};
+    // candidates are visited in ascending index, so '>' keeps the lowest
+    // index among equal keys
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      if (live[i]) {
+        const uint64_t o = ordered_bits(key[i]);
+        if (c.i == INT_MAX || o > c.k) {
+          c.k = o;
+          c.i = lane + 64 * i;
+        }
+      }
+    }
+    dpp_step<0xB1>(c);   // quad_perm [1,0,3,2]: lane ^ 1
+    dpp_step<0x4E>(c);   // quad_perm [2,3,0,1]: lane ^ 2
+    dpp_step<0x141>(c);  // row_half_mirror: i <-> 7 - i within 8 lanes
+    dpp_step<0x140>(c);  // row_mirror: i <-> 15 - i within 16 lanes
+    // the four rows' winners (uniform values)
+    uint64_t wk = 0;
+    int wi = INT_MAX;
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+      const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)c.k, 16 * row);
+      const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(c.k >> 32), 16 * row);
+      const int ri = __builtin_amdgcn_readlane(c.i, 16 * row);
+      const uint64_t rk = ((uint64_t)hi << 32) | lo;
+      if (better(rk, ri, wk, wi)) {
+        wk = rk;
+        wi = ri;
+      }
+    }
+    const int wl = wi & 63, wslot = wi >> 6;
+    double s_sel = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (i == wslot) {
+        s_sel = sc[i];
+        if (lane == wl) live[i] = false;
+      }
+    const double bs = readlane_f64(s_sel, wl);
+    gsum += bs;  // same order (j = 0..k-1) in every lane
+    if (lane == j) {
+      my_g = bs;
+      my_idx = wi;
+    }
+  }
+  if (lane < k) {
+    double w = my_g;
+    if (route_norm) w = gsum != 0.0 ? w / gsum : 0.0;
+    w *= (double)route_scale;
+    idx_row[lane] = my_idx;
+    w_row[lane] = (float)w;
+    if (ex_row) ex_row[lane] = my_idx;
+    if (counts) atomicAdd(counts + my_idx, 1);
+  }
+}
 
 template <int NPL>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
@@ -31,72 +155,28 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
                                                     int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out,
                                                     int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // the whole wave leaves together
-  const float* Lrow = logits + (size_t)t * E;
-  double key[NPL], sc[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) {
-      const double s = 1.0 / (1.0 + exp(-(double)Lrow[e]));
-      sc[i] = s;
-      key[i] = s + (bias ? (double)bias[e] : 0.0);
-    } else {
-      sc[i] = 0.0;
-      key[i] = -DBL_MAX;
-    }
-  }
-  bool live[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) live[i] = (lane + 64 * i) < E;
+  route_token<NPL>(logits + (size_t)t * E, bias, E, k, route_norm, route_scale,
+                   idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
+}
 
-  double gsum = 0.0, my_g = 0.0;
-  int my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    double bk = -DBL_MAX, bs = 0.0;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      // candidates are visited in ascending index, so '>' keeps the lowest
-      // index among equal keys
-      if (live[i] && (bi == INT_MAX || key[i] > bk)) {
-        bk = key[i];
-        bi = e;
-        bs = sc[i];
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const double os = __shfl_xor(bs, off);
-      const bool better = (oi != INT_MAX) && (bi == INT_MAX || ok > bk || (ok == bk && oi < bi));
-      if (better) {
-        bk = ok;
-        bi = oi;
-        bs = os;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i == bi) live[i] = false;
-    gsum += bs;  // same order (j = 0..k-1) in every lane
-    if (lane == j) {
-      my_g = bs;
-      my_idx = bi;
-    }
-  }
-  if (lane < k) {
-    double w = my_g;
-    if (route_norm) w = gsum != 0.0 ? w / gsum : 0.0;
-    w *= (double)route_scale;
-    idx_out[(size_t)t * k + lane] = my_idx;
-    w_out[(size_t)t * k + lane] = (float)w;
-    if (counts) atomicAdd(counts + my_idx, 1);
-  }
+// Decode batches (T*k <= 1024): routing and grouping in one workgroup of 16
+// waves. Wave w routes tokens w, w+16, ...; the chosen experts are kept in
+// LDS and sorted there (the same stable counting sort as moe_permute).
+template <int NPL>
+__global__ void __launch_bounds__(1024) route_permute_small_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+    int route_norm, float route_scale, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ row_pos) {
+  __shared__ int ex[1024];
+  __shared__ int cnt[1024];
+  __shared__ int wsum[16];
+  for (int t = threadIdx.x >> 6; t < T; t += 16)
+    route_token<NPL>(logits + (size_t)t * E, bias, E, k, route_norm, route_scale,
+                     idx_out + (size_t)t * k, w_out + (size_t)t * k, ex + t * k, nullptr);
+  block_sort_rows_1024(ex, T * k, E, cnt, wsum, offsets, sorted_rows, row_pos);
 }
 
 }  // namespace
@@ -116,5 +196,22 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
   else if (npl <= 8) MOE_ROUTE(8);
   else MOE_ROUTE(16);
 #undef MOE_ROUTE
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_small(const float* logits, const float* bias, int T, int E, int k,
+                                      int route_norm, float route_scale, int32_t* idx, float* w,
+                                      int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                      hipStream_t st) {
+  const int npl = (E + 63) / 64;
+#define MOE_RP(N)                                                                           \
+  hipLaunchKernelGGL(route_permute_small_kernel<N>, dim3(1), dim3(1024), 0, st, logits, bias, \
+                     T, E, k, route_norm, route_scale, idx, w, offsets, sorted_rows, row_pos)
+  if (npl <= 1) MOE_RP(1);
+  else if (npl <= 2) MOE_RP(2);
+  else if (npl <= 4) MOE_RP(4);
+  else if (npl <= 8) MOE_RP(8);
+  else MOE_RP(16);
+#undef MOE_RP
   return hipGetLastError();
 }

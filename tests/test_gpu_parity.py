@@ -197,3 +197,43 @@ def test_zero_tokens_is_a_no_op():
                           None, None, out, 0, ws)
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+@pytest.mark.parametrize("name", ["many_experts_k32", "one_token", "one_expert",
+                                  "k_eq_E_no_shared", "fp32_ragged", "clamp_swigluoai"])
+def test_layer_forward_small_batches(name):
+    """T*k <= 1024: the layer routes and groups in one workgroup; indices must
+    match the oracle bit for bit and the output the layer's bar, in both
+    combine modes."""
+    inp = _inputs(name)
+    cfg = inp.cfg
+    assert inp.x.shape[0] * cfg["num_experts_per_tok"] <= 1024
+    dev = Dev(inp)
+    for det in (1, 0):
+        res = dev.forward(deterministic=det)
+        check_routing(cfg, inp, res)
+        ref = O.moe_forward(inp, cfg, logits=res["logits"])
+        e = rel_err(res["out"], ref["out"])
+        say(f"[small] {name} det={det} rel err {e:.3e}")
+        assert e <= TOL[cfg["dtype"]]
+
+
+def test_layer_forward_exact_ties_small_batch():
+    """Host-built logits with exactly equal values through the single entry
+    point at a decode-sized batch (E=300, k=8, 64 tokens): lowest index wins,
+    indices in selection order."""
+    cfg = EDGE["e300_k8"]
+    inp = synth.generate(cfg, T=64)
+    dev = Dev(inp)
+    E, k, T = 300, 8, 64
+    rng = np.random.default_rng(11)
+    L = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[rng.choice(E, 20, replace=False)] = 0.25
+    dev.expert_bias = torch.from_numpy(b).cuda()
+    Ld = torch.from_numpy(L).cuda().reshape(-1)
+    res = dev.forward(deterministic=1, logits_in=Ld, want_logits=False)
+    _, keys, ridx, rw = O.route(L, b, k, "sigmoid", True, synth.layer_keys(cfg)["route_scale"])
+    assert O.boundary_gap(keys, k) == 0.0
+    assert np.array_equal(res["idx"], ridx)
+    assert np.allclose(res["w"], rw, rtol=1e-6, atol=0)
