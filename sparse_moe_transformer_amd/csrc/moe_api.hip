@@ -123,7 +123,9 @@ inline moe_status hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E
   } while (0)
 
 ActParams act_of(const moe_config* c) {
-  return ActParams{c->hidden_act, c->act_alpha, c->act_limit, c->act_beta};
+  if (c->hidden_act == MOE_ACT_SWIGLUOAI)
+    return ActParams{c->act_alpha, c->act_limit, c->act_limit, c->act_beta};
+  return ActParams{1.0f, INFINITY, INFINITY, 0.0f};  // silu
 }
 
 GemmArgs base_args(const moe_config* c, const Dims& d) {

@@ -29,10 +29,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // Expert activation on the fp32 accumulators (g = gate projection,
 // u = up projection). silu: g*sigmoid(g)*u. swigluoai: clamp g from above
 // and u on both sides at `limit`, then g*sigmoid(alpha*g)*(u+beta).
+//
+// Both are one branch-free formula,
+//   min(g, glimit) * sigmoid(alpha * min(g, glimit)) * (clamp(u, +-ulimit) + beta),
+// with silu as the case glimit = ulimit = +inf, alpha = 1, beta = 0 (every
+// step is then exact: min(g, inf) = g, 1*g = g, u + 0 = u), so the epilogues
+// carry no per-element branch.
 
 struct ActParams {
-  int kind;  // moe_hidden_act
-  float alpha, limit, beta;
+  float alpha, glimit, ulimit, beta;
 };
 
 // 1 / (1 + e^-z) with the hardware exp2 and reciprocal (about 1 ulp each);
@@ -42,12 +47,9 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 }
 
 __device__ __forceinline__ float act_apply(float g, float u, const ActParams& a) {
-  if (a.kind == MOE_ACT_SWIGLUOAI) {
-    float gc = fminf(g, a.limit);
-    float uc = fminf(fmaxf(u, -a.limit), a.limit);
-    return gc * sigmoid_f32(a.alpha * gc) * (uc + a.beta);
-  }
-  return g * sigmoid_f32(g) * u;
+  const float gc = fminf(g, a.glimit);
+  const float uc = fminf(fmaxf(u, -a.ulimit), a.ulimit);
+  return gc * sigmoid_f32(a.alpha * gc) * (uc + a.beta);
 }
 
 // ---------------------------------------------------------------------------

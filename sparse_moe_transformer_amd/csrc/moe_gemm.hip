@@ -34,6 +34,7 @@
 // the end of a tile (activation rows beyond the segment, weight rows beyond
 // N) load a valid clamped row; their results are never stored.
 #include "moe_common.h"
+#include "moe_gemm_common.h"
 #include "moe_kernels.h"
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
@@ -48,13 +49,6 @@ constexpr int NTHR = 256;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int LOADS_PER_STAGE = 12;  // per thread: 4 activation + 8 weight
 
-// DOWN_BOTH: shared tiles (stored to acc) then routed tiles (unweighted rows
-// to y_perm) in one launch; used with the fixed-order combine
-enum Kind { GATE_UP = 0, DOWN_SHARED = 1, DOWN_ROUTED = 2, DOWN_BOTH = 3 };
-
-// A 128-byte line of zeros: the source of the padding steps.
-__device__ __align__(128) uint32_t g_zero_line[32] = {};
-
 template <typename T>
 struct Elem;
 template <>
@@ -65,8 +59,6 @@ template <>
 struct Elem<float> {
   static constexpr int EPC = 4;
 };
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 #define MOE_LDS_STAGES                              \
   __shared__ __align__(16) u32x4_t lds_a0[BM * NCH]; \
@@ -82,13 +74,6 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int a_row(int j) { return (threadIdx.x >> 6) * 32 + 8 * j + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int b_row(int j) { return (threadIdx.x >> 6) * 64 + 8 * j + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int lane_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
-
-// vmcnt(n) with the other counters left alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // One tile: where its rows and weights are and how many K-steps it has.
 struct Tile {
@@ -206,77 +191,6 @@ __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* 
   }
 }
 
-// Grouped tile order: logical index b -> (m-slot, n-tile) with groups of gm
-// m-slots; inside a group the m-slot varies fastest.
-__device__ __forceinline__ void grouped_order(int b, int mt, int nt, int gm, int* m, int* n) {
-  const int per_group = gm * nt;
-  const int g = b / per_group;
-  const int first = g * gm;
-  const int gsize = min(gm, mt - first);
-  const int local = b - g * per_group;
-  *m = first + local % gsize;
-  *n = local / gsize;
-}
-
-// offs <- expert_offsets (E+1 ints); cum[e] = sum_{e'<e} ceil(n_e'/BM), e <= E
-__device__ void build_tile_prefix(const int32_t* __restrict__ offsets, int E, int* offs, int* cum) {
-  for (int e = threadIdx.x; e <= E; e += NTHR) offs[e] = offsets[e];
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (E + 63) / 64;
-    const int e0 = lane * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < E) local += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-    }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    int run = incl - local;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < E) {
-        cum[e] = run;
-        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      }
-    }
-    if (lane == 63) cum[E] = incl;
-  }
-}
-
-// the expert that owns routed m-slot `slot` (largest e with cum[e] <= slot;
-// it has cum[e+1] > slot, so it is not empty)
-__device__ __forceinline__ int owner(const int* cum, int E, int slot) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cum[mid] <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-template <typename T>
-__device__ __forceinline__ void store_out(T* p, float v);
-template <>
-__device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v) {
-  *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
-}
-template <>
-__device__ __forceinline__ void store_out<float>(float* p, float v) {
-  *p = v;
-}
-
-// Row (within the wave's 64 rows) of accumulator element v of block mb:
-// 32x32 MFMA lane l holds rows 8*(v/4) + 4*(l/32) + v%4 of column l%32.
-__device__ __forceinline__ int acc_row(int mb, int v, int q) {
-  return mb * 32 + (v >> 2) * 8 + q * 4 + (v & 3);
-}
-
 template <int KIND>
 __device__ __forceinline__ int tile_count(const GemmArgs& g, const int* cum) {
   if (KIND == GATE_UP || KIND == DOWN_BOTH) return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
@@ -324,14 +238,6 @@ __device__ __forceinline__ int4 place_of(const GemmArgs& g, const int* offs, con
   int shared, e, row0, nrows, nt;
   tile_place<KIND>(g, offs, cum, idx, &shared, &e, &row0, &nrows, &nt);
   return make_int4(row0, nrows | (shared << 16), e, nt);
-}
-
-// row / k for row ids (0 <= row < 2^31): multiply-high by floor(2^32 / k)
-// falls short by at most one, which the fix-up restores
-__device__ __forceinline__ int div_k(int row, int k, uint32_t kmagic) {
-  int t = (int)__umulhi((uint32_t)row, kmagic);
-  if ((t + 1) * k <= row) ++t;
-  return t;
 }
 
 // Tokens of this lane's 4 activation rows of routed gate/up tile p (global
@@ -435,33 +341,15 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   __shared__ float ep_w[BM];
   __shared__ int4 places[MAX_WG_TILES];
 
-  if (KIND != DOWN_SHARED) build_tile_prefix(g.offsets, g.E, offs, cum);
+  if (KIND != DOWN_SHARED) build_tile_prefix<BM>(g.offsets, g.E, offs, cum);
   __syncthreads();
   const int ntiles = tile_count<KIND>(g, cum);
-  // this workgroup's tiles: its XCD's contiguous range, walked with a stride
-  // of the number of workgroups on that XCD. Workgroups go to the nx XCDs
-  // round-robin; each XCD's range is proportional to its workgroup count, so
-  // the ranges cover every tile for any grid size.
-  const int G = gridDim.x, b = blockIdx.x;
-  const int nx = G < 8 ? G : 8;
-  const int x = b % nx, slot = b / nx;
-  const int gx = G / nx + (x < G % nx ? 1 : 0);
-  const int before = x * (G / nx) + min(x, G % nx);  // workgroups on XCDs < x
-  // In the combined down launch the shared tiles (K = S*I_s) and the routed
-  // tiles (K = I) are split over the XCDs separately, so every XCD gets its
-  // share of each kind and the same amount of work.
-  const int nsh = KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0;
-  const int nrt = ntiles - nsh;
-  const int slo = (int)((long)nsh * before / G), shi = (int)((long)nsh * (before + gx) / G);
-  const int rlo = (int)((long)nrt * before / G), rhi = (int)((long)nrt * (before + gx) / G);
-  const int ns_x = shi - slo, n_x = ns_x + (rhi - rlo);  // this XCD's tile list
-  if (slot >= n_x) return;
-  // this workgroup's tiles are entries slot + i * gx, i < n_my, of that list
-  const int n_my = (n_x - slot + gx - 1) / gx;
-  auto gtile = [&](int i) {
-    const int L = slot + i * gx;
-    return L < ns_x ? slo + L : nsh + rlo + (L - ns_x);
-  };
+  // this workgroup's tiles: its XCD's contiguous range (the shared down
+  // tiles of the combined down launch are split over the XCDs separately)
+  const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0);
+  const int n_my = wt.n_my;
+  if (n_my == 0) return;
+  auto gtile = [&](int i) { return wt.global(i); };
   for (int i = threadIdx.x; i < min(n_my, MAX_WG_TILES); i += NTHR)
     places[i] = place_of<KIND>(g, offs, cum, gtile(i));
   __syncthreads();
