@@ -35,7 +35,6 @@ hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
 
-
 // router GEMM scratch: bf16 split planes of the router weight + K-chunk partials
 int router_kchunks(int64_t T, int E, int H, int dtype);
 size_t router_ws_bytes(int64_t T, int E, int H, int dtype);
