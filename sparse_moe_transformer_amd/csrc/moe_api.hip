@@ -346,17 +346,12 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   }
   int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
   float* tw = topk_w_out ? topk_w_out : w.w;
-  if (T * d.k <= 1024) {
-    // decode batches: routing and grouping in one workgroup, one launch
-    MOE_TRY(hip_ok(launch_route_permute_small(logits, expert_bias, (int)T, d.E, d.k,
-                                              cfg->route_norm, cfg->route_scale, idx, tw,
-                                              w.offsets, w.sorted_rows, w.row_pos, st)));
-  } else {
-    MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
-                                cfg->route_scale, idx, tw, nullptr, st)));
-    MOE_TRY(hip_ok(launch_permute(idx, (int)(T * d.k), d.E, w.offsets, w.sorted_rows, w.row_pos,
-                                  w.local_rank, w.chunk_hist, st)));
-  }
+  // routing: one wavefront per token over many workgroups; grouping: one
+  // workgroup for decode batches (T*k <= 1024), else three small kernels
+  MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
+                              cfg->route_scale, idx, tw, nullptr, st)));
+  MOE_TRY(hip_ok(launch_permute(idx, (int)(T * d.k), d.E, w.offsets, w.sorted_rows, w.row_pos,
+                                w.local_rank, w.chunk_hist, st)));
   MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,
                      w.h_shared, st));
   void* yp = deterministic ? w.y_perm : nullptr;

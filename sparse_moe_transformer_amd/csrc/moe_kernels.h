@@ -46,11 +46,6 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
                         int32_t* counts, hipStream_t st);
 
 // permutation scratch: chunk histograms and per-row ranks
-// routing and grouping in one launch for T*k <= 1024 (decode batches)
-hipError_t launch_route_permute_small(const float* logits, const float* bias, int T, int E, int k,
-                                      int route_norm, float route_scale, int32_t* idx, float* w,
-                                      int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
-                                      hipStream_t st);
 int permute_chunk_rows();
 hipError_t launch_permute(const int32_t* idx, int rows, int E, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* row_pos, int32_t* local_rank,

@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_rows,
                                                              int32_t* __restrict__ row_pos) {
-  __shared__ int ex[1024];
+  __shared__ __align__(16) int ex[1024];
   __shared__ int cnt[1024];
   __shared__ int wsum[16];
   ex[threadIdx.x] = threadIdx.x < rows ? idx[threadIdx.x] : -1;

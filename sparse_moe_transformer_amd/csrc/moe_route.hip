@@ -24,7 +24,6 @@
 
 #include "moe_common.h"
 #include "moe_kernels.h"
-#include "moe_small_sort.h"
 
 namespace {
 
@@ -161,24 +160,6 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
                    idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
 }
 
-// Decode batches (T*k <= 1024): routing and grouping in one workgroup of 16
-// waves. Wave w routes tokens w, w+16, ...; the chosen experts are kept in
-// LDS and sorted there (the same stable counting sort as moe_permute).
-template <int NPL>
-__global__ void __launch_bounds__(1024) route_permute_small_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
-    int route_norm, float route_scale, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
-    int32_t* __restrict__ row_pos) {
-  __shared__ int ex[1024];
-  __shared__ int cnt[1024];
-  __shared__ int wsum[16];
-  for (int t = threadIdx.x >> 6; t < T; t += 16)
-    route_token<NPL>(logits + (size_t)t * E, bias, E, k, route_norm, route_scale,
-                     idx_out + (size_t)t * k, w_out + (size_t)t * k, ex + t * k, nullptr);
-  block_sort_rows_1024(ex, T * k, E, cnt, wsum, offsets, sorted_rows, row_pos);
-}
-
 }  // namespace
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
@@ -196,22 +177,5 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
   else if (npl <= 8) MOE_ROUTE(8);
   else MOE_ROUTE(16);
 #undef MOE_ROUTE
-  return hipGetLastError();
-}
-
-hipError_t launch_route_permute_small(const float* logits, const float* bias, int T, int E, int k,
-                                      int route_norm, float route_scale, int32_t* idx, float* w,
-                                      int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
-                                      hipStream_t st) {
-  const int npl = (E + 63) / 64;
-#define MOE_RP(N)                                                                           \
-  hipLaunchKernelGGL(route_permute_small_kernel<N>, dim3(1), dim3(1024), 0, st, logits, bias, \
-                     T, E, k, route_norm, route_scale, idx, w, offsets, sorted_rows, row_pos)
-  if (npl <= 1) MOE_RP(1);
-  else if (npl <= 2) MOE_RP(2);
-  else if (npl <= 4) MOE_RP(4);
-  else if (npl <= 8) MOE_RP(8);
-  else MOE_RP(16);
-#undef MOE_RP
   return hipGetLastError();
 }

@@ -1,9 +1,9 @@
 // Stable counting sort of up to 1024 routed rows by expert inside one
 // workgroup of 1024 threads (row = thread): the grouping step for decode
-// batches. ex[r] holds row r's expert (any value for r >= rows). Writes
-// expert_offsets [E+1] (exclusive scan of the counts), sorted_rows (rows of
-// expert 0 in ascending row order, then expert 1, ...) and row_pos (its
-// inverse). E <= 1024.
+// batches. ex[r] holds row r's expert (any value for r >= rows); ex is
+// 16-byte aligned. Writes expert_offsets [E+1] (exclusive scan of the
+// counts), sorted_rows (rows of expert 0 in ascending row order, then expert
+// 1, ...) and row_pos (its inverse). E <= 1024.
 #pragma once
 
 #include "moe_common.h"
@@ -18,7 +18,16 @@ __device__ __forceinline__ void block_sort_rows_1024(const int* ex, int rows, in
   const int my = t < rows ? ex[t] : -1;
   int rank = 0;  // earlier rows with the same expert
   if (my >= 0) {
-    for (int j = 0; j < t; ++j) rank += (ex[j] == my);
+    // four rows per LDS read (ex is 16-byte aligned); every lane of a wave
+    // reads the same address, a broadcast
+    const int4* ex4 = reinterpret_cast<const int4*>(ex);
+    const int n4 = t >> 2;
+#pragma unroll 4
+    for (int j = 0; j < n4; ++j) {
+      const int4 v = ex4[j];
+      rank += (v.x == my) + (v.y == my) + (v.z == my) + (v.w == my);
+    }
+    for (int j = n4 * 4; j < t; ++j) rank += (ex[j] == my);
     atomicAdd(&cnt[my], 1);
   }
   __syncthreads();

@@ -169,14 +169,19 @@ def test_deterministic_repeats_bitwise():
     assert np.array_equal(a["idx"], c["idx"]) and np.array_equal(a["w"], c["w"])
 
 
-def test_route_exact_ties_from_host_logits():
+# (E, k): E <= 256 selects by ranks, E > 256 by k rounds of wave reductions
+TIE_CASES = [(300, 8), (256, 8), (128, 8), (64, 6), (7, 3)]
+
+
+@pytest.mark.parametrize("E,k", TIE_CASES)
+def test_route_exact_ties_from_host_logits(E, k):
     """Host-built fp32 logits with exactly equal values: lowest index wins."""
-    cfg = synth.layer_keys(EDGE["e300_k8"])
-    E, k, T = 300, 8, 64
+    cfg = dict(synth.layer_keys(EDGE["e300_k8"]), num_experts=E, num_experts_per_tok=k)
+    T = 64
     rng = np.random.default_rng(7)
     L = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
     b = np.zeros(E, np.float32)
-    b[rng.choice(E, 20, replace=False)] = 0.25
+    b[rng.choice(E, min(20, E // 2), replace=False)] = 0.25
     Ld = torch.from_numpy(L).cuda()
     bd = torch.from_numpy(b).cuda()
     idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
@@ -218,18 +223,19 @@ def test_layer_forward_small_batches(name):
         assert e <= TOL[cfg["dtype"]]
 
 
-def test_layer_forward_exact_ties_small_batch():
+@pytest.mark.parametrize("E,k", TIE_CASES)
+def test_layer_forward_exact_ties_small_batch(E, k):
     """Host-built logits with exactly equal values through the single entry
-    point at a decode-sized batch (E=300, k=8, 64 tokens): lowest index wins,
-    indices in selection order."""
-    cfg = EDGE["e300_k8"]
+    point at a decode-sized batch (64 tokens): lowest index wins, indices in
+    selection order."""
+    cfg = dict(EDGE["e300_k8"], num_experts=E, num_experts_per_tok=k)
     inp = synth.generate(cfg, T=64)
     dev = Dev(inp)
-    E, k, T = 300, 8, 64
+    T = 64
     rng = np.random.default_rng(11)
     L = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
     b = np.zeros(E, np.float32)
-    b[rng.choice(E, 20, replace=False)] = 0.25
+    b[rng.choice(E, min(20, E // 2), replace=False)] = 0.25
     dev.expert_bias = torch.from_numpy(b).cuda()
     Ld = torch.from_numpy(L).cuda().reshape(-1)
     res = dev.forward(deterministic=1, logits_in=Ld, want_logits=False)
