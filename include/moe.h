@@ -7,7 +7,7 @@
  * "Architecture specification", MoE and Activation bullets):
  *
  *   L    = x . W_r^T                         router logits, fp32
- *   s    = sigmoid(L)                        scores
+ *   s    = sigmoid(L) (or softmax over E)    scores
  *   idx  = top-k of (s + expert_bias)        bias used for selection only;
  *                                            ties -> lower expert index;
  *                                            emitted in that order
@@ -52,8 +52,13 @@ typedef enum {
   MOE_ERR_HIP = 4          /* a HIP launch or API call failed */
 } moe_status;
 
-/* Scoring function: sigmoid (mlxcel #845 "Routing detail"); the HF doc also
- * names softmax scoring, which is not implemented (MOE_ERR_UNSUPPORTED). */
+/* Scoring function (the router's per-expert scores s from the logits L):
+ *   sigmoid: s_e = 1 / (1 + exp(-L_e))               (mlxcel #845 "Routing detail")
+ *   softmax: s_e = exp(L_e - max L) / sum_e' exp(L_e' - max L) over the E
+ *            routed experts                           (HF "AFMoE" doc, key
+ *            features: sigmoid- or softmax-based token-choice routing)
+ * Both are formed in fp64 from the fp32 logits; the selection bias, the
+ * gather of unbiased scores, route_norm and route_scale follow unchanged. */
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
 
 /* Expert activation: SiLU-SwiGLU (HF "AFMoE" doc, hidden_act "silu") or
@@ -104,8 +109,9 @@ moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
                              size_t ws_bytes, moe_stream_t stream);
 
 /* Routing (mlxcel #845 "Routing detail"; mlxcel #763 MoE bullet): sigmoid
- * scores, selection key s + expert_bias formed in fp64, top-k by (key desc,
- * index asc), weights from the unbiased scores, route_norm, route_scale.
+ * (or softmax) scores, selection key s + expert_bias formed in fp64, top-k by
+ * (key desc, index asc), weights from the unbiased scores, route_norm,
+ * route_scale.
  *   logits      [T,E] fp32
  *   expert_bias [E] fp32, or NULL (no bias)
  *   topk_idx    [T,k] int32 out, in selection order

@@ -46,7 +46,6 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
-  if (c->score_func == MOE_SCORE_SOFTMAX) return MOE_ERR_UNSUPPORTED;
   d->T = T;
   d->H = c->hidden_size;
   d->E = c->num_experts;
@@ -255,8 +254,9 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const float* logits,
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (expert_counts) MOE_TRY(hip_ok(launch_fill_zero(expert_counts, (size_t)d.E * 4, st)));
-  return hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
-                             cfg->route_scale, topk_idx, topk_w, expert_counts, st));
+  return hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->score_func,
+                             cfg->route_norm, cfg->route_scale, topk_idx, topk_w, expert_counts,
+                             st));
 }
 
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
@@ -348,8 +348,8 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   float* tw = topk_w_out ? topk_w_out : w.w;
   // routing: one wavefront per token over many workgroups; grouping: one
   // workgroup for decode batches (T*k <= 1024), else three small kernels
-  MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->route_norm,
-                              cfg->route_scale, idx, tw, nullptr, st)));
+  MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->score_func,
+                              cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st)));
   MOE_TRY(hip_ok(launch_permute(idx, (int)(T * d.k), d.E, w.offsets, w.sorted_rows, w.row_pos,
                                 w.local_rank, w.chunk_hist, st)));
   MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,

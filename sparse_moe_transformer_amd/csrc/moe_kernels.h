@@ -42,8 +42,8 @@ hipError_t launch_router_logits(const void* x, const float* w_router, float* log
                                 int H, int E, int dtype, void* ws, hipStream_t st);
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int route_norm, float route_scale, int32_t* idx, float* w,
-                        int32_t* counts, hipStream_t st);
+                        int score_func, int route_norm, float route_scale, int32_t* idx,
+                        float* w, int32_t* counts, hipStream_t st);
 
 // permutation scratch: chunk histograms and per-row ranks
 int permute_chunk_rows();

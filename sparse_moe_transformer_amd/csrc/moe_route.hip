@@ -4,7 +4,9 @@
 // specification", MoE bullet): sigmoid scores; a per-expert bias is added for
 // SELECTION only; the k chosen weights are gathered from the unbiased
 // scores, renormalised to sum to one (route_norm) and multiplied by
-// route_scale.
+// route_scale. Softmax scoring (HF "AFMoE" doc, key features: sigmoid or
+// softmax scores) replaces the sigmoid by exp(L - max L) / sum over the E
+// routed experts; the rest of the rule is the same.
 //
 // The selection key s + b is formed in fp64 from the fp32 logit, so that the
 // order of two keys is decided exactly the same way as by a float64
@@ -62,12 +64,25 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Wave-wide max / sum of a double by a fixed butterfly (every lane ends with
+// the same value; the order is the same on every call).
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 // Routes token row Lrow (one wavefront): writes its k indices and weights
 // (lanes < k, in selection order) and, if ex_row is given, the indices there.
 template <int NPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
                                             const float* __restrict__ bias, int E, int k,
-                                            int route_norm, float route_scale,
+                                            int score_func, int route_norm, float route_scale,
                                             int32_t* __restrict__ idx_row,
                                             float* __restrict__ w_row, int* ex_row,
                                             int32_t* __restrict__ counts) {
@@ -78,14 +93,32 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     live[i] = e < E;
-    if (live[i]) {
-      const double s = 1.0 / (1.0 + exp(-(double)Lrow[e]));
-      sc[i] = s;
-      key[i] = (s + (bias ? (double)bias[e] : 0.0)) + 0.0;
-    } else {
-      sc[i] = 0.0;
-      key[i] = 0.0;
+    sc[i] = live[i] ? (double)Lrow[e] : 0.0;
+  }
+  if (score_func == MOE_SCORE_SOFTMAX) {
+    double m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (live[i]) m = fmax(m, sc[i]);
+    m = wave_max_f64(m);
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      sc[i] = live[i] ? exp(sc[i] - m) : 0.0;
+      part += sc[i];
     }
+    const double den = wave_sum_f64(part);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sc[i] = sc[i] / den;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sc[i] = 1.0 / (1.0 + exp(-sc[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = live[i] ? (sc[i] + (bias ? (double)bias[e] : 0.0)) + 0.0 : 0.0;
+    if (!live[i]) sc[i] = 0.0;
   }
   double gsum = 0.0, my_g = 0.0;
   int my_idx = 0;
@@ -150,27 +183,28 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
 template <int NPL>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
-                                                    int k, int route_norm, float route_scale,
+                                                    int k, int score_func, int route_norm,
+                                                    float route_scale,
                                                     int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out,
                                                     int32_t* __restrict__ counts) {
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // the whole wave leaves together
-  route_token<NPL>(logits + (size_t)t * E, bias, E, k, route_norm, route_scale,
+  route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
                    idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
-                        int route_norm, float route_scale, int32_t* idx, float* w,
-                        int32_t* counts, hipStream_t st) {
+                        int score_func, int route_norm, float route_scale, int32_t* idx,
+                        float* w, int32_t* counts, hipStream_t st) {
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block), block(64 * waves_per_block);
   const int npl = (E + 63) / 64;
 #define MOE_ROUTE(N)                                                                        \
-  hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, st, logits, bias, T, E, k, route_norm, \
-                     route_scale, idx, w, counts)
+  hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, st, logits, bias, T, E, k, score_func, \
+                     route_norm, route_scale, idx, w, counts)
   if (npl <= 1) MOE_ROUTE(1);
   else if (npl <= 2) MOE_ROUTE(2);
   else if (npl <= 4) MOE_ROUTE(4);

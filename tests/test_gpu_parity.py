@@ -52,6 +52,17 @@ EDGE = {
                                moe_intermediate_size=64, num_shared_experts=1),
     "e300_k8": custom(T=257, hidden_size=128, num_experts=300, num_experts_per_tok=8,
                       moe_intermediate_size=64, num_shared_experts=1, route_scale=2.826),
+    # softmax scoring (HF "AFMoE" doc: sigmoid or softmax scores)
+    "softmax_norm": custom(T=150, hidden_size=128, num_experts=16, num_experts_per_tok=4,
+                           moe_intermediate_size=64, num_shared_experts=1,
+                           score_func="softmax", route_scale=1.5),
+    # the MiniMax-M2 router shape (256 experts, top-8; mlxcel #763 summary)
+    "m2_shape_softmax_nonorm": custom(T=40, hidden_size=128, num_experts=256,
+                                      num_experts_per_tok=8, moe_intermediate_size=64,
+                                      num_shared_experts=0, score_func="softmax",
+                                      route_norm=0, route_scale=2.0),
+    "m2_shape_sigmoid": custom(T=70, hidden_size=128, num_experts=256, num_experts_per_tok=8,
+                               moe_intermediate_size=64, num_shared_experts=1),
 }
 
 
@@ -173,10 +184,12 @@ def test_deterministic_repeats_bitwise():
 TIE_CASES = [(300, 8), (256, 8), (128, 8), (64, 6), (7, 3)]
 
 
+@pytest.mark.parametrize("score_func", ["sigmoid", "softmax"])
 @pytest.mark.parametrize("E,k", TIE_CASES)
-def test_route_exact_ties_from_host_logits(E, k):
+def test_route_exact_ties_from_host_logits(E, k, score_func):
     """Host-built fp32 logits with exactly equal values: lowest index wins."""
-    cfg = dict(synth.layer_keys(EDGE["e300_k8"]), num_experts=E, num_experts_per_tok=k)
+    cfg = dict(synth.layer_keys(EDGE["e300_k8"]), num_experts=E, num_experts_per_tok=k,
+               score_func=score_func)
     T = 64
     rng = np.random.default_rng(7)
     L = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
@@ -188,7 +201,7 @@ def test_route_exact_ties_from_host_logits(E, k):
     w = torch.empty(T * k, dtype=torch.float32, device="cuda")
     moe.moe_route(cfg, T, Ld, bd, idx, w)
     torch.cuda.synchronize()
-    _, keys, ridx, rw = O.route(L, b, k, "sigmoid", True, cfg["route_scale"])
+    _, keys, ridx, rw = O.route(L, b, k, score_func, True, cfg["route_scale"])
     assert O.boundary_gap(keys, k) == 0.0
     assert np.array_equal(idx.view(T, k).cpu().numpy(), ridx)
     assert np.allclose(w.view(T, k).cpu().numpy(), rw, rtol=1e-6, atol=0)
@@ -205,7 +218,8 @@ def test_zero_tokens_is_a_no_op():
 
 
 @pytest.mark.parametrize("name", ["many_experts_k32", "one_token", "one_expert",
-                                  "k_eq_E_no_shared", "fp32_ragged", "clamp_swigluoai"])
+                                  "k_eq_E_no_shared", "fp32_ragged", "clamp_swigluoai",
+                                  "softmax_norm", "m2_shape_softmax_nonorm"])
 def test_layer_forward_small_batches(name):
     """T*k <= 1024: the layer routes and groups in one workgroup; indices must
     match the oracle bit for bit and the output the layer's bar, in both

@@ -30,7 +30,7 @@ def _gold(name):
 
 
 def _logit(s):
-    return {"0": 0.0, "ln3": math.log(3.0), "-ln3": -math.log(3.0),
+    return {"0": 0.0, "ln2": math.log(2.0), "ln3": math.log(3.0), "-ln3": -math.log(3.0),
             "ln4": math.log(4.0), "-ln4": -math.log(4.0)}[s]
 
 
@@ -53,6 +53,55 @@ def test_softmax_scores():
     s = O.scores(L, "softmax")
     assert np.allclose(s.sum(-1), 1.0, rtol=0, atol=4 * ULP1)
     assert np.allclose(O.scores(np.zeros((1, 4)), "softmax"), 0.25, rtol=0, atol=0)
+
+
+def test_softmax_two_experts_is_sigmoid_of_the_difference():
+    """softmax(a, b)_0 = 1 / (1 + e^(b - a)) = sigmoid(a - b): the oracle's
+    softmax against its (separately pinned) sigmoid, a closed-form identity."""
+    rng = np.random.default_rng(3)
+    a, b = rng.normal(0, 4, 200), rng.normal(0, 4, 200)
+    s = O.scores(np.stack([a, b], axis=1), "softmax")
+    assert np.max(np.abs(s[:, 0] - O.sigmoid(a - b))) <= 4 * ULP1
+
+
+def test_softmax_shift_invariant_and_finite_for_large_logits():
+    """Subtracting the row maximum keeps large logits finite; adding a
+    constant to every logit leaves the scores unchanged."""
+    L = np.random.default_rng(4).normal(0, 3, (6, 9))
+    s = O.scores(L, "softmax")
+    s_big = O.scores(L + 800.0, "softmax")
+    assert np.all(np.isfinite(s_big))
+    assert np.max(np.abs(s_big - s)) <= 1e-12
+    # a planted mistake (no max subtraction) overflows at these logits
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(L + 800.0) / np.exp(L + 800.0).sum(-1, keepdims=True)
+    assert not np.all(np.isfinite(naive))
+
+
+def test_softmax_route_norm_cancels_the_full_normaliser():
+    """With route_norm on, softmax weights equal route_scale times the softmax
+    over the k chosen logits alone (the sum over all E experts cancels)."""
+    rng = np.random.default_rng(5)
+    L = rng.normal(0, 2, (40, 16))
+    b = rng.uniform(-0.05, 0.05, 16)
+    _, _, idx, w = O.route(L, b, 4, "softmax", True, 2.5)
+    Ls = np.take_along_axis(L, idx.astype(np.int64), axis=1)
+    ez = np.exp(Ls - Ls.max(axis=1, keepdims=True))
+    assert np.max(np.abs(w - 2.5 * ez / ez.sum(axis=1, keepdims=True))) <= 1e-14
+
+
+def test_route_softmax_hand_example():
+    g = _gold("route_softmax_hand_example.json")
+    for case in g["cases"]:
+        L = np.array([[_logit(v) for v in case["logits"]]])
+        b = np.array(case["bias"], dtype=np.float64)
+        s, keys, idx, w = O.route(L, b, g["k"], "softmax", case["route_norm"], g["route_scale"])
+        assert np.allclose(s[0], case["scores"], rtol=0, atol=4 * ULP1), case["what"]
+        assert idx[0].tolist() == case["idx"], case["what"]
+        assert np.allclose(w[0], case["w"], rtol=8 * ULP1, atol=0), case["what"]
+        if "idx_without_bias" in case:
+            _, _, idx0, _ = O.route(L, None, g["k"], "softmax", True, g["route_scale"])
+            assert idx0[0].tolist() == case["idx_without_bias"]
 
 
 # --------------------------------------------------------------------------
