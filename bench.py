@@ -56,6 +56,19 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
                 gate_up_bytes=gate_up_bytes)
 
 
+GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_common.h", "moe_common.h", "moe_kernels.h")
+
+
+def gemm_source_sha() -> str:
+    """Fingerprint of the grouped-GEMM kernel's sources (a traffic figure taken
+    on other sources is stale)."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_transformer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel: str, src_sha: str, units: float):
     """HBM bytes per launch of `kernel` from the committed PMC summary, or None
     if the summary is missing or was taken on another version of the source."""
@@ -68,6 +81,104 @@ def traffic_from_profile(kernel: str, src_sha: str, units: float):
     if not rec or rec.get("source_sha256") != src_sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (no GPU needed): the text files under profiles/
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name: str) -> str:
+    """Kernel name without template arguments and parameter list."""
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    n = n.split("(")[0].split("<")[0].strip()
+    if n.startswith("_Z"):  # mangled: _Z<len><name>...
+        i = 2
+        while i < len(n) and n[i].isdigit():
+            i += 1
+        ln = int(n[2:i]) if i > 2 else 0
+        n = n[i:i + ln] if ln else n
+    return n
+
+
+def summarize_trace(d: str) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` run (per kernel:
+    calls, average / min / max duration, share of GPU time)."""
+    rows = _csv_rows(d, "kernel_stats.csv")
+    agg = {}
+    for r in rows:
+        k = _short(r["Name"])
+        a = agg.setdefault(k, [0, 0.0, float("inf"), 0.0])
+        a[0] += int(r["Calls"])
+        a[1] += float(r["TotalDurationNs"])
+        a[2] = min(a[2], float(r["MinNs"]))
+        a[3] = max(a[3], float(r["MaxNs"]))
+    total = sum(a[1] for a in agg.values()) or 1.0
+    out = ["| kernel | calls | avg us | min us | max us | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for k, a in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {k} | {a[0]} | {a[1] / a[0] / 1e3:.1f} | {a[2] / 1e3:.1f} | "
+                   f"{a[3] / 1e3:.1f} | {100 * a[1] / total:.1f}% |")
+    return "\n".join(out)
+
+
+def _pmc_means(d: str, counter: str) -> dict:
+    """Mean value of one PMC counter per kernel (short name) over dispatches."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_traffic(d: str, kernel: str = "moe_gate_up_kernel") -> str:
+    """HBM traffic per launch from two `rocprofv3 --pmc` runs of the bench
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) scaled by what the same
+    counters read for a plain copy of known size; writes profiles/traffic.json
+    for the bench's roofline object and returns a markdown summary. Expects
+    d/bench.json (the bench line of the same workload), d/pmc_FETCH_SIZE,
+    d/pmc_WRITE_SIZE, d/cal_FETCH_SIZE, d/cal_WRITE_SIZE (rocprofv3 outputs)."""
+    with open(os.path.join(d, "bench.json")) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    fetch = _pmc_means(os.path.join(d, "pmc_FETCH_SIZE"), "FETCH_SIZE")
+    write = _pmc_means(os.path.join(d, "pmc_WRITE_SIZE"), "WRITE_SIZE")
+    cal_f = _pmc_means(os.path.join(d, "cal_FETCH_SIZE"), "FETCH_SIZE")
+    cal_w = _pmc_means(os.path.join(d, "cal_WRITE_SIZE"), "WRITE_SIZE")
+    copy_bytes = 256 * 1024 * 1024
+    ck = [k for k in cal_f if "copy" in k.lower()]
+    if not ck:
+        raise SystemExit(f"no copy kernel in the calibration run: {sorted(cal_f)}")
+    f_scale = copy_bytes / (cal_f[ck[0]] * 1024)
+    w_scale = copy_bytes / (cal_w[ck[0]] * 1024)
+    alg = line["layer"]["gate_up_bytes"]
+    hbm = fetch[kernel] * 1024 * f_scale + write[kernel] * 1024 * w_scale
+    rec = {kernel: {"workload": line["config"]["workload"], "source_sha256": gemm_source_sha(),
+                    "fetch_kib": fetch[kernel], "write_kib": write[kernel],
+                    "fetch_scale": f_scale, "write_scale": w_scale,
+                    "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg}}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    out = [f"Calibration: a plain copy of 256 MiB reads FETCH_SIZE = {cal_f[ck[0]]:.0f} KiB "
+           f"and WRITE_SIZE = {cal_w[ck[0]]:.0f} KiB per dispatch, so counter values are "
+           f"scaled by {f_scale:.3f} (fetch) and {w_scale:.3f} (write) to get bytes.", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+           "|---|---|---|---|---|"]
+    for k in sorted(set(fetch) | set(write)):
+        fk, wk = fetch.get(k, 0.0), write.get(k, 0.0)
+        out.append(f"| {k} | {fk:.0f} | {wk:.0f} | {fk * 1024 * f_scale / 1e6:.1f} | "
+                   f"{wk * 1024 * w_scale / 1e6:.1f} |")
+    out += ["", f"{kernel}: {hbm / 1e6:.0f} MB moved per launch against {alg / 1e6:.0f} MB "
+                f"algorithmic: ratio {hbm / alg:.2f}."]
+    return "\n".join(out)
 
 
 def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
@@ -110,7 +221,18 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 kernel-trace run and exit")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs (see "
+                         "summarize_traffic), write profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(args.summarize_traffic))
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -229,6 +351,24 @@ def main():
     else:
         ms = ms_eager
 
+    # HBM-cold steps: before each, write a 1 GiB buffer (more than the 256 MB
+    # MALL), then time only the layer call with events on the same stream,
+    # so expert weights come from HBM (what a multi-layer model sees: every
+    # layer's weights differ)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    n_cold = max(3, min(args.steps, 10))
+    cold = []
+    for _ in range(n_cold):
+        flush.fill_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        layer()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    del flush
+    ms_cold = float(np.median(cold))
+
     idx_h = idx.view(T, k).cpu().numpy()
     alg = algorithmic(cfg, T, idx_h)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
@@ -249,8 +389,7 @@ def main():
     r1.record(stream)
     torch.cuda.synchronize()
     gu_ms = r0.elapsed_time(r1) / n_rl
-    src = open(os.path.join(ROOT, "sparse_moe_transformer_amd", "csrc", "moe_gemm.hip"), "rb").read()
-    sha = hashlib.sha256(src).hexdigest()
+    sha = gemm_source_sha()
     gu_ai = alg["gate_up_flops"] / alg["gate_up_bytes"]
     if gu_ai >= ridge:
         roof = {"bound": "mfma", "achieved": alg["gate_up_flops"] / (gu_ms * 1e-3) / 1e12,
@@ -290,9 +429,13 @@ def main():
         "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],
                   "bytes": alg["bytes"], "arith_intensity": ai,
+                  "gate_up_flops": alg["gate_up_flops"], "gate_up_bytes": alg["gate_up_bytes"],
                   "bound": "mfma" if ai >= ridge else "hbm",
                   "touched_experts": alg["touched"], "stage_ms": stage_ms,
-                  "ms_per_step_eager": ms_eager, "ms_per_step_stage_calls": ms_stages},
+                  "ms_per_step_eager": ms_eager, "ms_per_step_stage_calls": ms_stages,
+                  "ms_per_step_hbm_cold": ms_cold,
+                  "gbs_hbm_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9,
+                  "frac_hbm_peak_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
