@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "moe.h"
@@ -145,6 +146,19 @@ const void* shared_slot(const void* stacked, const Dims& d, size_t per_expert_el
   return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.es;
 }
 
+// Grouped-GEMM tile choice. Decode-sized batches (at most 32 rows per expert
+// on average) stream expert weights: the 32-row tile kernel keeps more weight
+// K-steps in flight per compute unit. MOE_GEMM_TILE=32 or =128 forces one
+// kernel (a testing knob; 32 still needs bf16 and gemm_decode_fits).
+bool use_decode(const Dims& d) {
+  if (d.dtype != MOE_BF16 || !gemm_decode_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
+  if (const char* e = std::getenv("MOE_GEMM_TILE")) {
+    if (std::strcmp(e, "128") == 0) return false;
+    if (std::strcmp(e, "32") == 0) return true;
+  }
+  return d.T * d.k <= (int64_t)32 * d.E;
+}
+
 // --- stages (arguments already checked) ---
 
 moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
@@ -152,7 +166,8 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
                       const int32_t* offsets, const int32_t* sorted_rows, void* h,
                       void* h_shared, hipStream_t st) {
   GemmArgs g = base_args(c, d);
-  const int BM = gemm_bm();
+  const bool dec = use_decode(d);
+  const int BM = dec ? gemm_decode_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
   g.a = x;
   g.w0 = w_gate;
@@ -174,6 +189,7 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
   g.nt_shared = d.S ? (d.S * d.Is + 127) / 128 : 0;
   g.gm_routed = 8;
   g.gm_shared = 8;
+  if (dec) return hip_ok(launch_gate_up_decode(g, st));
   return hip_ok(launch_gate_up(g, d.dtype, st));
 }
 
@@ -182,7 +198,8 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
                    const int32_t* sorted_rows, const float* topk_w, float* acc, void* y_perm,
                    hipStream_t st) {
   GemmArgs g = base_args(c, d);
-  const int BM = gemm_bm();
+  const bool dec = use_decode(d);
+  const int BM = dec ? gemm_decode_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
   g.offsets = offsets;
   g.sorted_rows = sorted_rows;
@@ -203,10 +220,11 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
       g.a = h;
       g.a_shared = h_shared;
       g.w0 = w_down;
+      if (dec) return hip_ok(launch_down_both_decode(g, st));
       return hip_ok(launch_down_both(g, d.dtype, st));
     }
     g.a = h_shared;
-    MOE_TRY(hip_ok(launch_down_shared(g, d.dtype, st)));
+    MOE_TRY(hip_ok(dec ? launch_down_shared_decode(g, st) : launch_down_shared(g, d.dtype, st)));
   } else {
     MOE_TRY(hip_ok(launch_fill_zero(acc, (size_t)d.T * d.H * 4, st)));
   }
@@ -214,6 +232,7 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   g.nt_shared = 0;
   g.a = h;
   g.w0 = w_down;
+  if (dec) return hip_ok(launch_down_routed_decode(g, y_perm == nullptr, st));
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 

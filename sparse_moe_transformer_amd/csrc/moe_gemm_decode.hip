@@ -1,0 +1,515 @@
+// Grouped expert GEMMs for decode-sized batches (bf16, gfx950): 32-row tiles.
+//
+// Same operands, tile order and outputs as the 128-row kernel in
+// moe_gemm.hip (stacked [out, in] expert weights, mlxcel #845 "Checkpoint
+// weight layout"; activation rows gathered by sorted_rows). With a handful of
+// rows per expert the work is a stream of expert weights, so the tile is 32
+// activation rows x 256 weight rows and the LDS holds four stages of 36 KiB
+// (32 + 256 rows x 128 B of K): three K-steps of weights are in flight while
+// one is computed, against two with the 128-row tile's 48 KiB stages.
+//
+// Four waves each own the 32 rows x 64 weight rows: for gate/up, 32 gate and
+// the 32 up rows of the same columns (the activation is applied in
+// registers); for down, 64 output columns. Two 32x32x16 bf16 MFMAs per
+// sub-step.
+//
+// Persistent schedule and tile order as in moe_gemm.hip. Every K length is
+// a multiple of four K-steps (256 elements; the host falls back to the
+// 128-row kernel otherwise); the last three steps of a tile load the next
+// tile's first three stages. Every store of an epilogue is
+// a buffer store whose offset is pushed past the buffer's range when the
+// element is outside the tile, so each wave issues a fixed number of vector
+// memory operations per tile and the load-counter waits of a tile's first
+// steps can let the previous epilogue's stores stay in flight.
+#include "moe_common.h"
+#include "moe_gemm_common.h"
+#include "moe_kernels.h"
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int DBM = 32;        // activation rows per tile
+constexpr int DBR = 256;       // weight rows per tile
+constexpr int NCH = 8;         // 16-byte chunks per LDS row per K-step
+constexpr int KSB = NCH * 16;  // bytes per row per K-step
+constexpr int NTHR = 256;
+constexpr int NST = 4;         // LDS stages
+constexpr int LOADS = 9;       // per thread per stage: 1 activation + 8 weight
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_WG_TILES = 128;
+constexpr int EPI_GU = 16;     // vector memory ops of a gate/up epilogue (per thread)
+constexpr int EPI_DN = 32;     // ... of a down epilogue
+
+#define DEC_LDS_STAGES                                \
+  __shared__ __align__(16) u32x4_t lds_a0[DBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_a1[DBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_a2[DBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_a3[DBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b0[DBR * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b1[DBR * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b2[DBR * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b3[DBR * NCH];
+
+// Wave w loads activation rows 8w .. 8w+7 (one instruction) and weight rows
+// 64w + 8j .. +7 (instruction j < 8); the lane's row is that base + lane/8
+// and it fetches the logical chunk that lands at physical chunk lane % 8.
+__device__ __forceinline__ int a_row() { return 8 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int b_row(int j) {
+  return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3);
+}
+__device__ __forceinline__ int lane_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
+
+// Direct global->LDS loads (global_load_lds_dword / _dwordx4: each lane's
+// bytes land at LDS address m0 + lane * size), issued from inline assembly so
+// that the compiler does not track them: its tracking merges pending LDS
+// writes conservatively at every join and then waits for all loads before the
+// next LDS read. All waits for these loads are the explicit vmcnt waits and
+// barriers of the step loop. Every direct load of this kernel goes through
+// these two functions, so the compiler itself never relies on m0 here.
+// a wave-uniform pointer, moved to scalar registers
+__device__ __forceinline__ const char* sptr(const char* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, const void* lds) {
+  const char* sbase = sptr(base);
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(l)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const char* base, uint32_t voff, const void* lds) {
+  const char* sbase = sptr(base);
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(l)
+               : "memory");
+}
+
+// Loads use a scalar base that advances with the K-step and a 32-bit per-lane
+// offset fixed for the whole tile: the offset registers stay live, so the
+// compiler never reuses a load's address registers while the load is in
+// flight (a reuse it would guard with a wait for every load).
+struct DTile {
+  const char* abase;  // activations (x, h or h_shared)
+  const char* bbase;  // this wave's weight matrix (gate or up rows for gate/up)
+  uint32_t aoff;      // this lane's activation row + chunk, bytes from abase
+  uint32_t boff[8];   // this lane's weight rows + chunks, bytes from bbase
+  int nk;             // K-steps (a multiple of 4)
+  int kseg;           // weight K segment length in bytes (K-split of shared down)
+  int bstride;        // bytes between weight K segments (0: one segment)
+  int shared, e, row0, nrows, n0, N;
+};
+
+// The 9 loads of this lane for step j of tile t into stage (la, lb). Every
+// K length is a multiple of four steps (the host checks), so there are no
+// padding steps and no branch here: a branch would merge two load states
+// and make the compiler wait for every load before the next LDS read.
+__device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, u32x4_t* lb) {
+  const int w = threadIdx.x >> 6;
+  const long kb = (long)j * KSB;
+  long bk = kb;
+  if (t.bstride) {
+    const long seg = kb / t.kseg;
+    bk = seg * t.bstride + (kb - seg * t.kseg);
+  }
+  const char* ab = t.abase + kb;
+  const char* bb = t.bbase + bk;
+  dma16(ab, t.aoff, la + 8 * w * NCH);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
+}
+
+// First weight row (within the 256-row tile) of block nb (0..1) of wave w.
+template <int KIND>
+__device__ __forceinline__ int wrow(int w, int nb) {
+  if (KIND == GATE_UP) return nb == 0 ? 32 * w : 128 + 32 * w;
+  return 64 * w + 32 * nb;
+}
+
+typedef floatx16_t Acc2[2];
+
+// One K-step (4 sub-steps of K = 16): lane l reads row l%32, chunk 2s + l/32.
+template <int KIND>
+__device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, la[r * NCH + ((2 * s + q) ^ swz(r))]);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = wrow<KIND>(w, nb) + r;
+      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[nb], 0, 0, 0);
+    }
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ int tile_count(const GemmArgs& g, const int* cum) {
+  if (KIND == DOWN_SHARED) return g.mt_shared * g.nt_shared;
+  if (KIND == DOWN_ROUTED) return cum[g.E] * g.nt_routed;
+  return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
+}
+
+// Where tile `idx` is: row0 (x), nrows | shared << 16 (y), expert (z),
+// n-tile (w). Offsets and the prefix are in LDS.
+template <int KIND>
+__device__ __forceinline__ int4 place_of(const GemmArgs& g, const int* offs, const int* cum,
+                                         int idx) {
+  const int nshared = KIND == DOWN_ROUTED ? 0 : g.mt_shared * g.nt_shared;
+  int mt, nt, e = 0, row0, nrows, shared;
+  if (idx < nshared) {
+    shared = 1;
+    grouped_order(idx, g.mt_shared, g.nt_shared, g.gm_shared, &mt, &nt);
+    row0 = mt * DBM;
+    nrows = min(DBM, g.T - row0);
+  } else {
+    shared = 0;
+    const int t = idx - nshared;
+    e = owner(cum, g.E, t / g.nt_routed);
+    const int ms = cum[e + 1] - cum[e];
+    grouped_order(t - cum[e] * g.nt_routed, ms, g.nt_routed, g.gm_routed, &mt, &nt);
+    row0 = offs[e] + mt * DBM;
+    nrows = min(DBM, offs[e + 1] - row0);
+  }
+  return make_int4(row0, nrows | (shared << 16), e, nt);
+}
+
+// Row ids of a tile's (up to 32) activation rows, gathered by wave 0 straight
+// into LDS (dst: 64 ints) with one direct global->LDS load, a tile ahead of
+// their use. Kept out of registers on purpose: a register loaded from memory
+// in one tile and read in the next makes the compiler drain every load in
+// flight before the read. Lanes past the tile's rows repeat its last row.
+__device__ __forceinline__ void gather_rows(const GemmArgs& g, int4 p, int* dst) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63;
+  const int nrows = p.y & 0xFFFF;
+  dma4(reinterpret_cast<const char*>(g.sorted_rows),
+       (uint32_t)(p.x + min(lane, nrows - 1)) * 4u, dst);
+}
+
+// The token of this lane's activation row of gate/up tile p (rows: the tile's
+// gathered row ids in LDS).
+__device__ __forceinline__ int token_of(const GemmArgs& g, int4 p, const int* rows) {
+  const int row0 = p.x, nrows = p.y & 0xFFFF, shared = p.y >> 16;
+  const int R = min(a_row(), nrows - 1);
+  return shared ? row0 + R : div_k(rows[R], g.k, g.kmagic);
+}
+
+// tok: gate/up only, the token of this lane's activation row (token_of).
+template <int KIND>
+__device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DTile& t) {
+  constexpr int EPC = 8;
+  const int H = g.H;
+  t.row0 = p.x;
+  t.nrows = p.y & 0xFFFF;
+  t.shared = p.y >> 16;
+  t.e = p.z;
+  const int nt = p.w;
+  const int row = a_row();
+  const int w = threadIdx.x >> 6;
+  if (KIND == GATE_UP) {
+    t.n0 = nt * 128;
+    t.N = t.shared ? g.S * g.Is : g.I;
+    t.abase = static_cast<const char*>(g.a);
+    t.aoff = ((uint32_t)tok * (uint32_t)H + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
+    // waves 0, 1 load gate rows (weight rows 0..127), waves 2, 3 the up rows
+    const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? g.ws0 : g.w0)
+                                                    : (t.shared ? g.ws1 : g.w1));
+    t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * H * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int br = b_row(j);
+      const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
+      t.boff[j] = (n * (uint32_t)H + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+    }
+    t.nk = H / (NCH * EPC);
+    t.kseg = H * 2;
+    t.bstride = 0;
+  } else {
+    // down: shared tiles read h_shared [T, S*Is] against the S shared down
+    // matrices [H, Is] (K segment s at ws_down + s*H*Is); routed tiles read
+    // h [T*k, I] against expert e's down matrix [H, I]
+    const bool sh = KIND == DOWN_SHARED || (KIND == DOWN_BOTH && t.shared);
+    const int Ks = sh ? g.S * g.Is : g.I;
+    const int ldb = sh ? g.Is : g.I;
+    t.abase = static_cast<const char*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
+    t.bbase = sh ? static_cast<const char*>(g.ws0)
+                 : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I * 2;
+    t.n0 = nt * DBR;
+    t.N = H;
+    const uint32_t arow = (uint32_t)(t.row0 + min(row, t.nrows - 1));
+    t.aoff = (arow * (uint32_t)Ks + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int br = b_row(j);
+      const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
+      t.boff[j] = (n * (uint32_t)ldb + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+    }
+    t.nk = Ks / (NCH * EPC);
+    t.kseg = ldb * 2;
+    t.bstride = sh && g.S > 1 ? H * g.Is * 2 : 0;
+  }
+}
+
+// Buffer resource over [p, p + 2^31): the hardware range check drops stores
+// at offsets >= 2^31, which masks elements without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr uint32_t kDropped = 0x80000000u;
+
+// Epilogue: exactly EPI_GU (gate/up) or EPI_DN (down) buffer stores or
+// atomics per thread, masked by offset. Lane (q, r) holds rows
+// acc_row(0, v, q) of column r of each 32-column block.
+template <int KIND, bool ATOMIC>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const DTile& cur, const Acc2& acc,
+                                         const int* ep_tok, const float* ep_w) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 5, r = lane & 31;
+  if (KIND == GATE_UP) {
+    bf16_t* dst = static_cast<bf16_t*>(cur.shared ? g.out_shared : g.out);
+    const int ld = cur.shared ? g.S * g.Is : g.I;
+    const int c = cur.n0 + 32 * w + r;
+    const __amdgpu_buffer_rsrc_t rs = out_rsrc(dst + (size_t)cur.row0 * ld);
+    const bool cok = c < cur.N;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = acc_row(0, v, q);
+      const bool ok = cok && m < cur.nrows;
+      __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(act_apply(acc[0][v], acc[1][v], g.act)),
+                                            rs, ok ? (uint32_t)(m * ld + c) * 2u : kDropped, 0, 0);
+    }
+    return;
+  }
+  const int c0 = cur.n0 + 64 * w + r;
+  const bool sh = KIND == DOWN_SHARED || (KIND == DOWN_BOTH && cur.shared);
+  if (sh || !ATOMIC) {
+    if (sh) {
+      // shared rows: fp32 into acc (weight exactly 1)
+      const __amdgpu_buffer_rsrc_t rs =
+          out_rsrc(static_cast<float*>(g.out) + (size_t)cur.row0 * g.H);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int m = acc_row(0, v, q), c = c0 + 32 * nb;
+          const bool ok = c < cur.N && m < cur.nrows;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[nb][v]), rs,
+                                                ok ? (uint32_t)(m * g.H + c) * 4u : kDropped, 0, 0);
+        }
+    } else {
+      // routed rows, unweighted, into y_perm (moe_combine sums them in a fixed order)
+      const __amdgpu_buffer_rsrc_t rs =
+          out_rsrc(static_cast<bf16_t*>(g.y_perm) + (size_t)cur.row0 * g.H);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int m = acc_row(0, v, q), c = c0 + 32 * nb;
+          const bool ok = c < cur.N && m < cur.nrows;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc[nb][v]), rs,
+                                                ok ? (uint32_t)(m * g.H + c) * 2u : kDropped, 0, 0);
+        }
+    }
+  } else {
+    // routed rows, weighted by topk_w, added into acc[token] with fp32 atomics
+    const __amdgpu_buffer_rsrc_t rs = out_rsrc(g.out);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = acc_row(0, v, q);
+      const int tok = ep_tok[m];
+      const float wt = ep_w[m];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int c = c0 + 32 * nb;
+        const bool ok = c < cur.N && m < cur.nrows;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+            wt * acc[nb][v], rs, ok ? (uint32_t)((size_t)tok * g.H + c) * 4u : kDropped, 0, 0);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The persistent kernel. Step j of a tile: wait until this wave's loads of
+// stage j have landed (only the two younger stages, plus the previous tile's
+// epilogue stores in a tile's first three steps, may still be in flight),
+// barrier, issue the loads of step j+3 into the stage freed at step j-1
+// (the next tile's first stages when j+3 passes the end), compute stage j.
+template <int KIND, bool ATOMIC>
+__device__ __forceinline__ void decode_body(const GemmArgs& g) {
+  DEC_LDS_STAGES
+  __shared__ int offs[MAX_EXPERTS + 1];
+  __shared__ int cum[MAX_EXPERTS + 1];
+  __shared__ int4 places[MAX_WG_TILES];
+  __shared__ int rows_buf[3][64];  // gathered row ids of tiles li, li+1, li+2 (slot i % 3)
+  __shared__ int ep_tok[2][64];    // atomic down epilogue: token and weight of each
+  __shared__ float ep_w[2][64];    // row (by tile parity: written while the other
+                                   // waves may still read the previous tile's)
+
+  if (KIND != DOWN_SHARED) build_tile_prefix<DBM>(g.offsets, g.E, offs, cum);
+  __syncthreads();
+  const int ntiles = tile_count<KIND>(g, cum);
+  const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0);
+  const int n_my = wt.n_my;
+  if (n_my == 0) return;
+  for (int i = threadIdx.x; i < min(n_my, MAX_WG_TILES); i += NTHR)
+    places[i] = place_of<KIND>(g, offs, cum, wt.global(i));
+  __syncthreads();
+  auto place = [&](int i) -> int4 {
+    i = min(i, n_my - 1);
+    const int4 p = i < MAX_WG_TILES ? places[i] : place_of<KIND>(g, offs, cum, wt.global(i));
+    return make_int4(__builtin_amdgcn_readfirstlane(p.x), __builtin_amdgcn_readfirstlane(p.y),
+                     __builtin_amdgcn_readfirstlane(p.z), __builtin_amdgcn_readfirstlane(p.w));
+  };
+
+  constexpr int EPI = KIND == GATE_UP ? EPI_GU : EPI_DN;
+  constexpr bool ROWS = KIND == GATE_UP || (KIND == DOWN_ROUTED && ATOMIC);
+  if (ROWS) {
+    gather_rows(g, place(0), rows_buf[0]);
+    gather_rows(g, place(1), rows_buf[1]);
+    // the first tile's row ids are read right away (later gathers are a tile
+    // ahead: waited for by wave 0's step waits and published by the step
+    // barriers)
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  DTile cur, nxt;
+  make_tile<KIND>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
+  issue_stage(cur, 0, lds_a0, lds_b0);
+  issue_stage(cur, 1, lds_a1, lds_b1);
+  issue_stage(cur, 2, lds_a2, lds_b2);
+
+  bool first = true;
+  for (int li = 0;; ++li) {
+    const bool has_next = li + 1 < n_my;
+    // the next tile (its row ids were gathered a tile ago), then the row ids
+    // of the one after it
+    make_tile<KIND>(g, place(li + 1),
+                    KIND == GATE_UP ? token_of(g, place(li + 1), rows_buf[(li + 1) % 3]) : 0, nxt);
+    if (KIND == DOWN_ROUTED && ATOMIC && threadIdx.x < 64) {
+      // this tile's rows: token and routing weight of each (the weights are
+      // gathered straight into LDS as well)
+      const int r = rows_buf[li % 3][threadIdx.x];
+      ep_tok[li & 1][threadIdx.x] = div_k(r, g.k, g.kmagic);
+      dma4(reinterpret_cast<const char*>(g.topk_w), (uint32_t)r * 4u, ep_w[li & 1]);
+    }
+    if (ROWS) gather_rows(g, place(li + 2), rows_buf[(li + 2) % 3]);
+    // after the last tile, the look-ahead reloads its own first stages (never read)
+    const int nk4 = cur.nk;
+    Acc2 acc;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
+
+#define DEC_STEP(J, TL, JL, LA, LB, NA, NB)                                        \
+  {                                                                                  \
+    if ((J) < 3 && !first) wait_vmcnt<2 * LOADS + EPI>();                            \
+    else wait_vmcnt<2 * LOADS>();                                                    \
+    __builtin_amdgcn_s_barrier();                                                    \
+    issue_stage(TL, JL, NA, NB);                                                     \
+    compute_stage<KIND>(LA, LB, acc);                                                \
+  }
+    // steps j .. j+3 use stages 0..3 and load step j+3 .. j+6; the last four
+    // steps of the tile load its last step and the next tile's first three
+    int j = 0;
+    for (; j + 4 < nk4; j += 4) {
+      DEC_STEP(j, cur, j + 3, lds_a0, lds_b0, lds_a3, lds_b3)
+      DEC_STEP(j + 1, cur, j + 4, lds_a1, lds_b1, lds_a0, lds_b0)
+      DEC_STEP(j + 2, cur, j + 5, lds_a2, lds_b2, lds_a1, lds_b1)
+      DEC_STEP(j + 3, cur, j + 6, lds_a3, lds_b3, lds_a2, lds_b2)
+    }
+    DEC_STEP(j, cur, j + 3, lds_a0, lds_b0, lds_a3, lds_b3)
+    DEC_STEP(j + 1, nxt, 0, lds_a1, lds_b1, lds_a0, lds_b0)
+    DEC_STEP(j + 2, nxt, 1, lds_a2, lds_b2, lds_a1, lds_b1)
+    DEC_STEP(j + 3, nxt, 2, lds_a3, lds_b3, lds_a2, lds_b2)
+#undef DEC_STEP
+    epilogue<KIND, ATOMIC>(g, cur, acc, ep_tok[li & 1], ep_w[li & 1]);
+    if (!has_next) break;
+    first = false;
+    cur = nxt;
+  }
+  // the look-ahead loads after the last tile are not used: let them land
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ void __launch_bounds__(NTHR) moe_gate_up_decode_kernel(GemmArgs g) {
+  decode_body<GATE_UP, false>(g);
+}
+__global__ void __launch_bounds__(NTHR) moe_down_decode_kernel(GemmArgs g) {
+  decode_body<DOWN_BOTH, false>(g);
+}
+__global__ void __launch_bounds__(NTHR) moe_down_shared_decode_kernel(GemmArgs g) {
+  decode_body<DOWN_SHARED, false>(g);
+}
+template <bool ATOMIC>
+__global__ void __launch_bounds__(NTHR) moe_down_routed_decode_kernel(GemmArgs g) {
+  decode_body<DOWN_ROUTED, ATOMIC>(g);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+int gemm_decode_bm() { return DBM; }
+
+// Every K length is a whole number of four K-steps, and the per-lane 32-bit
+// offsets reach every row: x, h, h_shared, one expert's weights, the shared
+// weights, and acc rows of the atomic epilogue (< 2^31).
+bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is) {
+  if (H % 256 || I % 256 || (S && (S * Is) % 256)) return false;
+  const uint64_t lim = 1ull << 32;
+  const uint64_t x = (uint64_t)T * H * 2, h = (uint64_t)T * k * I * 2,
+                 hs = (uint64_t)T * S * Is * 2, w = (uint64_t)H * I * 2,
+                 ws = (uint64_t)S * H * Is * 2, acc = (uint64_t)T * H * 4;
+  return x < lim && h < lim && hs < lim && w < lim && ws < lim && acc < (1ull << 31);
+}
+
+static int g_dec_cus = 0;
+static int dec_num_cus() {
+  if (g_dec_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_dec_cus = n;
+    else
+      g_dec_cus = 256;
+  }
+  return g_dec_cus;
+}
+
+static hipError_t launch_decode(void (*kern)(GemmArgs), long n, const GemmArgs& g,
+                                hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long grid = n < dec_num_cus() ? n : dec_num_cus();
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st) {
+  return launch_decode(moe_gate_up_decode_kernel,
+                       (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed, g, st);
+}
+hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st) {
+  return launch_decode(moe_down_decode_kernel,
+                       (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed, g, st);
+}
+hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st) {
+  return launch_decode(moe_down_shared_decode_kernel, (long)g.mt_shared * g.nt_shared, g, st);
+}
+hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st) {
+  const long n = (long)g.mt_routed * g.nt_routed;
+  return atomic ? launch_decode(moe_down_routed_decode_kernel<true>, n, g, st)
+                : launch_decode(moe_down_routed_decode_kernel<false>, n, g, st);
+}

@@ -35,6 +35,15 @@ hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
 
+// 32-row tile kernels for decode-sized batches (bf16; every K length a
+// multiple of 256; per-lane 32-bit offsets: gemm_decode_fits).
+int gemm_decode_bm();
+bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is);
+hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st);
+hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st);
+hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st);
+hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st);
+
 // router GEMM scratch: bf16 split planes of the router weight + K-chunk partials
 int router_kchunks(int64_t T, int E, int H, int dtype);
 size_t router_ws_bytes(int64_t T, int E, int H, int dtype);
