@@ -30,6 +30,12 @@ pages, one step per function, in the pages' order:
      packed as slot E participates with a fixed score of 1.0)
  10. combine        out = sum_j w_j * y_{idx_j} + sum_s y_s
 
+The MoE block around the layer (mlxcel #845 "What the original body missed",
+the sandwich norm layout): out = h + post_mlp_norm(layer(pre_mlp_norm(h))),
+with RMSNorm y = x / sqrt(mean(x^2) + eps) * w (HF "AFMoE" doc: rms_norm_eps),
+or * (w + 1) for the Gemma-style norms of MiniMax-M3 (mlxcel #763
+"Architecture specification", Norms bullet).
+
 Readings where the pages are silent are listed in the design notes: the bias
 is added to the post-sigmoid scores; normalise then scale; no epsilon in the
 norm; ties go to the lower expert index and the k indices are emitted in the
@@ -262,3 +268,29 @@ def moe_forward_tokens(inp, cfg: dict, tokens, logits_rows: np.ndarray | None = 
     for (wg, wu, wd) in _shared_weights(inp, cfg):
         out += mlp_out(mlp_hidden(x, wg, wu, act), wd)
     return dict(logits=L, idx=idx, w=w, out=out)
+
+
+# ----------------------------------------------------------------------------
+# the MoE block: pre-norm, layer, post-norm, residual
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, add_one: bool) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * (w (+ 1))."""
+    x = as_f64(x)
+    scale = as_f64(w) + (1.0 if add_one else 0.0)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + F64(eps))
+    return x * r * scale
+
+
+def block_forward(inp, cfg: dict, pre_w: np.ndarray, post_w: np.ndarray, eps: float,
+                  add_one: bool, logits: np.ndarray | None = None) -> dict:
+    """out = h + post_norm(layer(pre_norm(h))), h = inp.x. The layer runs on the
+    float64 pre-normed rows; `logits` (fp32 values) replaces its router GEMM
+    when given."""
+    h = as_f64(inp.x)
+    xn = rms_norm(h, pre_w, eps, add_one)
+    sub = type(inp)(**{**inp.__dict__, "x": xn})
+    res = moe_forward(sub, cfg, logits=logits)
+    moe_out = res["out"]
+    y = rms_norm(moe_out, post_w, eps, add_one)
+    return dict(res, xn=xn, moe_out=moe_out, out=h + y)
+

@@ -412,3 +412,117 @@ def test_workloads_use_page_constants():
     assert c5["shared_intermediate_size"] == m3["shared_intermediate_size"]
     assert c5["shared_packed"] == 1 and c5["num_experts"] == m3["shared_slot"]
     assert (c5["act_alpha"], c5["act_limit"], c5["act_beta"]) == (m3["alpha"], m3["limit"], m3["beta"])
+    assert c2["rms_norm_eps"] == d["rms_norm_eps"]
+    assert c5["norm_add_one"] == 1 and c2["norm_add_one"] == 0
+
+
+# --------------------------------------------------------------------------
+# RMSNorm and the block around the layer (mlxcel #845 "What the original body
+# missed": out = h + post_mlp_norm(mlp(pre_mlp_norm(h))); mlxcel #763 Norms
+# bullet: Gemma-style w + 1)
+
+def test_rms_norm_hand_example():
+    for c in _gold("rms_norm_hand_example.json")["cases"]:
+        y = O.rms_norm(np.array([c["x"]]), np.array(c["w"]), c["eps"], bool(c["add_one"]))[0]
+        assert np.allclose(y, c["y"], rtol=4 * ULP1, atol=0), c["why"]
+
+
+def test_rms_norm_rows_by_loops():
+    """Each row is normalised on its own, over the hidden axis: explicit
+    per-element loops on rows of very different scales."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 9)) * np.array([1e-3, 1.0, 7.0, 1e3, 0.5, 40.0])[:, None]
+    w = rng.standard_normal(9)
+    for add_one in (False, True):
+        y = O.rms_norm(x, w, 1e-5, add_one)
+        for t in range(6):
+            ms = sum(float(v) * float(v) for v in x[t]) / 9
+            r = 1.0 / math.sqrt(ms + 1e-5)
+            for i in range(9):
+                ref = float(x[t, i]) * r * (float(w[i]) + (1.0 if add_one else 0.0))
+                assert abs(y[t, i] - ref) <= 8 * ULP1 * max(1.0, abs(ref))
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 64)) * np.array([1e-2, 1.0, 3.0, 1e4])[:, None]
+    ones = np.ones(64)
+    y = O.rms_norm(x, ones, 0.0, False)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=0, atol=8 * ULP1)
+    for a in (0.25, 3.0, 1e3):
+        assert np.allclose(O.rms_norm(a * x, ones, 0.0, False), y, rtol=8 * ULP1, atol=0)
+    assert np.array_equal(O.rms_norm(-x, ones, 0.0, False), -y)
+    # eps dominates a tiny row: y -> x / sqrt(eps)
+    tiny = np.full((1, 8), 1e-9)
+    assert np.allclose(O.rms_norm(tiny, np.ones(8), 1.0, False), tiny, rtol=1e-12, atol=0)
+
+
+def _block_inputs(cfg, T=5, seed=11):
+    inp = _tiny_inputs(cfg, T=T, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    H = cfg["hidden_size"]
+    return inp, rng.uniform(0.5, 1.5, H), rng.uniform(0.5, 1.5, H)
+
+
+def test_block_zero_expert_outputs_give_the_residual():
+    """With every down projection zero the layer output is zero, its RMSNorm
+    (eps > 0) is zero, and the block returns its input unchanged."""
+    cfg = _tiny_cfg()
+    inp, pre, post = _block_inputs(cfg)
+    inp.w_down[:] = 0
+    inp.ws_down[:] = 0
+    res = O.block_forward(inp, cfg, pre, post, 1e-5, False)
+    assert np.array_equal(res["out"], O.as_f64(inp.x))
+
+
+def test_block_branch_has_the_post_norm_scale():
+    """eps = 0 and a unit post-norm weight: every row of out - h has RMS 1;
+    with post weight w the row RMS of (out - h) / w is 1."""
+    cfg = _tiny_cfg(hidden_act="swigluoai")
+    inp, pre, post = _block_inputs(cfg, T=7)
+    for w, add_one in ((np.ones(8), False), (post, False), (post - 1.0, True)):
+        res = O.block_forward(inp, cfg, pre, w, 0.0, add_one)
+        scale = w + (1.0 if add_one else 0.0)
+        br = (res["out"] - O.as_f64(inp.x)) / scale
+        assert np.allclose(np.sqrt(np.mean(br * br, axis=-1)), 1.0, rtol=0, atol=1e-12)
+
+
+def test_block_ignores_the_input_scale():
+    """eps = 0: the pre-norm removes a positive scale of h, so routing and
+    out - h are unchanged while the residual scales."""
+    cfg = _tiny_cfg(num_experts=5, num_experts_per_tok=2)
+    inp, pre, post = _block_inputs(cfg, T=6)
+    a = O.block_forward(inp, cfg, pre, post, 0.0, False)
+    big = synth.MoeInputs(**{**inp.__dict__, "x": (inp.x * np.float32(16.0)).astype(np.float32)})
+    b = O.block_forward(big, cfg, pre, post, 0.0, False)
+    assert np.array_equal(a["idx"], b["idx"])
+    da = a["out"] - O.as_f64(inp.x)
+    db = b["out"] - O.as_f64(big.x)
+    assert np.allclose(da, db, rtol=1e-12, atol=1e-12)
+
+
+def test_block_by_loops():
+    """The whole block through explicit per-token loops: pre-norm, router,
+    selection, experts, post-norm, residual (Gemma-style and plain scales)."""
+    cfg = _tiny_cfg(num_experts=5, num_experts_per_tok=2, route_scale=1.5)
+    inp, pre, post = _block_inputs(cfg, T=4)
+    for add_one in (False, True):
+        res = O.block_forward(inp, cfg, pre, post, 1e-5, add_one)
+        off = 1.0 if add_one else 0.0
+        for t in range(4):
+            h = [float(v) for v in inp.x[t]]
+            r = 1.0 / math.sqrt(sum(v * v for v in h) / 8 + 1e-5)
+            xn = np.array([h[i] * r * (pre[i] + off) for i in range(8)])
+            logits = [sum(xn[i] * float(inp.w_router[e, i]) for i in range(8)) for e in range(5)]
+            s = [1.0 / (1.0 + math.exp(-v)) for v in logits]
+            key = [s[e] + float(inp.expert_bias[e]) for e in range(5)]
+            chosen = sorted(range(5), key=lambda e: (-key[e], e))[:2]
+            den = sum(s[e] for e in chosen)
+            y = _loop_swiglu_mlp(xn, inp.ws_gate[0], inp.ws_up[0], inp.ws_down[0], _py_silu)
+            for e in chosen:
+                y = y + 1.5 * s[e] / den * _loop_swiglu_mlp(xn, inp.w_gate[e], inp.w_up[e],
+                                                            inp.w_down[e], _py_silu)
+            r2 = 1.0 / math.sqrt(sum(float(v) * float(v) for v in y) / 8 + 1e-5)
+            ref = [h[i] + float(y[i]) * r2 * (post[i] + off) for i in range(8)]
+            assert res["idx"][t].tolist() == chosen
+            assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)

@@ -16,6 +16,9 @@ Shapes and value ranges follow the pages:
     one shared expert of width 3072 packed as slot 128, clamp-SwiGLU with
     alpha 1.702 / limit 7.0 / beta 1.0): mlxcel issue #763 "add MiniMax-M3",
     "Architecture specification", MoE and Activation bullets.
+  * The RMSNorms either side of the layer: rms_norm_eps 1e-5 (HF "AFMoE"
+    doc, AfmoeConfig); Gemma-style w + 1 scales for MiniMax-M3 (mlxcel #763,
+    Norms bullet), whose eps the pages do not print (1e-5 is used).
 
 Seeding: every tensor, and every expert (or token block) within a tensor, has
 its own stream np.random.default_rng(SeedSequence([seed, tensor_id, block])).
@@ -37,6 +40,7 @@ TID_X, TID_ROUTER, TID_BIAS = 0, 1, 2
 TID_GATE, TID_UP, TID_DOWN = 3, 4, 5
 TID_SGATE, TID_SUP, TID_SDOWN = 6, 7, 8
 TID_HOTSET = 9
+TID_PRE_NORM, TID_POST_NORM = 10, 11
 
 X_BLOCK_ROWS = 256          # rows of x drawn from one stream
 _CHUNK = 1 << 20            # elements drawn per call (buffers are reused)
@@ -50,7 +54,7 @@ def _cfg(**kw):
         seed=0, shared_packed=0, score_func="sigmoid", route_norm=1,
         route_scale=1.0, hidden_act="silu", act_alpha=1.702, act_limit=7.0,
         act_beta=1.0, x_scale=1.0, w_std=0.02, router_bf16_values=True,
-        skew=None,
+        skew=None, rms_norm_eps=1e-5, norm_add_one=0, norm_w_std=0.1,
     )
     base.update(kw)
     if base.get("shared_intermediate_size", 0) == 0:
@@ -96,12 +100,14 @@ CONFIGS: dict[str, dict] = {
         T=8192, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
         moe_intermediate_size=3072, num_shared_experts=1,
         shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
-        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai"),
+        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
+        norm_add_one=1),
     "minimax_m3_decode_T64": _cfg(
         T=64, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
         moe_intermediate_size=3072, num_shared_experts=1,
         shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
-        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai"),
+        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
+        norm_add_one=1),
 }
 
 
@@ -281,6 +287,27 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
         sk = load_skew(cfg["skew"])
         apply_skew_params(inp, sk)
     return inp
+
+
+def norm_weights(cfg: dict) -> dict:
+    """Weights of the RMSNorms either side of the layer (pre_mlp_norm,
+    post_mlp_norm), float32 [H] holding bf16 values, plus eps and the
+    Gemma-style offset flag.
+
+    Trained values are not available; the draw centres on the initial value
+    of each style (1 for a plain norm scale, 0 for a Gemma-style weight that
+    is used as w + 1) with spread norm_w_std."""
+    H = cfg["hidden_size"]
+    centre = np.float32(0.0 if cfg["norm_add_one"] else 1.0)
+    out = {}
+    for name, tid in (("pre", TID_PRE_NORM), ("post", TID_POST_NORM)):
+        w = np.empty(H, np.float32)
+        _fill_normal(w, _stream(cfg["seed"], tid, 0), cfg["norm_w_std"], False)
+        w += centre
+        out[name] = bf16_bits_to_f32(f32_to_bf16_bits(w))
+    out["eps"] = float(cfg["rms_norm_eps"])
+    out["add_one"] = int(cfg["norm_add_one"])
+    return out
 
 
 def hot_set(cfg: dict) -> np.ndarray:
