@@ -20,6 +20,7 @@
  *  - Pointers are DEVICE pointers unless marked "host". The caller owns all
  *    memory. The library allocates nothing and keeps no state between calls;
  *    work happens asynchronously on the given stream.
+ *  - Device tensors are 16-byte aligned (the kernels move 16-byte vectors).
  *  - Tensors are row-major and dense. Weights use the [out, in] layout of a
  *    linear layer: gate/up [E_tot, I, H], down [E_tot, H, I], where
  *    E_tot = E + 1 when the shared expert is packed as slot E, else E.
@@ -190,6 +191,64 @@ moe_status moe_layer_forward(
     float* router_logits_out, int32_t* topk_idx_out, float* topk_w_out,
     void* out, int32_t deterministic, void* ws, size_t ws_bytes,
     moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The MoE block: the layer between two RMSNorms, plus the residual
+ * (mlxcel #845 "What the original body missed": four norms per layer, the
+ * feed-forward half being out = h + post_mlp_norm(mlp(pre_mlp_norm(h)))):
+ *
+ *   RMSNorm(x)[i] = x[i] / sqrt(sum_i' x[i']^2 / H + eps) * scale[i]
+ *   scale = w           (AFMoE; eps = rms_norm_eps, 1e-5 in AfmoeConfig)
+ *   scale = w + 1       (Gemma style, MiniMax-M3: mlxcel #763 Norms bullet)
+ *
+ * The sum of squares is taken in fp32 in a fixed order, so results do not
+ * depend on timing. Norm weights are fp32 [H]. H <= 8192 (one workgroup
+ * holds a row); larger H returns MOE_ERR_UNSUPPORTED. */
+typedef struct {
+  float rms_norm_eps; /* eps >= 0, finite                                   */
+  int32_t add_one;    /* 0: scale = w; 1: scale = w + 1 (Gemma style)       */
+} moe_norm_config;
+
+/* y[T,H] = RMSNorm(x[T,H]) with weight [H] (fp32); x and y in cfg->dtype
+ * (only hidden_size and dtype of cfg are used). y may equal x (in place);
+ * partial overlap is not allowed. */
+moe_status moe_rms_norm(const moe_config* cfg, const moe_norm_config* norm,
+                        int64_t T, const void* x, const float* weight, void* y,
+                        moe_stream_t stream);
+
+/* Finalise with the post-norm and the residual:
+ *   v[t]   = acc[t]                                            (y_perm NULL)
+ *          = acc[t] + sum_j topk_w[t,j] * y_perm[row_pos[t*k+j]]  (j order)
+ *   out[t] = residual[t] + RMSNorm(v[t]) with post_norm_w
+ * v stays fp32 (the layer output is normalised before any rounding);
+ * residual and out [T,H] in dtype; out may equal residual (in place). */
+moe_status moe_combine_norm_residual(const moe_config* cfg,
+                                     const moe_norm_config* norm, int64_t T,
+                                     const float* acc, const void* y_perm,
+                                     const int32_t* row_pos,
+                                     const float* topk_w,
+                                     const float* post_norm_w,
+                                     const void* residual, void* out,
+                                     moe_stream_t stream);
+
+/* Workspace bytes of moe_block_forward: the layer's workspace plus the
+ * normalised input rows [T,H] (dtype). */
+moe_status moe_block_workspace_size(const moe_config* cfg, int64_t T,
+                                    size_t* bytes);
+
+/* The whole block: out = h + RMSNorm_post(layer(RMSNorm_pre(h))).
+ *   h [T,H] dtype (the residual stream); pre_norm_w, post_norm_w [H] fp32;
+ *   the layer's weights and outputs as in moe_layer_forward, the layer
+ *   running on the normalised rows (rounded to dtype); out [T,H] dtype,
+ *   may equal h (in place). ws: moe_block_workspace_size bytes. */
+moe_status moe_block_forward(
+    const moe_config* cfg, const moe_norm_config* norm, int64_t T,
+    const void* h, const float* pre_norm_w, const float* post_norm_w,
+    const float* w_router, const float* expert_bias, const void* w_gate,
+    const void* w_up, const void* w_down, const void* ws_gate,
+    const void* ws_up, const void* ws_down, float* router_logits_out,
+    int32_t* topk_idx_out, float* topk_w_out, void* out,
+    int32_t deterministic, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 const char* moe_status_string(moe_status s);
 

@@ -24,7 +24,9 @@ MOE_F32, MOE_BF16 = 0, 1
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
     "moe_grouped_gate_up_swiglu", "moe_grouped_down", "moe_combine",
-    "moe_layer_forward", "moe_status_string", "moe_build_info",
+    "moe_layer_forward", "moe_rms_norm", "moe_combine_norm_residual",
+    "moe_block_workspace_size", "moe_block_forward", "moe_status_string",
+    "moe_build_info",
 )
 
 
@@ -47,6 +49,21 @@ class MoeConfig(ctypes.Structure):
         ("act_beta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class MoeNormConfig(ctypes.Structure):
+    """Mirror of moe_norm_config (include/moe.h)."""
+    _fields_ = [("rms_norm_eps", ctypes.c_float), ("add_one", ctypes.c_int32)]
+
+
+def make_norm_config(norm) -> MoeNormConfig:
+    """MoeNormConfig from a dict with keys eps / add_one (or pass-through)."""
+    if isinstance(norm, MoeNormConfig):
+        return norm
+    n = MoeNormConfig()
+    n.rms_norm_eps = float(norm.get("eps", norm.get("rms_norm_eps", 1e-5)))
+    n.add_one = int(norm.get("add_one", 0))
+    return n
 
 
 _SCORE = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
@@ -100,6 +117,7 @@ def lib() -> ctypes.CDLL:
                 "`python -m sparse_moe_transformer_amd.build` (no fallback path exists)")
         L = ctypes.CDLL(LIB_PATH)
         cp = ctypes.POINTER(MoeConfig)
+        ncp = ctypes.POINTER(MoeNormConfig)
         i64, sz, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
         sig = {
             "moe_workspace_size": [cp, i64, ctypes.POINTER(sz)],
@@ -110,6 +128,10 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_down": [cp, i64] + [_vp] * 9 + [_vp, sz, _vp],
             "moe_combine": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
             "moe_layer_forward": [cp, i64] + [_vp] * 14 + [i32, _vp, sz, _vp],
+            "moe_rms_norm": [cp, ncp, i64, _vp, _vp, _vp, _vp],
+            "moe_combine_norm_residual": [cp, ncp, i64] + [_vp] * 7 + [_vp],
+            "moe_block_workspace_size": [cp, i64, ctypes.POINTER(sz)],
+            "moe_block_forward": [cp, ncp, i64] + [_vp] * 15 + [i32, _vp, sz, _vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -254,6 +276,56 @@ def moe_layer_forward(cfg, T, x, w_router, expert_bias, w_gate, w_up, w_down, ws
           _stream(stream))
 
 
+def moe_rms_norm(cfg, norm, T, x, weight, y, stream=None):
+    c = make_config(cfg)
+    n = make_norm_config(norm)
+    _need(x, T * c.hidden_size, "x")
+    _need(y, T * c.hidden_size, "y")
+    _need(weight, c.hidden_size, "weight")
+    _call("moe_rms_norm", ctypes.byref(c), ctypes.byref(n), int(T), _p(x), _p(weight), _p(y),
+          _stream(stream))
+
+
+def moe_combine_norm_residual(cfg, norm, T, acc, y_perm, row_pos, topk_w, post_norm_w,
+                              residual, out, stream=None):
+    c = make_config(cfg)
+    n = make_norm_config(norm)
+    _need(acc, T * c.hidden_size, "acc")
+    _need(residual, T * c.hidden_size, "residual")
+    _need(out, T * c.hidden_size, "out")
+    _need(post_norm_w, c.hidden_size, "post_norm_w")
+    _call("moe_combine_norm_residual", ctypes.byref(c), ctypes.byref(n), int(T), _p(acc),
+          _p(y_perm), _p(row_pos), _p(topk_w), _p(post_norm_w), _p(residual), _p(out),
+          _stream(stream))
+
+
+def moe_block_workspace_size(cfg, T: int) -> int:
+    c = make_config(cfg)
+    nb = ctypes.c_size_t(0)
+    _call("moe_block_workspace_size", ctypes.byref(c), int(T), ctypes.byref(nb))
+    return nb.value
+
+
+def moe_block_forward(cfg, norm, T, h, pre_norm_w, post_norm_w, w_router, expert_bias, w_gate,
+                      w_up, w_down, ws_gate, ws_up, ws_down, router_logits_out, topk_idx_out,
+                      topk_w_out, out, deterministic, ws, stream=None):
+    c = make_config(cfg)
+    n = make_norm_config(norm)
+    k = c.num_experts_per_tok
+    _need(h, T * c.hidden_size, "h")
+    _need(out, T * c.hidden_size, "out")
+    _need(pre_norm_w, c.hidden_size, "pre_norm_w")
+    _need(post_norm_w, c.hidden_size, "post_norm_w")
+    _need(router_logits_out, T * c.num_experts, "router_logits_out")
+    _need(topk_idx_out, T * k, "topk_idx_out")
+    _need(topk_w_out, T * k, "topk_w_out")
+    _call("moe_block_forward", ctypes.byref(c), ctypes.byref(n), int(T), _p(h), _p(pre_norm_w),
+          _p(post_norm_w), _p(w_router), _p(expert_bias), _p(w_gate), _p(w_up), _p(w_down),
+          _p(ws_gate), _p(ws_up), _p(ws_down), _p(router_logits_out), _p(topk_idx_out),
+          _p(topk_w_out), _p(out), int(deterministic), _p(ws),
+          ws.numel() if ws is not None else 0, _stream(stream))
+
+
 # ---------------------------------------------------------------------------
 # device plumbing for callers (torch memory only)
 
@@ -266,6 +338,11 @@ def torch_dtype(cfg):
 def alloc_workspace(cfg, T, device="cuda"):
     import torch
     return torch.empty(moe_workspace_size(cfg, T), dtype=torch.uint8, device=device)
+
+
+def alloc_block_workspace(cfg, T, device="cuda"):
+    import torch
+    return torch.empty(moe_block_workspace_size(cfg, T), dtype=torch.uint8, device=device)
 
 
 def to_device(arr, device="cuda"):

@@ -236,6 +236,65 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 
+moe_status check_layer_args(const Dims& d, const void* x, const float* w_router,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            const void* ws_gate, const void* ws_up, const void* ws_down,
+                            const float* router_logits_in, int32_t deterministic) {
+  if (!x || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (!router_logits_in && !w_router) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status check_norm(const Dims& d, const moe_norm_config* n) {
+  if (!n || !(std::isfinite(n->rms_norm_eps) && n->rms_norm_eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (n->add_one != 0 && n->add_one != 1) return MOE_ERR_INVALID_ARG;
+  if (!norm_fits(d.H)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t block_ws_bytes(const Dims& d) {
+  return carve(d, nullptr).total + align256((size_t)d.T * d.H * d.es);
+}
+
+struct LayerOut {
+  float* topk_w;  // routed weights the combine reads
+  void* y_perm;   // unweighted routed rows (fixed-order combine) or NULL
+};
+
+// Router GEMM through the down projection; the caller finalises from w.acc.
+moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const float* w_router,
+                     const float* expert_bias, const void* w_gate, const void* w_up,
+                     const void* w_down, const void* ws_gate, const void* ws_up,
+                     const void* ws_down, const float* router_logits_in,
+                     float* router_logits_out, int32_t* topk_idx_out, float* topk_w_out,
+                     int32_t deterministic, const Ws& w, hipStream_t st, LayerOut* res) {
+  const int T = (int)d.T;
+  const float* logits = router_logits_in;
+  if (!logits) {
+    float* lo = router_logits_out ? router_logits_out : w.logits;
+    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, T, d.H, d.E, d.dtype, w.router, st)));
+    logits = lo;
+  }
+  int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
+  float* tw = topk_w_out ? topk_w_out : w.w;
+  // routing: one wavefront per token over many workgroups; grouping: one
+  // workgroup for decode batches (T*k <= 1024), else three small kernels
+  MOE_TRY(hip_ok(launch_route(logits, expert_bias, T, d.E, d.k, cfg->score_func,
+                              cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st)));
+  MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
+                                w.local_rank, w.chunk_hist, st)));
+  MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,
+                     w.h_shared, st));
+  void* yp = deterministic ? w.y_perm : nullptr;
+  MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, w.offsets, w.sorted_rows, tw, w.acc,
+                  yp, st));
+  res->topk_w = tw;
+  res->y_perm = yp;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,33 +409,84 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   Dims d;
   MOE_TRY(check_cfg(cfg, T, &d));
   if (T == 0) return MOE_OK;
-  if (!x || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
-  if (!router_logits_in && !w_router) return MOE_ERR_INVALID_ARG;
-  if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
-  if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_layer_args(d, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                           router_logits_in, deterministic));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   hipStream_t st = (hipStream_t)stream;
   Ws w = carve(d, ws);
-  const float* logits = router_logits_in;
-  if (!logits) {
-    float* lo = router_logits_out ? router_logits_out : w.logits;
-    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, (int)T, d.H, d.E, d.dtype, w.router, st)));
-    logits = lo;
-  }
-  int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
-  float* tw = topk_w_out ? topk_w_out : w.w;
-  // routing: one wavefront per token over many workgroups; grouping: one
-  // workgroup for decode batches (T*k <= 1024), else three small kernels
-  MOE_TRY(hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->score_func,
-                              cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st)));
-  MOE_TRY(hip_ok(launch_permute(idx, (int)(T * d.k), d.E, w.offsets, w.sorted_rows, w.row_pos,
-                                w.local_rank, w.chunk_hist, st)));
-  MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,
-                     w.h_shared, st));
-  void* yp = deterministic ? w.y_perm : nullptr;
-  MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, w.offsets, w.sorted_rows, tw, w.acc,
-                  yp, st));
-  return hip_ok(launch_combine(w.acc, yp, w.row_pos, tw, out, (int)T, d.H, d.k, d.dtype, st));
+  LayerOut lo;
+  MOE_TRY(run_layer(cfg, d, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                    ws_down, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
+                    deterministic, w, st, &lo));
+  return hip_ok(launch_combine(w.acc, lo.y_perm, w.row_pos, lo.topk_w, out, (int)T, d.H, d.k,
+                               d.dtype, st));
+}
+
+moe_status moe_rms_norm(const moe_config* cfg, const moe_norm_config* norm, int64_t T,
+                        const void* x, const float* weight, void* y, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  MOE_TRY(check_norm(d, norm));
+  if (T == 0) return MOE_OK;
+  if (!x || !weight || !y) return MOE_ERR_INVALID_ARG;
+  return hip_ok(launch_rmsnorm(x, weight, norm->add_one, norm->rms_norm_eps, y, (int)T, d.H,
+                               d.dtype, (hipStream_t)stream));
+}
+
+moe_status moe_combine_norm_residual(const moe_config* cfg, const moe_norm_config* norm,
+                                     int64_t T, const float* acc, const void* y_perm,
+                                     const int32_t* row_pos, const float* topk_w,
+                                     const float* post_norm_w, const void* residual, void* out,
+                                     moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  MOE_TRY(check_norm(d, norm));
+  if (T == 0) return MOE_OK;
+  if (!acc || !post_norm_w || !residual || !out) return MOE_ERR_INVALID_ARG;
+  if (y_perm && (!row_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return hip_ok(launch_combine_norm(acc, y_perm, row_pos, topk_w, post_norm_w, norm->add_one,
+                                    norm->rms_norm_eps, residual, out, (int)T, d.H, d.k, d.dtype,
+                                    (hipStream_t)stream));
+}
+
+moe_status moe_block_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims d;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  *bytes = block_ws_bytes(d);
+  return MOE_OK;
+}
+
+moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm, int64_t T,
+                             const void* h, const float* pre_norm_w, const float* post_norm_w,
+                             const float* w_router, const float* expert_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, const void* ws_gate,
+                             const void* ws_up, const void* ws_down, float* router_logits_out,
+                             int32_t* topk_idx_out, float* topk_w_out, void* out,
+                             int32_t deterministic, void* ws, size_t ws_bytes,
+                             moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  MOE_TRY(check_norm(d, norm));
+  if (T == 0) return MOE_OK;
+  if (!pre_norm_w || !post_norm_w || !out) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_layer_args(d, h, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                           nullptr, deterministic));
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < block_ws_bytes(d)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Ws w = carve(d, ws);
+  void* xn = static_cast<char*>(ws) + w.total;  // normalised rows after the layer's segments
+  MOE_TRY(hip_ok(launch_rmsnorm(h, pre_norm_w, norm->add_one, norm->rms_norm_eps, xn, (int)T, d.H,
+                                d.dtype, st)));
+  LayerOut lo;
+  MOE_TRY(run_layer(cfg, d, xn, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                    ws_down, nullptr, router_logits_out, topk_idx_out, topk_w_out, deterministic,
+                    w, st, &lo));
+  return hip_ok(launch_combine_norm(w.acc, lo.y_perm, w.row_pos, lo.topk_w, post_norm_w,
+                                    norm->add_one, norm->rms_norm_eps, h, out, (int)T, d.H, d.k,
+                                    d.dtype, st));
 }
 
 const char* moe_status_string(moe_status s) {

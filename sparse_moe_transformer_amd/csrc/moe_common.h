@@ -67,3 +67,45 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
   uint32_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
   return base + slot;
 }
+
+// ---------------------------------------------------------------------------
+// Eight consecutive elements of a row as fp32 (16-byte loads and stores of
+// bf16, two of fp32); bf16 stores round to nearest even.
+
+constexpr int VEC8 = 8;
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[VEC8]) {
+    const floatx4_t a = *reinterpret_cast<const floatx4_t*>(p);
+    const floatx4_t b = *reinterpret_cast<const floatx4_t*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&v)[VEC8]) {
+    *reinterpret_cast<floatx4_t*>(p) = floatx4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<floatx4_t*>(p + 4) = floatx4_t{v[4], v[5], v[6], v[7]};
+  }
+};
+template <>
+struct Vec8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[VEC8]) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&v)[VEC8]) {
+    u32x4_t u;
+    u.x = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+    u.y = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+    u.z = f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
+    u.w = f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  }
+};

@@ -50,6 +50,8 @@ constexpr int EPI_DN = 32;     // ... of a down epilogue
   __shared__ __align__(16) u32x4_t lds_b1[DBR * NCH]; \
   __shared__ __align__(16) u32x4_t lds_b2[DBR * NCH]; \
   __shared__ __align__(16) u32x4_t lds_b3[DBR * NCH];
+static_assert(NST == 4, "DEC_LDS_STAGES and the main loop's rotation name four stages");
+static_assert(NST * (DBM + DBR) * KSB <= 160 * 1024, "LDS stages exceed one compute unit's LDS");
 
 // Wave w loads activation rows 8w .. 8w+7 (one instruction) and weight rows
 // 64w + 8j .. +7 (instruction j < 8); the lane's row is that base + lane/8

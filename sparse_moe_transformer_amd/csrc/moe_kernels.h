@@ -65,3 +65,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_combine(const float* acc, const void* y_perm, const int32_t* row_pos,
                           const float* topk_w, void* out, int T, int H, int k, int dtype,
                           hipStream_t st);
+
+// RMSNorm rows (one workgroup per row, H <= 8192) and the finalising combine
+// with the post-norm and the residual add
+bool norm_fits(int H);
+hipError_t launch_rmsnorm(const void* x, const float* w, int add_one, float eps, void* y, int T,
+                          int H, int dtype, hipStream_t st);
+hipError_t launch_combine_norm(const float* acc, const void* y_perm, const int32_t* row_pos,
+                               const float* topk_w, const float* w, int add_one, float eps,
+                               const void* residual, void* out, int T, int H, int k, int dtype,
+                               hipStream_t st);

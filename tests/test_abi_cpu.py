@@ -83,3 +83,31 @@ def test_host_checks_run_before_any_launch():
 def test_status_strings():
     for code in range(5):
         assert moe.status_string(code).startswith("MOE_")
+
+
+def _raw_block(cfg, T, norm=None, H_ok=True, ptr=0x1000, ws=0x100000, ws_bytes=1 << 40):
+    """moe_block_forward with fake (never dereferenced) device addresses."""
+    L = moe.lib()
+    c = moe.make_config(cfg)
+    n = moe.make_norm_config(norm or {"eps": 1e-5, "add_one": 0})
+    return L.moe_block_forward(ctypes.byref(c), ctypes.byref(n), T, ptr, ptr, ptr, ptr, None,
+                               ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, ptr, 0, ws,
+                               ws_bytes, None)
+
+
+def test_block_host_checks():
+    c = _cfg()
+    assert _raw_block(c, 0) == moe.MOE_OK
+    assert _raw_block(c, 8, ws_bytes=moe.moe_workspace_size(c, 8)) == moe.MOE_ERR_WORKSPACE
+    for bad in ({"eps": float("nan")}, {"eps": -1.0}, {"eps": 1e-5, "add_one": 2}):
+        assert _raw_block(c, 8, norm=bad) == moe.MOE_ERR_INVALID_ARG
+    # a row of more than 8192 columns does not fit one workgroup
+    assert _raw_block(_cfg(hidden_size=8256), 8) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_block_workspace_adds_the_normalised_rows():
+    c = _cfg()
+    for T in (1, 64, 4096):
+        extra = moe.moe_block_workspace_size(c, T) - moe.moe_workspace_size(c, T)
+        assert extra == -(-(T * 2048 * 2) // 256) * 256
+
