@@ -203,6 +203,69 @@ def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
                       f"{cfg['T']} tokens of {name} ({dt:.1f} s wall)"}
 
 
+def _launch_ms(torch, stream, fn, n):
+    """Average duration of n back-to-back launches on `stream` (HIP events)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def block_measurements(moe, synth, cfg, keys, T, ordered, args, stream, t, layer_ms):
+    """The MoE block around the layer, out = h + post_norm(layer(pre_norm(h))):
+    the whole block per step, and the two row kernels it adds (pre-norm, and
+    the finalising combine with post-norm and residual, beside the plain
+    combine) with their algorithmic HBM bytes."""
+    import torch
+    nw = synth.norm_weights(cfg)
+    norm = {"eps": nw["eps"], "add_one": nw["add_one"]}
+    pre_w, post_w = moe.to_device(nw["pre"]), moe.to_device(nw["post"])
+    hout = torch.empty_like(t["out"])
+    xn = torch.empty_like(t["x"])
+
+    def block():
+        moe.moe_block_forward(keys, norm, T, t["x"], pre_w, post_w, t["wr"], t["b"], t["wg"],
+                              t["wu"], t["wd"], t["sg"], t["su"], t["sd"], None, None, None, hout,
+                              int(ordered), t["ws"], stream)
+
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        block()
+    torch.cuda.synchronize()
+    ms_block = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the stage tensors still hold the last eager step's acc / y_perm / row_pos / w
+    n = max(args.steps, 10)
+    H, k = cfg["hidden_size"], cfg["num_experts_per_tok"]
+    bx = 2 if cfg["dtype"] == "bf16" else 4
+    ms_pre = _launch_ms(torch, stream, lambda: moe.moe_rms_norm(
+        keys, norm, T, t["x"], pre_w, xn, stream), n)
+    ms_post = _launch_ms(torch, stream, lambda: moe.moe_combine_norm_residual(
+        keys, norm, T, t["acc"], t["yp"], t["rp"], t["w"], post_w, t["x"], hout, stream), n)
+    ms_comb = _launch_ms(torch, stream, lambda: moe.moe_combine(
+        keys, T, t["acc"], t["yp"], t["rp"], t["w"], t["out"], stream), n)
+    gathered = T * k * (H * bx + 8) if ordered else 0
+    b_pre = 2 * T * H * bx + 4 * H
+    b_comb = 4 * T * H + gathered + T * H * bx
+    b_post = b_comb + T * H * bx + 4 * H
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    return {"entry": "moe_block_forward", "ms_per_step": ms_block,
+            "ms_over_layer": ms_block - layer_ms, "rms_norm_eps": norm["eps"],
+            "norm_add_one": norm["add_one"],
+            "pre_norm": {"kernel": "rmsnorm_kernel", "ms_per_launch": ms_pre, "bytes": b_pre,
+                         "gbs": gbs(b_pre, ms_pre), "frac_hbm_peak": gbs(b_pre, ms_pre) / PEAK_HBM_GBS},
+            "combine_norm_residual": {"kernel": "combine_norm_kernel", "ms_per_launch": ms_post,
+                                      "bytes": b_post, "gbs": gbs(b_post, ms_post),
+                                      "frac_hbm_peak": gbs(b_post, ms_post) / PEAK_HBM_GBS},
+            "combine": {"kernel": "combine_kernel", "ms_per_launch": ms_comb, "bytes": b_comb,
+                        "gbs": gbs(b_comb, ms_comb), "frac_hbm_peak": gbs(b_comb, ms_comb) / PEAK_HBM_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,7 +334,8 @@ def main():
     sg, su, sd = d(inp.ws_gate), d(inp.ws_up), d(inp.ws_down)
     dt = moe.torch_dtype(keys)
     dev = x.device
-    ws = moe.alloc_workspace(keys, T)
+    # the block's workspace holds the layer's, plus the normalised rows
+    ws = moe.alloc_block_workspace(keys, T)
     f32, i32 = torch.float32, torch.int32
     logits = torch.empty(T * E, dtype=f32, device=dev)
     idx = torch.empty(T * k, dtype=i32, device=dev)
@@ -403,6 +467,10 @@ def main():
     roof["ms_per_launch"] = gu_ms
     roof["launches_timed"] = n_rl
 
+    blk = block_measurements(moe, synth, cfg, keys, T, ordered, args, stream,
+                             dict(x=x, wr=wr, b=b, wg=wg, wu=wu, wd=wd, sg=sg, su=su, sd=sd,
+                                  acc=acc, yp=yp, rp=rp, w=w, out=out, ws=ws), ms_eager)
+
     sample = args.cpu_sample
     if sample is None:
         sample = T
@@ -437,6 +505,7 @@ def main():
                   "gbs_hbm_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9,
                   "frac_hbm_peak_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "roofline": roof,
+        "block": blk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

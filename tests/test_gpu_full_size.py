@@ -97,3 +97,28 @@ def test_minimax_m3_decode_T64(m3):
     assert np.array_equal(synth.generate(synth.config("minimax_m3_decode_T64"), experts=False).x,
                           inp.x[:64])
     _check(dev, "minimax_m3_decode_T64", 8)
+
+
+def _check_block(dev, name, nsample):
+    """The block (pre-norm, layer, post-norm, residual) at full size: routing
+    over every token, the output on a seeded sample of tokens."""
+    from tests.test_gpu_block import check_block, run_block
+    cfg = dev.inp.cfg
+    nw = synth.norm_weights(cfg)
+    say(f"[full] block {name} T={dev.T} add_one={nw['add_one']}")
+    res = run_block(dev, nw, 1)
+    k = cfg["num_experts_per_tok"]
+    _, _, idx, _ = O.route(res["logits"], dev.inp.expert_bias, k, cfg["score_func"],
+                           bool(cfg["route_norm"]), cfg["route_scale"])
+    assert np.array_equal(res["idx"], idx)
+    toks = _sample(dev.T, nsample, seed=1)
+    worst = check_block(cfg, dev.inp, nw, res, tokens=toks)
+    say(f"[full] block {name} sampled {toks.size} tokens worst err/bound {worst:.3f}")
+
+
+def test_minimax_m3_block_T8192(m3):
+    _check_block(m3, "minimax_m3_prefill_T8192", 8)
+
+
+def test_afmoe_default_block_T4096():
+    _check_block(Dev(generated("afmoe_default_T4096")), "afmoe_default_T4096", 16)
