@@ -36,6 +36,12 @@ with RMSNorm y = x / sqrt(mean(x^2) + eps) * w (HF "AFMoE" doc: rms_norm_eps),
 or * (w + 1) for the Gemma-style norms of MiniMax-M3 (mlxcel #763
 "Architecture specification", Norms bullet).
 
+Expert weights may also arrive as MXFP8 (mlxcel #763 "Validation": the
+checkpoint's MXFP8 export), read as the OCP Microscaling (MX) v1.0 format:
+every 32 consecutive inputs of a weight row share one E8M0 scale 2^(e-127)
+and each element is an OCP FP8 E4M3 code; a weight is code value x scale.
+The layer then runs unchanged on those exact values (mx_dequantize).
+
 Readings where the pages are silent are listed in the design notes: the bias
 is added to the post-sigmoid scores; normalise then scale; no epsilon in the
 norm; ties go to the lower expert index and the k indices are emitted in the
@@ -59,6 +65,55 @@ def as_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(F64)
     return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 weights (OCP MX v1.0: E4M3 elements, one E8M0 scale per 32 inputs)
+
+MX_BLOCK = 32
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 codes: sign bit, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); 0x7F and
+    0xFF are NaN; there are no infinities (largest finite 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = (c & 0x7).astype(F64)
+    mag = np.where(ef == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(ef.astype(F64) - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def e8m0_value(e: np.ndarray) -> np.ndarray:
+    """Exact value of E8M0 scale bytes: 2^(e - 127); 0xFF is NaN."""
+    e = np.asarray(e, dtype=np.uint8).astype(F64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Weight values of one MXFP8 matrix: codes [N, K] (uint8), scales
+    [K/32, N] (uint8, block-major: the scales of all N rows for each block of
+    32 inputs) -> float64 [N, K], w[n, k] = e4m3(codes[n, k]) * 2^(s[k/32, n] - 127)."""
+    N, K = codes.shape
+    sc = e8m0_value(scales).T                                   # [N, K/32]
+    return e4m3_value(codes) * np.repeat(sc, MX_BLOCK, axis=1)[:, :K]
+
+
+class MxStacked:
+    """Stacked MXFP8 matrices ([E, N, K] codes, [E, K/32, N] scales) whose
+    item e is the float64 dequantised matrix of expert e (computed on access,
+    one expert at a time)."""
+
+    def __init__(self, codes: np.ndarray, scales: np.ndarray):
+        self.codes, self.scales = codes, scales
+        self.shape = codes.shape
+
+    def __len__(self):
+        return self.codes.shape[0]
+
+    def __getitem__(self, e):
+        return mx_dequantize(self.codes[e], self.scales[e])
 
 
 # ----------------------------------------------------------------------------

@@ -526,3 +526,87 @@ def test_block_by_loops():
             ref = [h[i] + float(y[i]) * r2 * (post[i] + off) for i in range(8)]
             assert res["idx"][t].tolist() == chosen
             assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# MXFP8 expert weights (OCP MX v1.0 format; the MXFP8 export of mlxcel #763
+# "Validation")
+
+def test_e4m3_hand_values():
+    g = _gold("mxfp8_hand_example.json")
+    for code, val in g["e4m3"]:
+        got = O.e4m3_value(np.array([int(code, 16)], np.uint8))[0]
+        assert got == val, code
+    for code in g["e4m3_nan"]:
+        assert np.isnan(O.e4m3_value(np.array([int(code, 16)], np.uint8))[0])
+
+
+def test_e4m3_all_codes_match_torch():
+    """Every code against an independent decoder (torch's float8_e4m3fn)."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e8m0_hand_values_and_torch():
+    g = _gold("mxfp8_hand_example.json")
+    for e, val in g["e8m0"]:
+        assert O.e8m0_value(np.array([e], np.uint8))[0] == val
+    assert np.isnan(O.e8m0_value(np.array([255], np.uint8))[0])
+    torch = pytest.importorskip("torch")
+    codes = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(O.e8m0_value(codes), ref)
+
+
+def test_mx_dequantize_block_major_scales():
+    """Scales are [K/32, N]: a transposed read gives row 1's first block the
+    wrong scale and fails here."""
+    d = _gold("mxfp8_hand_example.json")["dequant"]
+    codes = np.full((2, 64), int(d["codes_fill"], 16), np.uint8)
+    for r, k, c in d["codes_set"]:
+        codes[r, k] = int(c, 16)
+    w = O.mx_dequantize(codes, np.array(d["scales"], np.uint8))
+    for row in d["rows"]:
+        r = row["row"]
+        first = np.delete(w[r, :32], [])
+        last = w[r, 32:].copy()
+        if "at40" in row:
+            assert w[r, 40] == row["at40"]
+            last = np.delete(last, 8)
+        assert np.all(first == row["first32"]) and np.all(last == row["last32"])
+
+
+def test_mx_layer_runs_on_the_dequantised_values():
+    """The layer with stacked MXFP8 experts (lazy per-expert dequantisation,
+    packed shared slot included) equals the layer given the dequantised
+    matrices as plain float64 tensors."""
+    cfg = _tiny_cfg(hidden_size=64, moe_intermediate_size=64, shared_packed=1,
+                    hidden_act="swigluoai", route_scale=2.0)
+    rng = np.random.default_rng(4)
+    T, H, E, I = 6, 64, 3, 64
+    codes = {k: rng.integers(0, 256, (E + 1, n, kk), dtype=np.uint8)
+             for k, (n, kk) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I)))}
+    for c in codes.values():
+        c[(c & 0x7F) == 0x7F] = 0x38               # no NaN codes
+    scales = {k: rng.integers(118, 124, (E + 1, c.shape[2] // 32, c.shape[1]), dtype=np.uint8)
+              for k, c in codes.items()}
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    mx = synth.MoeInputs(cfg=cfg, x=x, w_router=wr, expert_bias=b,
+                         w_gate=O.MxStacked(codes["gate"], scales["gate"]),
+                         w_up=O.MxStacked(codes["up"], scales["up"]),
+                         w_down=O.MxStacked(codes["down"], scales["down"]))
+    dense = synth.MoeInputs(cfg=cfg, x=x, w_router=wr, expert_bias=b,
+                            w_gate=np.stack([mx.w_gate[e] for e in range(E + 1)]),
+                            w_up=np.stack([mx.w_up[e] for e in range(E + 1)]),
+                            w_down=np.stack([mx.w_down[e] for e in range(E + 1)]))
+    a, d = O.moe_forward(mx, cfg), O.moe_forward(dense, cfg)
+    assert np.array_equal(a["idx"], d["idx"]) and np.array_equal(a["out"], d["out"])
+

@@ -3,6 +3,7 @@ prefix of a larger one), bf16 rounding to nearest-even (checked against
 torch's float32 -> bfloat16 conversion), and the skewed workload's stored
 parameters."""
 import numpy as np
+import pytest
 import torch
 
 from workloads import synth
@@ -45,3 +46,31 @@ def test_skew_parameters_are_applied():
     assert np.all(inp.expert_bias[hot] > base.expert_bias[hot])
     assert abs(sk["hot_share"] - 0.60) <= 0.01
     assert 0.03 <= sk["tie_straddle_rate"] <= 0.07
+
+
+def test_mxfp8_quantiser():
+    """Scales follow the OCP MX rule 2^(floor(log2 amax) - 8); codes are the
+    round-to-nearest-even E4M3 cast (torch's) of the clamped scaled values;
+    the MXFP8 workload draws the same fp32 weights as the bf16 one."""
+    rng = np.random.default_rng(0)
+    w = (rng.standard_normal((48, 256)) * 0.02).astype(np.float32)
+    w[3, 32:64] = 0.0                                   # an all-zero block
+    codes, sc = synth.quantize_mxfp8(w)
+    assert codes.shape == w.shape and sc.shape == (8, 48) and sc.dtype == np.uint8
+    amax = np.abs(w.astype(np.float64)).reshape(48, 8, 32).max(2)
+    nz = amax > 0
+    assert np.array_equal(sc.T[nz].astype(np.int64), np.floor(np.log2(amax[nz])).astype(np.int64) - 8 + 127)
+    v = w.astype(np.float64).reshape(48, 8, 32) / np.exp2(sc.T.astype(np.float64) - 127)[:, :, None]
+    ref = torch.from_numpy(np.clip(v, -448, 448).reshape(48, 256)).to(torch.float8_e4m3fn)
+    assert np.array_equal(ref.view(torch.uint8).numpy() & 0x7F, codes & 0x7F)
+    assert np.all(codes[3, 32:64] & 0x7F == 0)
+    cfg = synth.config("trinity_nano_decode_T32_mxfp8")
+    a = synth.generate(cfg)
+    b = synth.generate(synth.config("trinity_nano_decode_T32"))
+    assert np.array_equal(a.x, b.x) and a.mx["down"].shape == (128, 256 // 32, 1024)
+    # expert 5's gate matrix is the quantised fp32 draw of its own stream
+    tmp = np.empty((256, 1024), np.float32)
+    synth._fill_normal(tmp, synth._stream(0, synth.TID_GATE, 5), cfg["w_std"], False)
+    assert np.array_equal(synth.f32_to_bf16_bits(tmp), b.w_gate[5])
+    g, gs = synth.quantize_mxfp8(tmp)
+    assert np.array_equal(a.w_gate[5], g) and np.array_equal(a.mx["gate"][5], gs)

@@ -55,6 +55,7 @@ def _cfg(**kw):
         route_scale=1.0, hidden_act="silu", act_alpha=1.702, act_limit=7.0,
         act_beta=1.0, x_scale=1.0, w_std=0.02, router_bf16_values=True,
         skew=None, rms_norm_eps=1e-5, norm_add_one=0, norm_w_std=0.1,
+        weight_format="dtype",
     )
     base.update(kw)
     if base.get("shared_intermediate_size", 0) == 0:
@@ -108,6 +109,25 @@ CONFIGS: dict[str, dict] = {
         shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
         bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
         norm_add_one=1),
+    # the same layers with MXFP8 expert weights (the M3 checkpoint's MXFP8
+    # export): the same fp32 draws, quantised instead of rounded to bf16
+    "minimax_m3_decode_T64_mxfp8": _cfg(
+        T=64, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
+        moe_intermediate_size=3072, num_shared_experts=1,
+        shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
+        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
+        norm_add_one=1, weight_format="mxfp8"),
+    "minimax_m3_prefill_T8192_mxfp8": _cfg(
+        T=8192, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
+        moe_intermediate_size=3072, num_shared_experts=1,
+        shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
+        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
+        norm_add_one=1, weight_format="mxfp8"),
+    "trinity_nano_decode_T32_mxfp8": _cfg(
+        T=32, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
+        moe_intermediate_size=256, num_shared_experts=1,
+        shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
+        route_scale=2.826, router_bf16_values=False, weight_format="mxfp8"),
 }
 
 
@@ -124,7 +144,7 @@ def layer_keys(cfg: dict) -> dict:
             "num_shared_experts", "moe_intermediate_size",
             "shared_intermediate_size", "shared_packed", "score_func",
             "route_norm", "route_scale", "hidden_act", "act_alpha",
-            "act_limit", "act_beta", "dtype")
+            "act_limit", "act_beta", "dtype", "weight_format")
     return {k: cfg[k] for k in keys}
 
 
@@ -200,6 +220,11 @@ class MoeInputs:
     ws_up: np.ndarray | None = None
     ws_down: np.ndarray | None = None  # [S, H, I_s]
     meta: dict = field(default_factory=dict)
+    # MXFP8 expert weights: the w_* / ws_* arrays hold E4M3 codes (uint8) and
+    # mx holds their E8M0 scales, block-major: [E_tot or S, K/32, N] for a
+    # stack of [N, K] matrices (keys gate, up, down, shared_gate, shared_up,
+    # shared_down)
+    mx: dict | None = None
 
 
 def load_skew(name: str) -> dict:
@@ -223,10 +248,12 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
                 cfg["shared_intermediate_size"])
     bf16 = cfg["dtype"] == "bf16"
     wdt = np.uint16 if bf16 else np.float32
+    mx = cfg.get("weight_format", "dtype") == "mxfp8"
+    xdt = wdt
     std = cfg["w_std"]
 
     # x: N(0,1) * x_scale, per 256-row block streams
-    x = np.empty((T, H), wdt)
+    x = np.empty((T, H), xdt)
     nblk = (T + X_BLOCK_ROWS - 1) // X_BLOCK_ROWS
 
     def _xblock(b):
@@ -256,25 +283,44 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
     inp = MoeInputs(cfg=dict(cfg, T=T), x=x, w_router=wr, expert_bias=bias)
 
     jobs = [(_xblock, b) for b in range(nblk)]
+
+    def _matrix(arr, sc, tid, e):
+        # one expert's matrix: fp32 draws, then bf16 rounding or MXFP8 quantisation
+        if sc is None:
+            _fill_normal(arr[e], _stream(seed, tid, e), std, bf16)
+            return
+        tmp = np.empty(arr.shape[1:], np.float32)
+        _fill_normal(tmp, _stream(seed, tid, e), std, False)
+        arr[e], sc[e] = quantize_mxfp8(tmp)
+
     if experts:
         Etot = E + (1 if cfg["shared_packed"] else 0)
-        inp.w_gate = np.empty((Etot, I, H), wdt)
-        inp.w_up = np.empty((Etot, I, H), wdt)
-        inp.w_down = np.empty((Etot, H, I), wdt)
-        for arr, tid in ((inp.w_gate, TID_GATE), (inp.w_up, TID_UP),
-                         (inp.w_down, TID_DOWN)):
+        edt = np.uint8 if mx else wdt
+        inp.w_gate = np.empty((Etot, I, H), edt)
+        inp.w_up = np.empty((Etot, I, H), edt)
+        inp.w_down = np.empty((Etot, H, I), edt)
+        if mx:
+            inp.mx = {"gate": np.empty((Etot, H // 32, I), np.uint8),
+                      "up": np.empty((Etot, H // 32, I), np.uint8),
+                      "down": np.empty((Etot, I // 32, H), np.uint8)}
+        scl = (lambda key: inp.mx[key]) if mx else (lambda key: None)
+        for arr, key, tid in ((inp.w_gate, "gate", TID_GATE), (inp.w_up, "up", TID_UP),
+                              (inp.w_down, "down", TID_DOWN)):
             for e in range(Etot):
-                jobs.append((lambda e, arr=arr, tid=tid:
-                             _fill_normal(arr[e], _stream(seed, tid, e), std, bf16), e))
+                jobs.append((lambda e, arr=arr, sc=scl(key), tid=tid: _matrix(arr, sc, tid, e), e))
         if S > 0 and not cfg["shared_packed"]:
-            inp.ws_gate = np.empty((S, Is, H), wdt)
-            inp.ws_up = np.empty((S, Is, H), wdt)
-            inp.ws_down = np.empty((S, H, Is), wdt)
-            for arr, tid in ((inp.ws_gate, TID_SGATE), (inp.ws_up, TID_SUP),
-                             (inp.ws_down, TID_SDOWN)):
+            inp.ws_gate = np.empty((S, Is, H), edt)
+            inp.ws_up = np.empty((S, Is, H), edt)
+            inp.ws_down = np.empty((S, H, Is), edt)
+            if mx:
+                inp.mx.update({"shared_gate": np.empty((S, H // 32, Is), np.uint8),
+                               "shared_up": np.empty((S, H // 32, Is), np.uint8),
+                               "shared_down": np.empty((S, Is // 32, H), np.uint8)})
+            for arr, key, tid in ((inp.ws_gate, "shared_gate", TID_SGATE),
+                                  (inp.ws_up, "shared_up", TID_SUP),
+                                  (inp.ws_down, "shared_down", TID_SDOWN)):
                 for s in range(S):
-                    jobs.append((lambda s, arr=arr, tid=tid:
-                                 _fill_normal(arr[s], _stream(seed, tid, s), std, bf16), s))
+                    jobs.append((lambda s, arr=arr, sc=scl(key), tid=tid: _matrix(arr, sc, tid, s), s))
     nthr = _threads()
     if nthr > 1 and len(jobs) > 1:
         with ThreadPoolExecutor(nthr) as ex:
@@ -287,6 +333,42 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
         sk = load_skew(cfg["skew"])
         apply_skew_params(inp, sk)
     return inp
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 (OCP Microscaling v1.0: E4M3 elements, one E8M0 scale per 32 inputs)
+
+def _e4m3_nonneg() -> np.ndarray:
+    """The 127 finite non-negative E4M3 values, codes 0x00..0x7E in order
+    (exponent bias 7, 3 mantissa bits, subnormals below 2^-6)."""
+    c = np.arange(127)
+    ef, m = c >> 3, (c & 7).astype(np.float64)
+    return np.where(ef == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(ef - 7.0))
+
+
+_E4M3_NONNEG = _e4m3_nonneg()
+_E4M3_MID = (_E4M3_NONNEG[:-1] + _E4M3_NONNEG[1:]) / 2.0
+
+
+def quantize_mxfp8(w: np.ndarray):
+    """float32 [N, K] -> (codes uint8 [N, K], scales uint8 [K/32, N]).
+
+    Per block of 32 inputs of a row: scale 2^(floor(log2 amax) - 8) (8 is
+    E4M3's largest exponent), elements rounded to the nearest E4M3 value
+    (ties to the even code) after clamping to +-448."""
+    N, K = w.shape
+    blk = np.asarray(w, dtype=np.float64).reshape(N, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
+    ex = np.where(amax > 0, ex - 1, -119)        # floor(log2 amax); zero block: scale byte 0
+    sbyte = np.clip(ex - 8 + 127, 0, 254).astype(np.uint8)
+    v = blk / np.exp2(sbyte.astype(np.float64) - 127.0)[:, :, None]
+    a = np.minimum(np.abs(v), 448.0)
+    i = np.searchsorted(_E4M3_MID, a, side="left")
+    tie = (i < _E4M3_MID.size) & (a == _E4M3_MID[np.minimum(i, _E4M3_MID.size - 1)]) & (i % 2 == 1)
+    i = i + tie
+    codes = (i | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8).reshape(N, K)
+    return codes, np.ascontiguousarray(sbyte.T)
 
 
 def norm_weights(cfg: dict) -> dict:
