@@ -45,18 +45,34 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
     H, E, k = cfg["hidden_size"], cfg["num_experts"], cfg["num_experts_per_tok"]
     I, S = cfg["moe_intermediate_size"], cfg["num_shared_experts"]
     Is = cfg["shared_intermediate_size"] or I
-    bw = 2 if cfg["dtype"] == "bf16" else 4
+    bx = 2 if cfg["dtype"] == "bf16" else 4
+    # expert weight bytes per weight: MXFP8 is one code plus 1/32 of a scale byte
+    bw = 1 + 1 / 32 if cfg.get("weight_format") == "mxfp8" else bx
     flops = T * (2 * H * E + 6 * k * H * I + 6 * S * H * Is)
     touched = E if idx is None else int(np.unique(idx).size)
-    bytes_ = touched * 3 * H * I * bw + S * 3 * H * Is * bw + 4 * E * H + 2 * T * H * bw + 4 * E
+    bytes_ = touched * 3 * H * I * bw + S * 3 * H * Is * bw + 4 * E * H + 2 * T * H * bx + 4 * E
     gate_up_flops = 4 * T * H * (k * I + S * Is)
-    gate_up_bytes = touched * 2 * H * I * bw + S * 2 * H * Is * bw + T * H * bw \
-        + (T * k * I + T * S * Is) * bw
+    gate_up_bytes = touched * 2 * H * I * bw + S * 2 * H * Is * bw + T * H * bx \
+        + (T * k * I + T * S * Is) * bx
     return dict(flops=flops, bytes=bytes_, touched=touched, gate_up_flops=gate_up_flops,
                 gate_up_bytes=gate_up_bytes)
 
 
-GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_common.h", "moe_common.h", "moe_kernels.h")
+GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_decode.hip", "moe_gemm_common.h", "moe_common.h",
+                "moe_kernels.h")
+
+
+def gate_up_kernel(cfg: dict, T: int) -> str:
+    """Name of the grouped gate/up kernel the library runs for this workload
+    (the 32-row tile kernel for MXFP8 weights and for decode-sized bf16
+    batches, else the 128-row one)."""
+    H, I, k, E = cfg["hidden_size"], cfg["moe_intermediate_size"], cfg["num_experts_per_tok"], \
+        cfg["num_experts"]
+    S, Is = cfg["num_shared_experts"], cfg["shared_intermediate_size"] or I
+    fits = H % 256 == 0 and I % 256 == 0 and (S * Is) % 256 == 0
+    dec = cfg.get("weight_format") == "mxfp8" or (
+        cfg["dtype"] == "bf16" and fits and T * k <= 32 * E)
+    return "moe_gate_up_decode_kernel" if dec else "moe_gate_up_kernel"
 
 
 def gemm_source_sha() -> str:
@@ -69,18 +85,22 @@ def gemm_source_sha() -> str:
     return h.hexdigest()
 
 
-def traffic_from_profile(kernel: str, src_sha: str, units: float):
-    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
-    if the summary is missing or was taken on another version of the source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _traffic_records() -> list:
     try:
-        with open(path) as f:
-            rec = json.load(f).get(kernel)
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            return json.load(f).get("records", [])
     except (OSError, ValueError):
-        return None
-    if not rec or rec.get("source_sha256") != src_sha:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return []
+
+
+def traffic_from_profile(kernel: str, workload: str, src_sha: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed PMC
+    summaries, or None if there is none or it was taken on other sources."""
+    for rec in _traffic_records():
+        if (rec.get("kernel"), rec.get("workload"), rec.get("source_sha256")) == \
+                (kernel, workload, src_sha):
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -140,7 +160,7 @@ def _pmc_means(d: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def summarize_traffic(d: str, kernel: str = "moe_gate_up_kernel") -> str:
+def summarize_traffic(d: str, kernel: str | None = None) -> str:
     """HBM traffic per launch from two `rocprofv3 --pmc` runs of the bench
     (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) scaled by what the same
     counters read for a plain copy of known size; writes profiles/traffic.json
@@ -149,6 +169,7 @@ def summarize_traffic(d: str, kernel: str = "moe_gate_up_kernel") -> str:
     d/pmc_WRITE_SIZE, d/cal_FETCH_SIZE, d/cal_WRITE_SIZE (rocprofv3 outputs)."""
     with open(os.path.join(d, "bench.json")) as f:
         line = json.loads(f.read().strip().splitlines()[-1])
+    kernel = kernel or line["roofline"]["kernel"]
     fetch = _pmc_means(os.path.join(d, "pmc_FETCH_SIZE"), "FETCH_SIZE")
     write = _pmc_means(os.path.join(d, "pmc_WRITE_SIZE"), "WRITE_SIZE")
     cal_f = _pmc_means(os.path.join(d, "cal_FETCH_SIZE"), "FETCH_SIZE")
@@ -161,12 +182,14 @@ def summarize_traffic(d: str, kernel: str = "moe_gate_up_kernel") -> str:
     w_scale = copy_bytes / (cal_w[ck[0]] * 1024)
     alg = line["layer"]["gate_up_bytes"]
     hbm = fetch[kernel] * 1024 * f_scale + write[kernel] * 1024 * w_scale
-    rec = {kernel: {"workload": line["config"]["workload"], "source_sha256": gemm_source_sha(),
-                    "fetch_kib": fetch[kernel], "write_kib": write[kernel],
-                    "fetch_scale": f_scale, "write_scale": w_scale,
-                    "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg}}
+    wl = line["config"]["workload"]
+    rec = {"kernel": kernel, "workload": wl, "source_sha256": gemm_source_sha(),
+           "fetch_kib": fetch[kernel], "write_kib": write[kernel],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg}
+    recs = [r for r in _traffic_records() if (r.get("kernel"), r.get("workload")) != (kernel, wl)]
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump({"records": recs + [rec]}, f, indent=1)
     out = [f"Calibration: a plain copy of 256 MiB reads FETCH_SIZE = {cal_f[ck[0]]:.0f} KiB "
            f"and WRITE_SIZE = {cal_w[ck[0]]:.0f} KiB per dispatch, so counter values are "
            f"scaled by {f_scale:.3f} (fetch) and {w_scale:.3f} (write) to get bytes.", "",
@@ -190,10 +213,14 @@ def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    wts = {n: getattr(inp, n) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    if inp.mx is not None:  # MXFP8 stacks, dequantised one expert at a time
+        keys = {"w_gate": "gate", "w_up": "up", "w_down": "down", "ws_gate": "shared_gate",
+                "ws_up": "shared_up", "ws_down": "shared_down"}
+        wts = {n: (O.MxStacked(a, inp.mx[keys[n]]) if a is not None else None)
+               for n, a in wts.items()}
     sub = synth.MoeInputs(cfg=dict(cfg, T=sample_tokens), x=inp.x[:sample_tokens],
-                          w_router=inp.w_router, expert_bias=inp.expert_bias,
-                          w_gate=inp.w_gate, w_up=inp.w_up, w_down=inp.w_down,
-                          ws_gate=inp.ws_gate, ws_up=inp.ws_up, ws_down=inp.ws_down)
+                          w_router=inp.w_router, expert_bias=inp.expert_bias, **wts)
     t0 = time.perf_counter()
     O.moe_forward(sub, cfg)
     dt = time.perf_counter() - t0
@@ -229,7 +256,7 @@ def block_measurements(moe, synth, cfg, keys, T, ordered, args, stream, t, layer
     def block():
         moe.moe_block_forward(keys, norm, T, t["x"], pre_w, post_w, t["wr"], t["b"], t["wg"],
                               t["wu"], t["wd"], t["sg"], t["su"], t["sd"], None, None, None, hout,
-                              int(ordered), t["ws"], stream)
+                              int(ordered), t["ws"], stream, mx=t["mx"])
 
     for _ in range(args.warmup):
         block()
@@ -332,6 +359,7 @@ def main():
     x, wr, b = d(inp.x), d(inp.w_router), d(inp.expert_bias)
     wg, wu, wd = d(inp.w_gate), d(inp.w_up), d(inp.w_down)
     sg, su, sd = d(inp.ws_gate), d(inp.ws_up), d(inp.ws_down)
+    mx = {key: d(v) for key, v in inp.mx.items()} if inp.mx is not None else None
     dt = moe.torch_dtype(keys)
     dev = x.device
     # the block's workspace holds the layer's, plus the normalised rows
@@ -366,9 +394,9 @@ def main():
         rec(2)
         moe.moe_permute(keys, T, idx, offs, sr, rp, ws, st)
         rec(3)
-        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, st)
+        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, st, mx=mx)
         rec(4)
-        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, st)
+        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, st, mx=mx)
         rec(5)
         moe.moe_combine(keys, T, acc, yp, rp, w, out, st)
         rec(6)
@@ -389,7 +417,7 @@ def main():
     # (intermediates in the library workspace)
     def layer():
         moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
-                              out, int(ordered), ws, torch.cuda.current_stream())
+                              out, int(ordered), ws, torch.cuda.current_stream(), mx=mx)
 
     for _ in range(args.warmup):
         layer()
@@ -449,7 +477,8 @@ def main():
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     r0.record(stream)
     for _ in range(n_rl):
-        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream)
+        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream,
+                                       mx=mx)
     r1.record(stream)
     torch.cuda.synchronize()
     gu_ms = r0.elapsed_time(r1) / n_rl
@@ -462,14 +491,15 @@ def main():
         roof = {"bound": "hbm", "achieved": alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profile("moe_gate_up_kernel", sha, 1.0)
-    roof["kernel"] = "moe_gate_up_kernel"
+    kname = gate_up_kernel(cfg, T)
+    roof["traffic"] = traffic_from_profile(kname, args.workload, sha)
+    roof["kernel"] = kname
     roof["ms_per_launch"] = gu_ms
     roof["launches_timed"] = n_rl
 
     blk = block_measurements(moe, synth, cfg, keys, T, ordered, args, stream,
                              dict(x=x, wr=wr, b=b, wg=wg, wu=wu, wd=wd, sg=sg, su=su, sd=sd,
-                                  acc=acc, yp=yp, rp=rp, w=w, out=out, ws=ws), ms_eager)
+                                  acc=acc, yp=yp, rp=rp, w=w, out=out, ws=ws, mx=mx), ms_eager)
 
     sample = args.cpu_sample
     if sample is None:
@@ -493,6 +523,8 @@ def main():
                    "num_experts_per_tok": k, "moe_intermediate_size": I,
                    "num_shared_experts": S, "shared_intermediate_size": Is,
                    "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"],
+                   "expert_weights": ("mxfp8" if cfg.get("weight_format") == "mxfp8"
+                                      else cfg["dtype"]),
                    "combine": args.combine, "graph": args.graph, "entry": "moe_layer_forward"},
         "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],

@@ -72,6 +72,38 @@ typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLUOAI = 1 } moe_hidden_act;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage of the expert weights (routed and shared; the router stays fp32):
+ *   MOE_WEIGHTS_DTYPE  as moe_config.dtype
+ *   MOE_WEIGHTS_MXFP8  OCP Microscaling (MX) v1.0 MXFP8, the format of the
+ *                      MiniMax-M3 MXFP8 export (mlxcel #763 "Validation"):
+ *                      each weight is one E4M3 code (uint8; bias 7, largest
+ *                      finite 448, 0x7F/0xFF NaN), and every 32 consecutive
+ *                      inputs of a weight row share one E8M0 scale byte
+ *                      (2^(e-127)); w = e4m3(code) * 2^(e-127). The code
+ *                      tensors keep the weights' shapes and layout; the
+ *                      scales are passed in moe_mx_scales. Needs dtype bf16
+ *                      (activations stay bf16, accumulation fp32), and H, I
+ *                      and S*I_s multiples of 256 (else MOE_ERR_UNSUPPORTED). */
+typedef enum { MOE_WEIGHTS_DTYPE = 0, MOE_WEIGHTS_MXFP8 = 1 } moe_weight_format;
+
+/* E8M0 scales of MXFP8 expert weights, block-major: for an [N, K] weight
+ * matrix the scales are [K/32, N] (for every block of 32 inputs, the scales
+ * of all N rows), stacked like the weights:
+ *   gate, up      [E_tot, H/32, I]     down        [E_tot, I/32, H]
+ *   shared_gate,  [S, H/32, I_s]       shared_down [S, I_s/32, H]
+ *   shared_up                          (NULL when S == 0 or packed: the
+ *                                       packed shared expert's scales are
+ *                                       slot E of gate/up/down)
+ * A checkpoint's [N, K/32] scale tensor is the transpose of this layout. */
+typedef struct {
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const uint8_t* shared_gate;
+  const uint8_t* shared_up;
+  const uint8_t* shared_down;
+} moe_mx_scales;
+
 /* Layer configuration (host struct, passed by const pointer). Field names
  * follow the pages' config keys. */
 typedef struct {
@@ -92,7 +124,9 @@ typedef struct {
   float act_alpha;                  /* swigluoai alpha (1.702)                   */
   float act_limit;                  /* swigluoai limit (7.0)                     */
   float act_beta;                   /* swigluoai beta  (1.0)                     */
-  int32_t dtype;                    /* moe_dtype of x, expert weights, h, out    */
+  int32_t dtype;                    /* moe_dtype of x, h, out (and the expert
+                                       weights when weight_format is DTYPE)     */
+  int32_t weight_format;            /* moe_weight_format of the expert weights   */
 } moe_config;
 
 /* Bytes of device workspace that moe_layer_forward (and every stage entry
@@ -142,12 +176,15 @@ moe_status moe_permute(const moe_config* cfg, int64_t T,
  *   h_shared[t, s*I_s:(s+1)*I_s] = act(x[t] . Ws_g[s]^T, x[t] . Ws_u[s]^T)
  *   x [T,H]; w_gate, w_up [E_tot,I,H]; ws_gate, ws_up [S,I_s,H] (NULL when
  *   S == 0 or the shared expert is packed: then slot E of w_gate/w_up is
- *   used); h [T*k, I] out; h_shared [T, S*I_s] out (NULL iff S == 0). */
+ *   used); mx: host pointer to the scales when weight_format is MXFP8
+ *   (ignored otherwise, may be NULL); h [T*k, I] out; h_shared [T, S*I_s]
+ *   out (NULL iff S == 0). */
 moe_status moe_grouped_gate_up_swiglu(
     const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
     const void* w_up, const void* ws_gate, const void* ws_up,
-    const int32_t* expert_offsets, const int32_t* sorted_rows, void* h,
-    void* h_shared, void* ws, size_t ws_bytes, moe_stream_t stream);
+    const moe_mx_scales* mx, const int32_t* expert_offsets,
+    const int32_t* sorted_rows, void* h, void* h_shared, void* ws,
+    size_t ws_bytes, moe_stream_t stream);
 
 /* Grouped down projection with the combine:
  *   acc[t, :]  = sum_s h_shared[t, s] . Ws_d[s]^T          (stored; zeros
@@ -158,12 +195,14 @@ moe_status moe_grouped_gate_up_swiglu(
  *     y_perm != NULL:  y_perm[p, :] = h[p] . W_d[e]^T   (dtype, unweighted;
  *                      moe_combine then sums in a fixed order)
  *   h [T*k, I]; w_down [E_tot,H,I]; h_shared [T,S*I_s]; ws_down [S,H,I_s] or
- *   NULL (packed or S == 0); topk_w [T,k]; acc [T,H] fp32 out. The shared
+ *   NULL (packed or S == 0); mx as for the gate/up call; topk_w [T,k];
+ *   acc [T,H] fp32 out. The shared
  *   experts carry weight exactly 1 and no route_scale (HF "AFMoE" doc:
  *   route_scale scales the routed experts; mlxcel #763: fixed score 1.0). */
 moe_status moe_grouped_down(const moe_config* cfg, int64_t T, const void* h,
                             const void* w_down, const void* h_shared,
-                            const void* ws_down, const int32_t* expert_offsets,
+                            const void* ws_down, const moe_mx_scales* mx,
+                            const int32_t* expert_offsets,
                             const int32_t* sorted_rows, const float* topk_w,
                             float* acc, void* y_perm, void* ws,
                             size_t ws_bytes, moe_stream_t stream);
@@ -179,7 +218,8 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
  * down + combine, cast.
  *   x [T,H] dtype; w_router [E,H] fp32; expert_bias [E] fp32 or NULL;
  *   w_gate, w_up, w_down stacked experts; ws_* separate shared experts or
- *   NULL; router_logits_in [T,E] or NULL (when given, the router GEMM is
+ *   NULL; mx: scales of MXFP8 weights (host pointer) or NULL;
+ *   router_logits_in [T,E] or NULL (when given, the router GEMM is
  *   skipped and these logits are routed); router_logits_out [T,E] or NULL;
  *   topk_idx_out [T,k] / topk_w_out [T,k] or NULL; out [T,H] dtype.
  *   deterministic: 0 = fp32 atomic combine, 1 = fixed-order combine. */
@@ -187,7 +227,7 @@ moe_status moe_layer_forward(
     const moe_config* cfg, int64_t T, const void* x, const float* w_router,
     const float* expert_bias, const void* w_gate, const void* w_up,
     const void* w_down, const void* ws_gate, const void* ws_up,
-    const void* ws_down, const float* router_logits_in,
+    const void* ws_down, const moe_mx_scales* mx, const float* router_logits_in,
     float* router_logits_out, int32_t* topk_idx_out, float* topk_w_out,
     void* out, int32_t deterministic, void* ws, size_t ws_bytes,
     moe_stream_t stream);
@@ -246,7 +286,8 @@ moe_status moe_block_forward(
     const void* h, const float* pre_norm_w, const float* post_norm_w,
     const float* w_router, const float* expert_bias, const void* w_gate,
     const void* w_up, const void* w_down, const void* ws_gate,
-    const void* ws_up, const void* ws_down, float* router_logits_out,
+    const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
+    float* router_logits_out,
     int32_t* topk_idx_out, float* topk_w_out, void* out,
     int32_t deterministic, void* ws, size_t ws_bytes, moe_stream_t stream);
 

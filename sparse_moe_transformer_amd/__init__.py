@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLUOAI = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MXFP8 = 0, 1
 
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
@@ -48,7 +49,30 @@ class MoeConfig(ctypes.Structure):
         ("act_limit", ctypes.c_float),
         ("act_beta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32),
     ]
+
+
+class MoeMxScales(ctypes.Structure):
+    """Mirror of moe_mx_scales (include/moe.h): device pointers of the E8M0
+    scale tensors of MXFP8 expert weights."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")]
+
+
+def make_mx_scales(mx):
+    """MoeMxScales from a dict of device tensors (keys as the struct fields),
+    or None."""
+    if mx is None or isinstance(mx, MoeMxScales):
+        return mx
+    m = MoeMxScales()
+    for n, _ in MoeMxScales._fields_:
+        setattr(m, n, _p(mx.get(n)))
+    return m
+
+
+def _mxp(m):
+    return ctypes.byref(m) if m is not None else None
 
 
 class MoeNormConfig(ctypes.Structure):
@@ -69,6 +93,7 @@ def make_norm_config(norm) -> MoeNormConfig:
 _SCORE = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 _ACT = {"silu": MOE_ACT_SILU, "swigluoai": MOE_ACT_SWIGLUOAI}
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16}
+_WF = {"dtype": MOE_WEIGHTS_DTYPE, "mxfp8": MOE_WEIGHTS_MXFP8}
 
 
 def make_config(cfg) -> MoeConfig:
@@ -94,6 +119,8 @@ def make_config(cfg) -> MoeConfig:
     c.act_beta = float(cfg.get("act_beta", 1.0))
     dt = cfg.get("dtype", "bf16")
     c.dtype = _DT.get(dt, dt) if isinstance(dt, str) else dt
+    wf = cfg.get("weight_format", "dtype")
+    c.weight_format = _WF.get(wf, wf) if isinstance(wf, str) else wf
     return c
 
 
@@ -124,14 +151,14 @@ def lib() -> ctypes.CDLL:
             "moe_router_logits": [cp, i64, _vp, _vp, _vp, _vp, sz, _vp],
             "moe_route": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
             "moe_permute": [cp, i64, _vp, _vp, _vp, _vp, _vp, sz, _vp],
-            "moe_grouped_gate_up_swiglu": [cp, i64] + [_vp] * 9 + [_vp, sz, _vp],
-            "moe_grouped_down": [cp, i64] + [_vp] * 9 + [_vp, sz, _vp],
+            "moe_grouped_gate_up_swiglu": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
+            "moe_grouped_down": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
             "moe_combine": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
-            "moe_layer_forward": [cp, i64] + [_vp] * 14 + [i32, _vp, sz, _vp],
+            "moe_layer_forward": [cp, i64] + [_vp] * 15 + [i32, _vp, sz, _vp],
             "moe_rms_norm": [cp, ncp, i64, _vp, _vp, _vp, _vp],
             "moe_combine_norm_residual": [cp, ncp, i64] + [_vp] * 7 + [_vp],
             "moe_block_workspace_size": [cp, i64, ctypes.POINTER(sz)],
-            "moe_block_forward": [cp, ncp, i64] + [_vp] * 15 + [i32, _vp, sz, _vp],
+            "moe_block_forward": [cp, ncp, i64] + [_vp] * 16 + [i32, _vp, sz, _vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -233,22 +260,27 @@ def moe_permute(cfg, T, topk_idx, expert_offsets, sorted_rows, row_pos, ws, stre
 
 
 def moe_grouped_gate_up_swiglu(cfg, T, x, w_gate, w_up, ws_gate, ws_up, expert_offsets,
-                               sorted_rows, h, h_shared, ws, stream=None):
+                               sorted_rows, h, h_shared, ws, stream=None, mx=None):
+    """mx: MXFP8 scales (dict of device tensors or MoeMxScales), in the C
+    argument list after ws_up."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     _need(h, T * c.num_experts_per_tok * c.moe_intermediate_size, "h")
     _call("moe_grouped_gate_up_swiglu", ctypes.byref(c), int(T), _p(x), _p(w_gate), _p(w_up),
-          _p(ws_gate), _p(ws_up), _p(expert_offsets), _p(sorted_rows), _p(h), _p(h_shared),
-          _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
+          _p(ws_gate), _p(ws_up), _mxp(m), _p(expert_offsets), _p(sorted_rows), _p(h),
+          _p(h_shared), _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
 
 
 def moe_grouped_down(cfg, T, h, w_down, h_shared, ws_down, expert_offsets, sorted_rows, topk_w,
-                     acc, y_perm, ws, stream=None):
+                     acc, y_perm, ws, stream=None, mx=None):
+    """mx: MXFP8 scales, in the C argument list after ws_down."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     _need(acc, T * c.hidden_size, "acc")
     _need(y_perm, T * c.num_experts_per_tok * c.hidden_size, "y_perm")
     _call("moe_grouped_down", ctypes.byref(c), int(T), _p(h), _p(w_down), _p(h_shared),
-          _p(ws_down), _p(expert_offsets), _p(sorted_rows), _p(topk_w), _p(acc), _p(y_perm),
-          _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
+          _p(ws_down), _mxp(m), _p(expert_offsets), _p(sorted_rows), _p(topk_w), _p(acc),
+          _p(y_perm), _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
 
 
 def moe_combine(cfg, T, acc, y_perm, row_pos, topk_w, out, stream=None):
@@ -260,8 +292,10 @@ def moe_combine(cfg, T, acc, y_perm, row_pos, topk_w, out, stream=None):
 
 def moe_layer_forward(cfg, T, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                       ws_down, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
-                      out, deterministic, ws, stream=None):
+                      out, deterministic, ws, stream=None, mx=None):
+    """mx: MXFP8 scales, in the C argument list after ws_down."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     k = c.num_experts_per_tok
     _need(x, T * c.hidden_size, "x")
     _need(out, T * c.hidden_size, "out")
@@ -270,7 +304,7 @@ def moe_layer_forward(cfg, T, x, w_router, expert_bias, w_gate, w_up, w_down, ws
     _need(topk_idx_out, T * k, "topk_idx_out")
     _need(topk_w_out, T * k, "topk_w_out")
     _call("moe_layer_forward", ctypes.byref(c), int(T), _p(x), _p(w_router), _p(expert_bias),
-          _p(w_gate), _p(w_up), _p(w_down), _p(ws_gate), _p(ws_up), _p(ws_down),
+          _p(w_gate), _p(w_up), _p(w_down), _p(ws_gate), _p(ws_up), _p(ws_down), _mxp(m),
           _p(router_logits_in), _p(router_logits_out), _p(topk_idx_out), _p(topk_w_out),
           _p(out), int(deterministic), _p(ws), ws.numel() if ws is not None else 0,
           _stream(stream))
@@ -308,8 +342,10 @@ def moe_block_workspace_size(cfg, T: int) -> int:
 
 def moe_block_forward(cfg, norm, T, h, pre_norm_w, post_norm_w, w_router, expert_bias, w_gate,
                       w_up, w_down, ws_gate, ws_up, ws_down, router_logits_out, topk_idx_out,
-                      topk_w_out, out, deterministic, ws, stream=None):
+                      topk_w_out, out, deterministic, ws, stream=None, mx=None):
+    """mx: MXFP8 scales, in the C argument list after ws_down."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     n = make_norm_config(norm)
     k = c.num_experts_per_tok
     _need(h, T * c.hidden_size, "h")
@@ -321,7 +357,7 @@ def moe_block_forward(cfg, norm, T, h, pre_norm_w, post_norm_w, w_router, expert
     _need(topk_w_out, T * k, "topk_w_out")
     _call("moe_block_forward", ctypes.byref(c), ctypes.byref(n), int(T), _p(h), _p(pre_norm_w),
           _p(post_norm_w), _p(w_router), _p(expert_bias), _p(w_gate), _p(w_up), _p(w_down),
-          _p(ws_gate), _p(ws_up), _p(ws_down), _p(router_logits_out), _p(topk_idx_out),
+          _p(ws_gate), _p(ws_up), _p(ws_down), _mxp(m), _p(router_logits_out), _p(topk_idx_out),
           _p(topk_w_out), _p(out), int(deterministic), _p(ws),
           ws.numel() if ws is not None else 0, _stream(stream))
 

@@ -16,7 +16,9 @@ namespace {
 struct Dims {
   int64_t T;
   int H, E, k, S, I, Is, packed, dtype;
-  size_t es;  // element size of dtype tensors
+  size_t es;   // element size of dtype tensors
+  int fp8;     // MXFP8 expert weights
+  size_t wes;  // element size of expert weights (1 for MXFP8)
 };
 
 constexpr int64_t kMaxTokens = 1 << 24;
@@ -46,6 +48,8 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
       !(std::isfinite(c->act_alpha) && std::isfinite(c->act_limit) && std::isfinite(c->act_beta)))
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_MXFP8)
+    return MOE_ERR_INVALID_ARG;
   if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   d->T = T;
   d->H = c->hidden_size;
@@ -57,6 +61,11 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
   d->packed = c->shared_packed;
   d->dtype = c->dtype;
   d->es = c->dtype == MOE_BF16 ? 2 : 4;
+  d->fp8 = c->weight_format == MOE_WEIGHTS_MXFP8;
+  d->wes = d->fp8 ? 1 : d->es;
+  // MXFP8 weights run on the 32-row tile kernels (bf16 activations)
+  if (d->fp8 && (c->dtype != MOE_BF16 || !gemm_decode_fits(T, d->H, d->I, d->k, d->S, d->Is)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -143,7 +152,24 @@ GemmArgs base_args(const moe_config* c, const Dims& d) {
 }
 
 const void* shared_slot(const void* stacked, const Dims& d, size_t per_expert_elems) {
-  return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.es;
+  return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.wes;
+}
+
+// MXFP8 scales: present and complete exactly when the weights are MXFP8
+moe_status check_mx(const Dims& d, const moe_mx_scales* mx, bool gate_up, bool down) {
+  if (!d.fp8) return MOE_OK;
+  if (!mx) return MOE_ERR_INVALID_ARG;
+  if (gate_up && (!mx->gate || !mx->up)) return MOE_ERR_INVALID_ARG;
+  if (down && !mx->down) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed) {
+    if (gate_up && (!mx->shared_gate || !mx->shared_up)) return MOE_ERR_INVALID_ARG;
+    if (down && !mx->shared_down) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+const uint8_t* scale_slot(const uint8_t* stacked, const Dims& d, size_t per_expert) {
+  return stacked + (size_t)d.E * per_expert;
 }
 
 // Grouped-GEMM tile choice. Decode-sized batches (at most 32 rows per expert
@@ -151,6 +177,7 @@ const void* shared_slot(const void* stacked, const Dims& d, size_t per_expert_el
 // K-steps in flight per compute unit. MOE_GEMM_TILE=32 or =128 forces one
 // kernel (a testing knob; 32 still needs bf16 and gemm_decode_fits).
 bool use_decode(const Dims& d) {
+  if (d.fp8) return true;  // the only kernels with MXFP8 weights (check_cfg checked the fit)
   if (d.dtype != MOE_BF16 || !gemm_decode_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
   if (const char* e = std::getenv("MOE_GEMM_TILE")) {
     if (std::strcmp(e, "128") == 0) return false;
@@ -163,9 +190,17 @@ bool use_decode(const Dims& d) {
 
 moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
                       const void* w_up, const void* ws_gate, const void* ws_up,
-                      const int32_t* offsets, const int32_t* sorted_rows, void* h,
-                      void* h_shared, hipStream_t st) {
+                      const moe_mx_scales* mx, const int32_t* offsets,
+                      const int32_t* sorted_rows, void* h, void* h_shared, hipStream_t st) {
   GemmArgs g = base_args(c, d);
+  if (d.fp8) {
+    g.fp8 = 1;
+    g.sw0 = mx->gate;
+    g.sw1 = mx->up;
+    const size_t per = (size_t)(d.H / 32) * d.I;
+    g.sws0 = d.packed ? scale_slot(mx->gate, d, per) : mx->shared_gate;
+    g.sws1 = d.packed ? scale_slot(mx->up, d, per) : mx->shared_up;
+  }
   const bool dec = use_decode(d);
   const int BM = dec ? gemm_decode_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
@@ -194,10 +229,15 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
 }
 
 moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void* w_down,
-                   const void* h_shared, const void* ws_down, const int32_t* offsets,
-                   const int32_t* sorted_rows, const float* topk_w, float* acc, void* y_perm,
-                   hipStream_t st) {
+                   const void* h_shared, const void* ws_down, const moe_mx_scales* mx,
+                   const int32_t* offsets, const int32_t* sorted_rows, const float* topk_w,
+                   float* acc, void* y_perm, hipStream_t st) {
   GemmArgs g = base_args(c, d);
+  if (d.fp8) {
+    g.fp8 = 1;
+    g.sw0 = mx->down;
+    g.sws0 = d.packed ? scale_slot(mx->down, d, (size_t)(d.I / 32) * d.H) : mx->shared_down;
+  }
   const bool dec = use_decode(d);
   const int BM = dec ? gemm_decode_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
@@ -267,7 +307,7 @@ struct LayerOut {
 moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const float* w_router,
                      const float* expert_bias, const void* w_gate, const void* w_up,
                      const void* w_down, const void* ws_gate, const void* ws_up,
-                     const void* ws_down, const float* router_logits_in,
+                     const void* ws_down, const moe_mx_scales* mx, const float* router_logits_in,
                      float* router_logits_out, int32_t* topk_idx_out, float* topk_w_out,
                      int32_t deterministic, const Ws& w, hipStream_t st, LayerOut* res) {
   const int T = (int)d.T;
@@ -285,11 +325,11 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
                               cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st)));
   MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
                                 w.local_rank, w.chunk_hist, st)));
-  MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, w.offsets, w.sorted_rows, w.h,
+  MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, mx, w.offsets, w.sorted_rows, w.h,
                      w.h_shared, st));
   void* yp = deterministic ? w.y_perm : nullptr;
-  MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, w.offsets, w.sorted_rows, tw, w.acc,
-                  yp, st));
+  MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, mx, w.offsets, w.sorted_rows, tw,
+                  w.acc, yp, st));
   res->topk_w = tw;
   res->y_perm = yp;
   return MOE_OK;
@@ -353,7 +393,8 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx
 
 moe_status moe_grouped_gate_up_swiglu(const moe_config* cfg, int64_t T, const void* x,
                                       const void* w_gate, const void* w_up, const void* ws_gate,
-                                      const void* ws_up, const int32_t* expert_offsets,
+                                      const void* ws_up, const moe_mx_scales* mx,
+                                      const int32_t* expert_offsets,
                                       const int32_t* sorted_rows, void* h, void* h_shared,
                                       void* ws, size_t ws_bytes, moe_stream_t stream) {
   Dims d;
@@ -362,14 +403,15 @@ moe_status moe_grouped_gate_up_swiglu(const moe_config* cfg, int64_t T, const vo
   if (!x || !w_gate || !w_up || !expert_offsets || !sorted_rows || !h) return MOE_ERR_INVALID_ARG;
   if (d.S && !h_shared) return MOE_ERR_INVALID_ARG;
   if (d.S && !d.packed && (!ws_gate || !ws_up)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_mx(d, mx, true, false));
   (void)ws;
   (void)ws_bytes;
-  return do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, expert_offsets, sorted_rows, h,
+  return do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, mx, expert_offsets, sorted_rows, h,
                     h_shared, (hipStream_t)stream);
 }
 
 moe_status moe_grouped_down(const moe_config* cfg, int64_t T, const void* h, const void* w_down,
-                            const void* h_shared, const void* ws_down,
+                            const void* h_shared, const void* ws_down, const moe_mx_scales* mx,
                             const int32_t* expert_offsets, const int32_t* sorted_rows,
                             const float* topk_w, float* acc, void* y_perm, void* ws,
                             size_t ws_bytes, moe_stream_t stream) {
@@ -380,10 +422,11 @@ moe_status moe_grouped_down(const moe_config* cfg, int64_t T, const void* h, con
   if (!y_perm && !topk_w) return MOE_ERR_INVALID_ARG;
   if (d.S && !h_shared) return MOE_ERR_INVALID_ARG;
   if (d.S && !d.packed && !ws_down) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_mx(d, mx, false, true));
   (void)ws;
   (void)ws_bytes;
-  return do_down(cfg, d, h, w_down, h_shared, ws_down, expert_offsets, sorted_rows, topk_w, acc,
-                 y_perm, (hipStream_t)stream);
+  return do_down(cfg, d, h, w_down, h_shared, ws_down, mx, expert_offsets, sorted_rows, topk_w,
+                 acc, y_perm, (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc, const void* y_perm,
@@ -401,7 +444,7 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc, const
 moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
                              const float* w_router, const float* expert_bias, const void* w_gate,
                              const void* w_up, const void* w_down, const void* ws_gate,
-                             const void* ws_up, const void* ws_down,
+                             const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
                              const float* router_logits_in, float* router_logits_out,
                              int32_t* topk_idx_out, float* topk_w_out, void* out,
                              int32_t deterministic, void* ws, size_t ws_bytes,
@@ -412,12 +455,13 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   if (!out) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_layer_args(d, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                            router_logits_in, deterministic));
+  MOE_TRY(check_mx(d, mx, true, true));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   hipStream_t st = (hipStream_t)stream;
   Ws w = carve(d, ws);
   LayerOut lo;
   MOE_TRY(run_layer(cfg, d, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
-                    ws_down, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
+                    ws_down, mx, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
                     deterministic, w, st, &lo));
   return hip_ok(launch_combine(w.acc, lo.y_perm, w.row_pos, lo.topk_w, out, (int)T, d.H, d.k,
                                d.dtype, st));
@@ -462,7 +506,8 @@ moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm,
                              const void* h, const float* pre_norm_w, const float* post_norm_w,
                              const float* w_router, const float* expert_bias, const void* w_gate,
                              const void* w_up, const void* w_down, const void* ws_gate,
-                             const void* ws_up, const void* ws_down, float* router_logits_out,
+                             const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
+                             float* router_logits_out,
                              int32_t* topk_idx_out, float* topk_w_out, void* out,
                              int32_t deterministic, void* ws, size_t ws_bytes,
                              moe_stream_t stream) {
@@ -473,6 +518,7 @@ moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm,
   if (!pre_norm_w || !post_norm_w || !out) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_layer_args(d, h, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                            nullptr, deterministic));
+  MOE_TRY(check_mx(d, mx, true, true));
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < block_ws_bytes(d)) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
@@ -482,8 +528,8 @@ moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm,
                                 d.dtype, st)));
   LayerOut lo;
   MOE_TRY(run_layer(cfg, d, xn, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
-                    ws_down, nullptr, router_logits_out, topk_idx_out, topk_w_out, deterministic,
-                    w, st, &lo));
+                    ws_down, mx, nullptr, router_logits_out, topk_idx_out, topk_w_out,
+                    deterministic, w, st, &lo));
   return hip_ok(launch_combine_norm(w.acc, lo.y_perm, w.row_pos, lo.topk_w, post_norm_w,
                                     norm->add_one, norm->rms_norm_eps, h, out, (int)T, d.H, d.k,
                                     d.dtype, st));
@@ -500,6 +546,6 @@ const char* moe_status_string(moe_status s) {
   return "unknown moe_status";
 }
 
-const char* moe_build_info(void) { return "libmoe 0.1 gfx950 (bf16/fp32 MFMA)"; }
+const char* moe_build_info(void) { return "libmoe 0.1 gfx950 (bf16/fp32 MFMA, MXFP8 weights)"; }
 
 }  // extern "C"

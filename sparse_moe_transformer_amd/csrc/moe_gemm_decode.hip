@@ -21,6 +21,17 @@
 // element is outside the tile, so each wave issues a fixed number of vector
 // memory operations per tile and the load-counter waits of a tile's first
 // steps can let the previous epilogue's stores stay in flight.
+//
+// MXFP8 expert weights (OCP MX: E4M3 codes, one E8M0 scale per 32 inputs,
+// scales block-major [K/32, N]; the MXFP8 export of mlxcel #763
+// "Validation"): a weight row holds 64 bytes per K-step, so the weight part
+// of a stage is 16 KiB, and the step's two scale bytes of each row ride in
+// the stage's spare LDS. Within a step the K order is permuted, the same way
+// for both operands: lane half q takes inputs 32q .. 32q+31, sub-step s the
+// eight at 32q + 8s, so a lane reads two 16-byte weight chunks and one scale
+// per row and step. Codes become bf16 with the scaled conversion
+// (v_cvt_scalef32_pk_bf16_fp8: exact for these values, the scale's exponent
+// taken as the E8M0 value) and the bf16 MFMAs run unchanged.
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
@@ -35,7 +46,9 @@ constexpr int NCH = 8;         // 16-byte chunks per LDS row per K-step
 constexpr int KSB = NCH * 16;  // bytes per row per K-step
 constexpr int NTHR = 256;
 constexpr int NST = 4;         // LDS stages
-constexpr int LOADS = 9;       // per thread per stage: 1 activation + 8 weight
+constexpr int LOADS_BF16 = 9;  // per thread per stage: 1 activation + 8 weight
+constexpr int LOADS_FP8 = 6;   // 1 activation + 4 weight + 1 scale
+constexpr int FP8_SCALES = 1024;  // u32x4 index of the scale bytes in an MXFP8 weight stage
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_WG_TILES = 128;
 constexpr int EPI_GU = 16;     // vector memory ops of a gate/up epilogue (per thread)
@@ -61,6 +74,12 @@ __device__ __forceinline__ int b_row(int j) {
   return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3);
 }
 __device__ __forceinline__ int lane_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
+// MXFP8 weight rows: 4 chunks of 16 B per step, chunk c of row r at c ^ swz4(r)
+// (rows r .. r+15 then spread a chunk over every bank)
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int b_row_fp8(int j) {
+  return 64 * (threadIdx.x >> 6) + 16 * j + ((threadIdx.x & 63) >> 2);
+}
 
 // Direct global->LDS loads (global_load_lds_dword / _dwordx4: each lane's
 // bytes land at LDS address m0 + lane * size), issued from inline assembly so
@@ -100,8 +119,11 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t voff, const void
 struct DTile {
   const char* abase;  // activations (x, h or h_shared)
   const char* bbase;  // this wave's weight matrix (gate or up rows for gate/up)
+  const char* sbase;  // MXFP8: this wave's scale matrix (block-major)
   uint32_t aoff;      // this lane's activation row + chunk, bytes from abase
   uint32_t boff[8];   // this lane's weight rows + chunks, bytes from bbase
+  uint32_t soff;      // MXFP8: this lane's 4 scale bytes of the step's first block
+  int sstep;          // MXFP8: scale bytes per K-step (two blocks)
   int nk;             // K-steps (a multiple of 4)
   int kseg;           // weight K segment length in bytes (K-split of shared down)
   int bstride;        // bytes between weight K segments (0: one segment)
@@ -112,19 +134,29 @@ struct DTile {
 // K length is a multiple of four steps (the host checks), so there are no
 // padding steps and no branch here: a branch would merge two load states
 // and make the compiler wait for every load before the next LDS read.
+template <bool FP8>
 __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, u32x4_t* lb) {
   const int w = threadIdx.x >> 6;
-  const long kb = (long)j * KSB;
-  long bk = kb;
+  const long kb = (long)j * KSB;                 // activation bytes per step
+  const long wb = FP8 ? (long)j * (KSB / 2) : kb;  // weight bytes per step
+  long bk = wb;
   if (t.bstride) {
-    const long seg = kb / t.kseg;
-    bk = seg * t.bstride + (kb - seg * t.kseg);
+    const long seg = wb / t.kseg;
+    bk = seg * t.bstride + (wb - seg * t.kseg);
   }
   const char* ab = t.abase + kb;
   const char* bb = t.bbase + bk;
   dma16(ab, t.aoff, la + 8 * w * NCH);
+  if (FP8) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
+    for (int q = 0; q < 4; ++q) dma16(bb, t.boff[q], lb + (64 * w + 16 * q) * 4);
+    // wave w: lanes 0..31 the scales of rows 64w .. 64w+63 (block 0, then
+    // block 1), lanes 32..63 the same bytes again into the slot's unused half
+    dma4(t.sbase + (long)j * t.sstep, t.soff, reinterpret_cast<const char*>(lb + FP8_SCALES) + 256 * w);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
+  }
 }
 
 // First weight row (within the 256-row tile) of block nb (0..1) of wave w.
@@ -136,11 +168,54 @@ __device__ __forceinline__ int wrow(int w, int nb) {
 
 typedef floatx16_t Acc2[2];
 
-// One K-step (4 sub-steps of K = 16): lane l reads row l%32, chunk 2s + l/32.
-template <int KIND>
+// Eight E4M3 codes (two dwords) -> eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// E8M0 byte -> a float whose exponent field is that byte (the conversion
+// reads only the exponent); byte 0 becomes the subnormal 2^-127 exactly.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
+}
+
+// One K-step (4 sub-steps of K = 16).
+//   bf16 weights: lane l reads row l%32, chunk 2s + l/32.
+//   MXFP8 weights: lane l takes inputs 32q + 8s .. +7 (q = l/32): activation
+//   chunk 4q + s; weight bytes of chunks 2q, 2q+1 and the scale of block q.
+template <int KIND, bool FP8>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 5, r = lane & 31;
+  if (FP8) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + FP8_SCALES);
+    u32x4_t wv[2][2];
+    float scale[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = wrow<KIND>(w, nb) + r;
+      wv[nb][0] = lb[row * 4 + ((2 * q) ^ swz4(row))];
+      wv[nb][1] = lb[row * 4 + ((2 * q + 1) ^ swz4(row))];
+      scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * q + (row & 63)]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, la[r * NCH + ((4 * q + s) ^ swz(r))]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const u32x4_t& c = wv[nb][s >> 1];
+        const bf16x8_t fb = (s & 1) ? fp8x8_to_bf16(c.z, c.w, scale[nb])
+                                    : fp8x8_to_bf16(c.x, c.y, scale[nb]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[nb], 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, la[r * NCH + ((2 * s + q) ^ swz(r))]);
@@ -205,10 +280,17 @@ __device__ __forceinline__ int token_of(const GemmArgs& g, int4 p, const int* ro
   return shared ? row0 + R : div_k(rows[R], g.k, g.kmagic);
 }
 
+// The scale bytes this lane loads for MXFP8 tile rows 64w .. 64w+63 of
+// the stage: lanes 0..31 cover (block l/16, four rows from 4 * (l%16)),
+// lanes 32..63 repeat them. col(tr) maps a tile row to its matrix column.
+__device__ __forceinline__ int scale_lane_row() { return 64 * (threadIdx.x >> 6) + 4 * (threadIdx.x & 15); }
+__device__ __forceinline__ int scale_lane_block() { return (threadIdx.x >> 4) & 1; }
+
 // tok: gate/up only, the token of this lane's activation row (token_of).
-template <int KIND>
+template <int KIND, bool FP8>
 __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DTile& t) {
   constexpr int EPC = 8;
+  constexpr uint32_t WES = FP8 ? 1u : 2u;  // weight element size
   const int H = g.H;
   t.row0 = p.x;
   t.nrows = p.y & 0xFFFF;
@@ -225,15 +307,34 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     // waves 0, 1 load gate rows (weight rows 0..127), waves 2, 3 the up rows
     const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? g.ws0 : g.w0)
                                                     : (t.shared ? g.ws1 : g.w1));
-    t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * H * 2);
+    t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * H * WES);
+    if (FP8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int br = b_row(j);
-      const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
-      t.boff[j] = (n * (uint32_t)H + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+      for (int j = 0; j < 4; ++j) {
+        const int br = b_row_fp8(j);
+        const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
+        t.boff[j] = n * (uint32_t)H + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
+      }
+      // scales [., H/32, N_s] per matrix; the shared experts are S matrices
+      // of width Is one after another (one, slot E, when packed), so a
+      // shared column n is column n - s*Is of matrix s = n / Is
+      const int ns = t.shared ? g.Is : g.I;
+      const uint8_t* sm = w < 2 ? (t.shared ? g.sws0 : g.sw0) : (t.shared ? g.sws1 : g.sw1);
+      const int n = min(t.n0 + (scale_lane_row() & 127), t.N - 4);
+      const int se = t.shared ? n / ns : 0;
+      t.sbase = reinterpret_cast<const char*>(sm) + (t.shared ? 0 : (size_t)t.e * (H / 32) * ns);
+      t.soff = (uint32_t)((size_t)se * (H / 32) * ns + (n - se * ns) + (size_t)scale_lane_block() * ns);
+      t.sstep = 2 * ns;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int br = b_row(j);
+        const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
+        t.boff[j] = (n * (uint32_t)H + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+      }
     }
     t.nk = H / (NCH * EPC);
-    t.kseg = H * 2;
+    t.kseg = H * WES;
     t.bstride = 0;
   } else {
     // down: shared tiles read h_shared [T, S*Is] against the S shared down
@@ -244,20 +345,36 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     const int ldb = sh ? g.Is : g.I;
     t.abase = static_cast<const char*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
     t.bbase = sh ? static_cast<const char*>(g.ws0)
-                 : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I * 2;
+                 : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I * WES;
     t.n0 = nt * DBR;
     t.N = H;
     const uint32_t arow = (uint32_t)(t.row0 + min(row, t.nrows - 1));
     t.aoff = (arow * (uint32_t)Ks + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
+    if (FP8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int br = b_row(j);
-      const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
-      t.boff[j] = (n * (uint32_t)ldb + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+      for (int j = 0; j < 4; ++j) {
+        const int br = b_row_fp8(j);
+        const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
+        t.boff[j] = n * (uint32_t)ldb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
+      }
+      // scales [K/32, H]: the S shared matrices' blocks follow one another
+      // along K, so a shared tile's K-step j always reads blocks 2j, 2j+1
+      const uint8_t* sm = sh ? g.sws0 : g.sw0 + (size_t)t.e * (g.I / 32) * H;
+      const int n = min(t.n0 + scale_lane_row(), H - 4);
+      t.sbase = reinterpret_cast<const char*>(sm);
+      t.soff = (uint32_t)(n + scale_lane_block() * H);
+      t.sstep = 2 * H;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int br = b_row(j);
+        const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
+        t.boff[j] = (n * (uint32_t)ldb + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+      }
     }
     t.nk = Ks / (NCH * EPC);
-    t.kseg = ldb * 2;
-    t.bstride = sh && g.S > 1 ? H * g.Is * 2 : 0;
+    t.kseg = ldb * WES;
+    t.bstride = sh && g.S > 1 ? H * g.Is * WES : 0;
   }
 }
 
@@ -348,7 +465,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const DTile& cur, co
 // epilogue stores in a tile's first three steps, may still be in flight),
 // barrier, issue the loads of step j+3 into the stage freed at step j-1
 // (the next tile's first stages when j+3 passes the end), compute stage j.
-template <int KIND, bool ATOMIC>
+template <int KIND, bool ATOMIC, bool FP8>
 __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   DEC_LDS_STAGES
   __shared__ int offs[MAX_EXPERTS + 1];
@@ -376,6 +493,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   };
 
   constexpr int EPI = KIND == GATE_UP ? EPI_GU : EPI_DN;
+  constexpr int LOADS = FP8 ? LOADS_FP8 : LOADS_BF16;
   constexpr bool ROWS = KIND == GATE_UP || (KIND == DOWN_ROUTED && ATOMIC);
   if (ROWS) {
     gather_rows(g, place(0), rows_buf[0]);
@@ -387,17 +505,17 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     __syncthreads();
   }
   DTile cur, nxt;
-  make_tile<KIND>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
-  issue_stage(cur, 0, lds_a0, lds_b0);
-  issue_stage(cur, 1, lds_a1, lds_b1);
-  issue_stage(cur, 2, lds_a2, lds_b2);
+  make_tile<KIND, FP8>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
+  issue_stage<FP8>(cur, 0, lds_a0, lds_b0);
+  issue_stage<FP8>(cur, 1, lds_a1, lds_b1);
+  issue_stage<FP8>(cur, 2, lds_a2, lds_b2);
 
   bool first = true;
   for (int li = 0;; ++li) {
     const bool has_next = li + 1 < n_my;
     // the next tile (its row ids were gathered a tile ago), then the row ids
     // of the one after it
-    make_tile<KIND>(g, place(li + 1),
+    make_tile<KIND, FP8>(g, place(li + 1),
                     KIND == GATE_UP ? token_of(g, place(li + 1), rows_buf[(li + 1) % 3]) : 0, nxt);
     if (KIND == DOWN_ROUTED && ATOMIC && threadIdx.x < 64) {
       // this tile's rows: token and routing weight of each (the weights are
@@ -420,8 +538,8 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     if ((J) < 3 && !first) wait_vmcnt<2 * LOADS + EPI>();                            \
     else wait_vmcnt<2 * LOADS>();                                                    \
     __builtin_amdgcn_s_barrier();                                                    \
-    issue_stage(TL, JL, NA, NB);                                                     \
-    compute_stage<KIND>(LA, LB, acc);                                                \
+    issue_stage<FP8>(TL, JL, NA, NB);                                                \
+    compute_stage<KIND, FP8>(LA, LB, acc);                                           \
   }
     // steps j .. j+3 use stages 0..3 and load step j+3 .. j+6; the last four
     // steps of the tile load its last step and the next tile's first three
@@ -447,18 +565,21 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   __builtin_amdgcn_s_barrier();
 }
 
+template <bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_decode_kernel(GemmArgs g) {
-  decode_body<GATE_UP, false>(g);
+  decode_body<GATE_UP, false, FP8>(g);
 }
+template <bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_BOTH, false>(g);
+  decode_body<DOWN_BOTH, false, FP8>(g);
 }
+template <bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_SHARED, false>(g);
+  decode_body<DOWN_SHARED, false, FP8>(g);
 }
-template <bool ATOMIC>
+template <bool ATOMIC, bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_ROUTED, ATOMIC>(g);
+  decode_body<DOWN_ROUTED, ATOMIC, FP8>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,19 +620,27 @@ static hipError_t launch_decode(void (*kern)(GemmArgs), long n, const GemmArgs& 
   return hipGetLastError();
 }
 
+// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1).
 hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st) {
-  return launch_decode(moe_gate_up_decode_kernel,
-                       (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed, g, st);
+  const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
+  return g.fp8 ? launch_decode(moe_gate_up_decode_kernel<true>, n, g, st)
+               : launch_decode(moe_gate_up_decode_kernel<false>, n, g, st);
 }
 hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st) {
-  return launch_decode(moe_down_decode_kernel,
-                       (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed, g, st);
+  const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
+  return g.fp8 ? launch_decode(moe_down_decode_kernel<true>, n, g, st)
+               : launch_decode(moe_down_decode_kernel<false>, n, g, st);
 }
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st) {
-  return launch_decode(moe_down_shared_decode_kernel, (long)g.mt_shared * g.nt_shared, g, st);
+  const long n = (long)g.mt_shared * g.nt_shared;
+  return g.fp8 ? launch_decode(moe_down_shared_decode_kernel<true>, n, g, st)
+               : launch_decode(moe_down_shared_decode_kernel<false>, n, g, st);
 }
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st) {
   const long n = (long)g.mt_routed * g.nt_routed;
-  return atomic ? launch_decode(moe_down_routed_decode_kernel<true>, n, g, st)
-                : launch_decode(moe_down_routed_decode_kernel<false>, n, g, st);
+  if (g.fp8)
+    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true>, n, g, st)
+                  : launch_decode(moe_down_routed_decode_kernel<false, true>, n, g, st);
+  return atomic ? launch_decode(moe_down_routed_decode_kernel<true, false>, n, g, st)
+                : launch_decode(moe_down_routed_decode_kernel<false, false>, n, g, st);
 }

@@ -25,6 +25,14 @@ struct GemmArgs {
   int mt_routed, nt_routed, mt_shared, nt_shared;
   int gm_routed, gm_shared;  // m-slots per group of the tile order
   ActParams act;
+  // MXFP8 weights (fp8 != 0): E8M0 scales, block-major [K/32, N] per matrix,
+  // of the stacked gate (or down) and up weights and of the shared gate (or
+  // down) and up weights (the shared ones start at slot E when packed)
+  int fp8;
+  const uint8_t* sw0;
+  const uint8_t* sw1;
+  const uint8_t* sws0;
+  const uint8_t* sws1;
 };
 
 size_t gemm_lds_bytes(int E);

@@ -49,6 +49,8 @@ class Dev:
         self.ws_up = t(inp.ws_up, device)
         self.ws_down = t(inp.ws_down, device)
         self.ws = moe.alloc_workspace(self.keys, self.T, device)
+        self.mx = ({key: t(v, device) for key, v in inp.mx.items()} if inp.mx is not None
+                   else None)
 
     def forward(self, deterministic=0, logits_in=None, want_logits=True):
         import torch
@@ -61,7 +63,7 @@ class Dev:
         out = torch.empty(T * H, dtype=moe.torch_dtype(c), device=dev)
         moe.moe_layer_forward(c, T, self.x, self.w_router, self.expert_bias, self.w_gate,
                               self.w_up, self.w_down, self.ws_gate, self.ws_up, self.ws_down,
-                              logits_in, logits, idx, w, out, deterministic, self.ws)
+                              logits_in, logits, idx, w, out, deterministic, self.ws, mx=self.mx)
         torch.cuda.synchronize()
         res = dict(idx=idx.view(T, k).cpu().numpy(), w=w.view(T, k).cpu().numpy(),
                    out=out.view(T, H).float().cpu().numpy().astype(np.float64))

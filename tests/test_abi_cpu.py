@@ -62,13 +62,13 @@ def test_workspace_grows_with_tokens():
     assert all(s % 256 == 0 for s in sizes)
 
 
-def _raw_forward(cfg, T, ptr=0x1000, ws=0x100000, ws_bytes=1 << 40, x=True):
+def _raw_forward(cfg, T, ptr=0x1000, ws=0x100000, ws_bytes=1 << 40, x=True, mx=None):
     """moe_layer_forward with fake (never dereferenced) device addresses."""
     L = moe.lib()
     c = moe.make_config(cfg)
     p = ptr if x else None
     return L.moe_layer_forward(ctypes.byref(c), T, p, ptr, None, ptr, ptr, ptr, ptr, ptr, ptr,
-                               None, None, None, None, ptr, 0, ws, ws_bytes, None)
+                               mx, None, None, None, None, ptr, 0, ws, ws_bytes, None)
 
 
 def test_host_checks_run_before_any_launch():
@@ -91,7 +91,7 @@ def _raw_block(cfg, T, norm=None, H_ok=True, ptr=0x1000, ws=0x100000, ws_bytes=1
     c = moe.make_config(cfg)
     n = moe.make_norm_config(norm or {"eps": 1e-5, "add_one": 0})
     return L.moe_block_forward(ctypes.byref(c), ctypes.byref(n), T, ptr, ptr, ptr, ptr, None,
-                               ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, ptr, 0, ws,
+                               ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, None, ptr, 0, ws,
                                ws_bytes, None)
 
 
@@ -110,4 +110,26 @@ def test_block_workspace_adds_the_normalised_rows():
     for T in (1, 64, 4096):
         extra = moe.moe_block_workspace_size(c, T) - moe.moe_workspace_size(c, T)
         assert extra == -(-(T * 2048 * 2) // 256) * 256
+
+
+def _mx_cfg(**kw):
+    c = synth.layer_keys(synth.config("minimax_m3_decode_T64_mxfp8"))
+    c.update(kw)
+    return c
+
+
+def test_mxfp8_config_checks():
+    """MXFP8 weights need bf16 activations and K lengths the 32-row kernels
+    cover; the scales must be given."""
+    assert moe.moe_workspace_size(_mx_cfg(), 64) > 0
+    for bad, status in ((dict(weight_format=2), moe.MOE_ERR_INVALID_ARG),
+                        (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED),
+                        (dict(hidden_size=6208), moe.MOE_ERR_UNSUPPORTED)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_workspace_size(_mx_cfg(**bad), 64)
+        assert ei.value.status == status, bad
+    # missing scales: rejected on the host before any launch
+    assert _raw_forward(_mx_cfg(), 8) == moe.MOE_ERR_INVALID_ARG
+    m = moe.MoeMxScales(gate=0x2000, up=0x2000, down=None)
+    assert _raw_forward(_mx_cfg(), 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
 

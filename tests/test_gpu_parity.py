@@ -90,8 +90,9 @@ def run_stages(dev: Dev, deterministic=False):
     moe.moe_route(c, T, logits, dev.expert_bias, idx, w, counts)
     moe.moe_permute(c, T, idx, offs, sr, rp, dev.ws)
     moe.moe_grouped_gate_up_swiglu(c, T, dev.x, dev.w_gate, dev.w_up, dev.ws_gate, dev.ws_up,
-                                   offs, sr, h, hs, dev.ws)
-    moe.moe_grouped_down(c, T, h, dev.w_down, hs, dev.ws_down, offs, sr, w, acc, yp, dev.ws)
+                                   offs, sr, h, hs, dev.ws, mx=dev.mx)
+    moe.moe_grouped_down(c, T, h, dev.w_down, hs, dev.ws_down, offs, sr, w, acc, yp, dev.ws,
+                         mx=dev.mx)
     moe.moe_combine(c, T, acc, yp, rp, w, out)
     torch.cuda.synchronize()
     g = lambda t, *shape: t[: int(np.prod(shape))].view(*shape).float().cpu().numpy() \

@@ -55,6 +55,15 @@ def test_mxfp8_quantiser():
     rng = np.random.default_rng(0)
     w = (rng.standard_normal((48, 256)) * 0.02).astype(np.float32)
     w[3, 32:64] = 0.0                                   # an all-zero block
+    # blocks with scale 2^0 (maximum 448): every non-negative E4M3 value up to
+    # code 0x3E (subnormals included), then the midpoints between neighbours
+    # (exact ties: the even code wins) and values just off them
+    vals = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    w[7, :32] = np.concatenate([[448.0], vals[:31]])
+    w[7, 32:64] = np.concatenate([[448.0], vals[31:62]])
+    w[8, :32] = np.concatenate([[448.0], (vals[:31] + vals[1:32]) / 2])
+    w[8, 32:64] = np.concatenate([[448.0], np.nextafter((vals[:31] + vals[1:32]) / 2, 1)])
+    w[8, 64:96] = -w[8, :32]
     codes, sc = synth.quantize_mxfp8(w)
     assert codes.shape == w.shape and sc.shape == (8, 48) and sc.dtype == np.uint8
     amax = np.abs(w.astype(np.float64)).reshape(48, 8, 32).max(2)
@@ -62,7 +71,8 @@ def test_mxfp8_quantiser():
     assert np.array_equal(sc.T[nz].astype(np.int64), np.floor(np.log2(amax[nz])).astype(np.int64) - 8 + 127)
     v = w.astype(np.float64).reshape(48, 8, 32) / np.exp2(sc.T.astype(np.float64) - 127)[:, :, None]
     ref = torch.from_numpy(np.clip(v, -448, 448).reshape(48, 256)).to(torch.float8_e4m3fn)
-    assert np.array_equal(ref.view(torch.uint8).numpy() & 0x7F, codes & 0x7F)
+    assert np.array_equal(ref.view(torch.uint8).numpy(), codes)
+    assert np.array_equal(codes[7, 1:32], np.arange(31)) and np.all(codes[8, 1:32] % 2 == 0)
     assert np.all(codes[3, 32:64] & 0x7F == 0)
     cfg = synth.config("trinity_nano_decode_T32_mxfp8")
     a = synth.generate(cfg)

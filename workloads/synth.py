@@ -338,37 +338,32 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
 # ----------------------------------------------------------------------------
 # MXFP8 (OCP Microscaling v1.0: E4M3 elements, one E8M0 scale per 32 inputs)
 
-def _e4m3_nonneg() -> np.ndarray:
-    """The 127 finite non-negative E4M3 values, codes 0x00..0x7E in order
-    (exponent bias 7, 3 mantissa bits, subnormals below 2^-6)."""
-    c = np.arange(127)
-    ef, m = c >> 3, (c & 7).astype(np.float64)
-    return np.where(ef == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(ef - 7.0))
-
-
-_E4M3_NONNEG = _e4m3_nonneg()
-_E4M3_MID = (_E4M3_NONNEG[:-1] + _E4M3_NONNEG[1:]) / 2.0
-
-
 def quantize_mxfp8(w: np.ndarray):
     """float32 [N, K] -> (codes uint8 [N, K], scales uint8 [K/32, N]).
 
     Per block of 32 inputs of a row: scale 2^(floor(log2 amax) - 8) (8 is
-    E4M3's largest exponent), elements rounded to the nearest E4M3 value
-    (ties to the even code) after clamping to +-448."""
+    E4M3's largest exponent); each element, divided by the scale (exact) and
+    clamped to +-448, is rounded to the nearest E4M3 value, ties to the even
+    code: from 2^-6 up by rounding the float32 significand to 3 bits (the
+    carry moves into the exponent), below it to a multiple of 2^-9 (codes
+    0..8, where 8 is 2^-6)."""
     N, K = w.shape
-    blk = np.asarray(w, dtype=np.float64).reshape(N, K // 32, 32)
+    blk = np.ascontiguousarray(w, dtype=np.float32).reshape(N, K // 32, 32)
     amax = np.abs(blk).max(axis=2)
     _, ex = np.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
     ex = np.where(amax > 0, ex - 1, -119)        # floor(log2 amax); zero block: scale byte 0
     sbyte = np.clip(ex - 8 + 127, 0, 254).astype(np.uint8)
-    v = blk / np.exp2(sbyte.astype(np.float64) - 127.0)[:, :, None]
-    a = np.minimum(np.abs(v), 448.0)
-    i = np.searchsorted(_E4M3_MID, a, side="left")
-    tie = (i < _E4M3_MID.size) & (a == _E4M3_MID[np.minimum(i, _E4M3_MID.size - 1)]) & (i % 2 == 1)
-    i = i + tie
-    codes = (i | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8).reshape(N, K)
-    return codes, np.ascontiguousarray(sbyte.T)
+    v = blk * np.ldexp(np.float32(1.0), 127 - sbyte.astype(np.int32))[:, :, None]
+    a = np.minimum(np.abs(v), np.float32(448.0))
+    u = a.view(np.uint32)
+    # (u + 0x7FFFF + lsb) >> 20 is (exponent << 3 | mantissa) rounded to
+    # nearest even; minus (127 - 7) << 3 rebiases the exponent (wraps below
+    # 2^-6, where the subnormal branch is taken instead)
+    normal = ((u + np.uint32(0x7FFFF) + ((u >> 20) & np.uint32(1))) >> 20) - np.uint32(120 << 3)
+    sub = np.rint(a * np.float32(512.0)).astype(np.uint32)
+    code = np.where(a >= np.float32(2.0 ** -6), normal, sub)
+    code |= (v.view(np.uint32) >> 24) & np.uint32(0x80)
+    return code.astype(np.uint8).reshape(N, K), np.ascontiguousarray(sbyte.T)
 
 
 def norm_weights(cfg: dict) -> dict:
