@@ -6,7 +6,8 @@
 // rows per expert the work is a stream of expert weights, so the tile is 32
 // activation rows x 256 weight rows and the LDS holds four stages of 36 KiB
 // (32 + 256 rows x 128 B of K): three K-steps of weights are in flight while
-// one is computed, against two with the 128-row tile's 48 KiB stages.
+// one is computed, against two with the 128-row tile's 48 KiB stages
+// (MXFP8 stages are 21 KiB: six of them when the K lengths allow).
 //
 // Four waves each own the 32 rows x 64 weight rows: for gate/up, 32 gate and
 // the 32 up rows of the same columns (the activation is applied in
@@ -14,9 +15,9 @@
 // sub-step.
 //
 // Persistent schedule and tile order as in moe_gemm.hip. Every K length is
-// a multiple of four K-steps (256 elements; the host falls back to the
-// 128-row kernel otherwise); the last three steps of a tile load the next
-// tile's first three stages. Every store of an epilogue is
+// a multiple of the stage count in K-steps (four steps, 256 elements, or six
+// for the six-stage MXFP8 kernels; the host checks); the last NST-1 steps of
+// a tile load the next tile's first NST-1 stages. Every store of an epilogue is
 // a buffer store whose offset is pushed past the buffer's range when the
 // element is outside the tile, so each wave issues a fixed number of vector
 // memory operations per tile and the load-counter waits of a tile's first
@@ -45,7 +46,9 @@ constexpr int DBR = 256;       // weight rows per tile
 constexpr int NCH = 8;         // 16-byte chunks per LDS row per K-step
 constexpr int KSB = NCH * 16;  // bytes per row per K-step
 constexpr int NTHR = 256;
-constexpr int NST = 4;         // LDS stages
+// LDS stages: four (three K-steps of weights in flight while one is
+// computed); MXFP8 stages are smaller, so six when every K length of the
+// launch is a multiple of six steps.
 constexpr int LOADS_BF16 = 9;  // per thread per stage: 1 activation + 8 weight
 constexpr int LOADS_FP8 = 6;   // 1 activation + 4 weight + 1 scale
 constexpr int FP8_SCALES = 1024;  // u32x4 index of the scale bytes in an MXFP8 weight stage
@@ -54,17 +57,13 @@ constexpr int MAX_WG_TILES = 128;
 constexpr int EPI_GU = 16;     // vector memory ops of a gate/up epilogue (per thread)
 constexpr int EPI_DN = 32;     // ... of a down epilogue
 
-#define DEC_LDS_STAGES                                \
-  __shared__ __align__(16) u32x4_t lds_a0[DBM * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_a1[DBM * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_a2[DBM * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_a3[DBM * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_b0[DBR * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_b1[DBR * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_b2[DBR * NCH]; \
-  __shared__ __align__(16) u32x4_t lds_b3[DBR * NCH];
-static_assert(NST == 4, "DEC_LDS_STAGES and the main loop's rotation name four stages");
-static_assert(NST * (DBM + DBR) * KSB <= 160 * 1024, "LDS stages exceed one compute unit's LDS");
+// A stage: DBM activation rows, then the weight rows (bf16: DBR x 128 B;
+// MXFP8: DBR x 64 B and the step's scale bytes, 1 KiB), in 16-byte units.
+constexpr int STAGE_A = DBM * NCH;
+template <bool FP8>
+constexpr int stage_u4() { return STAGE_A + (FP8 ? 1024 + 64 : DBR * NCH); }
+static_assert(4 * stage_u4<false>() * 16 <= 144 * 1024, "bf16 stages exceed their LDS budget");
+static_assert(6 * stage_u4<true>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
 
 // Wave w loads activation rows 8w .. 8w+7 (one instruction) and weight rows
 // 64w + 8j .. +7 (instruction j < 8); the lane's row is that base + lane/8
@@ -465,9 +464,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const DTile& cur, co
 // epilogue stores in a tile's first three steps, may still be in flight),
 // barrier, issue the loads of step j+3 into the stage freed at step j-1
 // (the next tile's first stages when j+3 passes the end), compute stage j.
-template <int KIND, bool ATOMIC, bool FP8>
+template <int KIND, bool ATOMIC, bool FP8, int NST>
 __device__ __forceinline__ void decode_body(const GemmArgs& g) {
-  DEC_LDS_STAGES
+  constexpr int STAGE = stage_u4<FP8>();
+  __shared__ __align__(16) u32x4_t lds_st[NST][STAGE];
   __shared__ int offs[MAX_EXPERTS + 1];
   __shared__ int cum[MAX_EXPERTS + 1];
   __shared__ int4 places[MAX_WG_TILES];
@@ -506,9 +506,8 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   }
   DTile cur, nxt;
   make_tile<KIND, FP8>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
-  issue_stage<FP8>(cur, 0, lds_a0, lds_b0);
-  issue_stage<FP8>(cur, 1, lds_a1, lds_b1);
-  issue_stage<FP8>(cur, 2, lds_a2, lds_b2);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue_stage<FP8>(cur, st, lds_st[st], lds_st[st] + STAGE_A);
 
   bool first = true;
   for (int li = 0;; ++li) {
@@ -533,27 +532,25 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[nb][v] = 0.f;
 
-#define DEC_STEP(J, TL, JL, LA, LB, NA, NB)                                        \
-  {                                                                                  \
-    if ((J) < 3 && !first) wait_vmcnt<2 * LOADS + EPI>();                            \
-    else wait_vmcnt<2 * LOADS>();                                                    \
-    __builtin_amdgcn_s_barrier();                                                    \
-    issue_stage<FP8>(TL, JL, NA, NB);                                                \
-    compute_stage<KIND, FP8>(LA, LB, acc);                                           \
+#define DEC_STEP(J, TL, JL, SC, SN)                                                     \
+  {                                                                                    \
+    if ((J) < NST - 1 && !first) wait_vmcnt<(NST - 2) * LOADS + EPI>();                \
+    else wait_vmcnt<(NST - 2) * LOADS>();                                              \
+    __builtin_amdgcn_s_barrier();                                                      \
+    issue_stage<FP8>(TL, JL, lds_st[SN], lds_st[SN] + STAGE_A);                        \
+    compute_stage<KIND, FP8>(lds_st[SC], lds_st[SC] + STAGE_A, acc);                   \
   }
-    // steps j .. j+3 use stages 0..3 and load step j+3 .. j+6; the last four
-    // steps of the tile load its last step and the next tile's first three
+    // a group of NST steps uses stages 0 .. NST-1 and loads NST-1 steps ahead;
+    // the tile's last group loads its last step and the next tile's first
+    // NST-1 steps (nk is a multiple of NST)
     int j = 0;
-    for (; j + 4 < nk4; j += 4) {
-      DEC_STEP(j, cur, j + 3, lds_a0, lds_b0, lds_a3, lds_b3)
-      DEC_STEP(j + 1, cur, j + 4, lds_a1, lds_b1, lds_a0, lds_b0)
-      DEC_STEP(j + 2, cur, j + 5, lds_a2, lds_b2, lds_a1, lds_b1)
-      DEC_STEP(j + 3, cur, j + 6, lds_a3, lds_b3, lds_a2, lds_b2)
+    for (; j + NST < nk4; j += NST) {
+#pragma unroll
+      for (int u = 0; u < NST; ++u) DEC_STEP(j + u, cur, j + u + NST - 1, u, (u + NST - 1) % NST)
     }
-    DEC_STEP(j, cur, j + 3, lds_a0, lds_b0, lds_a3, lds_b3)
-    DEC_STEP(j + 1, nxt, 0, lds_a1, lds_b1, lds_a0, lds_b0)
-    DEC_STEP(j + 2, nxt, 1, lds_a2, lds_b2, lds_a1, lds_b1)
-    DEC_STEP(j + 3, nxt, 2, lds_a3, lds_b3, lds_a2, lds_b2)
+    DEC_STEP(j, cur, j + NST - 1, 0, NST - 1)
+#pragma unroll
+    for (int u = 1; u < NST; ++u) DEC_STEP(j + u, nxt, u - 1, u, u - 1)
 #undef DEC_STEP
     epilogue<KIND, ATOMIC>(g, cur, acc, ep_tok[li & 1], ep_w[li & 1]);
     if (!has_next) break;
@@ -565,21 +562,21 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   __builtin_amdgcn_s_barrier();
 }
 
-template <bool FP8>
+template <bool FP8, int NST>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_decode_kernel(GemmArgs g) {
-  decode_body<GATE_UP, false, FP8>(g);
+  decode_body<GATE_UP, false, FP8, NST>(g);
 }
-template <bool FP8>
+template <bool FP8, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_BOTH, false, FP8>(g);
+  decode_body<DOWN_BOTH, false, FP8, NST>(g);
 }
-template <bool FP8>
+template <bool FP8, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_SHARED, false, FP8>(g);
+  decode_body<DOWN_SHARED, false, FP8, NST>(g);
 }
-template <bool ATOMIC, bool FP8>
+template <bool ATOMIC, bool FP8, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_ROUTED, ATOMIC, FP8>(g);
+  decode_body<DOWN_ROUTED, ATOMIC, FP8, NST>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,27 +617,37 @@ static hipError_t launch_decode(void (*kern)(GemmArgs), long n, const GemmArgs& 
   return hipGetLastError();
 }
 
-// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1).
+// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1),
+// with six stages when every K length the launch streams is a multiple of
+// six 64-element steps.
+static bool six(int K) { return (K / 64) % 6 == 0; }
+
 hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
-  return g.fp8 ? launch_decode(moe_gate_up_decode_kernel<true>, n, g, st)
-               : launch_decode(moe_gate_up_decode_kernel<false>, n, g, st);
+  if (!g.fp8) return launch_decode(moe_gate_up_decode_kernel<false, 4>, n, g, st);
+  return six(g.H) ? launch_decode(moe_gate_up_decode_kernel<true, 6>, n, g, st)
+                  : launch_decode(moe_gate_up_decode_kernel<true, 4>, n, g, st);
 }
 hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
-  return g.fp8 ? launch_decode(moe_down_decode_kernel<true>, n, g, st)
-               : launch_decode(moe_down_decode_kernel<false>, n, g, st);
+  if (!g.fp8) return launch_decode(moe_down_decode_kernel<false, 4>, n, g, st);
+  return six(g.I) && six(g.S * g.Is) ? launch_decode(moe_down_decode_kernel<true, 6>, n, g, st)
+                                     : launch_decode(moe_down_decode_kernel<true, 4>, n, g, st);
 }
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared;
-  return g.fp8 ? launch_decode(moe_down_shared_decode_kernel<true>, n, g, st)
-               : launch_decode(moe_down_shared_decode_kernel<false>, n, g, st);
+  if (!g.fp8) return launch_decode(moe_down_shared_decode_kernel<false, 4>, n, g, st);
+  return six(g.S * g.Is) ? launch_decode(moe_down_shared_decode_kernel<true, 6>, n, g, st)
+                         : launch_decode(moe_down_shared_decode_kernel<true, 4>, n, g, st);
 }
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st) {
   const long n = (long)g.mt_routed * g.nt_routed;
-  if (g.fp8)
-    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true>, n, g, st)
-                  : launch_decode(moe_down_routed_decode_kernel<false, true>, n, g, st);
-  return atomic ? launch_decode(moe_down_routed_decode_kernel<true, false>, n, g, st)
-                : launch_decode(moe_down_routed_decode_kernel<false, false>, n, g, st);
+  if (!g.fp8)
+    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, false, 4>, n, g, st)
+                  : launch_decode(moe_down_routed_decode_kernel<false, false, 4>, n, g, st);
+  if (six(g.I))
+    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true, 6>, n, g, st)
+                  : launch_decode(moe_down_routed_decode_kernel<false, true, 6>, n, g, st);
+  return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true, 4>, n, g, st)
+                : launch_decode(moe_down_routed_decode_kernel<false, true, 4>, n, g, st);
 }
