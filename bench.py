@@ -64,14 +64,12 @@ GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_decode.hip", "moe_gemm_common.h", "moe
 
 def gate_up_kernel(cfg: dict, T: int) -> str:
     """Name of the grouped gate/up kernel the library runs for this workload
-    (the 32-row tile kernel for MXFP8 weights and for decode-sized bf16
-    batches, else the 128-row one)."""
+    (the 32-row tile kernel for decode-sized batches, else the 128-row one)."""
     H, I, k, E = cfg["hidden_size"], cfg["moe_intermediate_size"], cfg["num_experts_per_tok"], \
         cfg["num_experts"]
     S, Is = cfg["num_shared_experts"], cfg["shared_intermediate_size"] or I
     fits = H % 256 == 0 and I % 256 == 0 and (S * Is) % 256 == 0
-    dec = cfg.get("weight_format") == "mxfp8" or (
-        cfg["dtype"] == "bf16" and fits and T * k <= 32 * E)
+    dec = cfg["dtype"] == "bf16" and fits and T * k <= 32 * E
     return "moe_gate_up_decode_kernel" if dec else "moe_gate_up_kernel"
 
 

@@ -82,8 +82,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *                      (2^(e-127)); w = e4m3(code) * 2^(e-127). The code
  *                      tensors keep the weights' shapes and layout; the
  *                      scales are passed in moe_mx_scales. Needs dtype bf16
- *                      (activations stay bf16, accumulation fp32), and H, I
- *                      and S*I_s multiples of 256 (else MOE_ERR_UNSUPPORTED). */
+ *                      (activations stay bf16, accumulation fp32; else
+ *                      MOE_ERR_UNSUPPORTED). */
 typedef enum { MOE_WEIGHTS_DTYPE = 0, MOE_WEIGHTS_MXFP8 = 1 } moe_weight_format;
 
 /* E8M0 scales of MXFP8 expert weights, block-major: for an [N, K] weight

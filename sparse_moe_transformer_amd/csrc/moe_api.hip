@@ -63,9 +63,8 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
   d->es = c->dtype == MOE_BF16 ? 2 : 4;
   d->fp8 = c->weight_format == MOE_WEIGHTS_MXFP8;
   d->wes = d->fp8 ? 1 : d->es;
-  // MXFP8 weights run on the 32-row tile kernels (bf16 activations)
-  if (d->fp8 && (c->dtype != MOE_BF16 || !gemm_decode_fits(T, d->H, d->I, d->k, d->S, d->Is)))
-    return MOE_ERR_UNSUPPORTED;
+  // MXFP8 weights take bf16 activations
+  if (d->fp8 && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -177,7 +176,6 @@ const uint8_t* scale_slot(const uint8_t* stacked, const Dims& d, size_t per_expe
 // K-steps in flight per compute unit. MOE_GEMM_TILE=32 or =128 forces one
 // kernel (a testing knob; 32 still needs bf16 and gemm_decode_fits).
 bool use_decode(const Dims& d) {
-  if (d.fp8) return true;  // the only kernels with MXFP8 weights (check_cfg checked the fit)
   if (d.dtype != MOE_BF16 || !gemm_decode_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
   if (const char* e = std::getenv("MOE_GEMM_TILE")) {
     if (std::strcmp(e, "128") == 0) return false;

@@ -33,6 +33,18 @@
 // bank conflicts for the 32x32 fragment reads (measured on gfx950). Rows past
 // the end of a tile (activation rows beyond the segment, weight rows beyond
 // N) load a valid clamped row; their results are never stored.
+//
+// MXFP8 expert weights (OCP MX: E4M3 codes, one E8M0 scale per 32 inputs,
+// scales block-major [K/32, N]; the MXFP8 export of mlxcel #763
+// "Validation"), with bf16 activations: a weight row holds 64 bytes per
+// K-step (4 chunks, chunk c of row r at c ^ ((r >> 2) & 3)) and the step's
+// two scale bytes of each row sit after the weight rows of the stage. Inside
+// a step the K order is permuted, the same for both operands: lane half q
+// takes inputs 32q .. 32q+31, sub-step s the eight at 32q + 8s. A lane reads
+// two 16-byte weight chunks and one scale per weight block and step, turns
+// the codes into bf16 with the scaled conversion (exact for these values)
+// and runs the bf16 MFMAs; per step the LDS moves a third less than with
+// bf16 weights (stage writes 33 KiB, fragment reads 64 KiB).
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
@@ -47,7 +59,9 @@ constexpr int NCH = 8;     // 16-byte chunks per LDS row per K-step
 constexpr int KSB = NCH * 16;  // bytes per row per K-step
 constexpr int NTHR = 256;
 constexpr int MAX_EXPERTS = 1024;
-constexpr int LOADS_PER_STAGE = 12;  // per thread: 4 activation + 8 weight
+constexpr int LOADS_BF16 = 12;  // per thread: 4 activation + 8 weight
+constexpr int LOADS_FP8 = 9;    // 4 activation + 4 weight + 1 scale
+constexpr int FP8_SCALES = 1024;  // u32x4 index of the scale bytes in an MXFP8 weight stage
 
 template <typename T>
 struct Elem;
@@ -74,11 +88,24 @@ struct Elem<float> {
 __device__ __forceinline__ int a_row(int j) { return (threadIdx.x >> 6) * 32 + 8 * j + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int b_row(int j) { return (threadIdx.x >> 6) * 64 + 8 * j + ((threadIdx.x & 63) >> 3); }
 __device__ __forceinline__ int lane_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
+// MXFP8 weight rows: instruction j of wave w fills rows 64w+16j .. +15, four
+// lanes per row; chunk c of row r is stored at c ^ swz4(r)
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int b_row_fp8(int j) {
+  return (threadIdx.x >> 6) * 64 + 16 * j + ((threadIdx.x & 63) >> 2);
+}
+// the scale bytes a lane loads: lanes 0..31 of wave w take 4 rows from
+// 64w + 4 (l % 16) of block l / 16 (lanes 32..63 repeat them into the unused
+// half of the wave's 256-byte slot)
+__device__ __forceinline__ int scale_lane_row() { return 64 * (threadIdx.x >> 6) + 4 * (threadIdx.x & 15); }
+__device__ __forceinline__ int scale_lane_block() { return (threadIdx.x >> 4) & 1; }
 
 // One tile: where its rows and weights are and how many K-steps it has.
 struct Tile {
   const char* a[4];  // activation row pointers (+ lane chunk offset), bytes
-  const char* b[8];  // weight row pointers (+ lane chunk offset), bytes
+  const char* b[8];  // weight row pointers (+ lane chunk offset), bytes (MXFP8: 4)
+  const char* s;     // MXFP8: this lane's scale bytes of the first K-step
+  int sstep;         // MXFP8: scale bytes per K-step
   int nk;            // real K-steps
   int nk3;           // steps padded to a multiple of 3
   int kseg;          // weight K segment length in bytes (K-split of shared down)
@@ -86,21 +113,49 @@ struct Tile {
   int shared, e, row0, nrows, n0, N;
 };
 
-// Load the 12 chunks of this lane for step j of tile t into LDS stage (la, lb)
-// (the zero line for padding steps j >= nk).
+// Load this lane's chunks for step j of tile t into LDS stage (la, lb) (the
+// zero line for padding steps j >= nk: zero codes and zero activations add
+// exactly zero).
+template <bool FP8>
 __device__ __forceinline__ void issue_stage(const Tile& t, int j, u32x4_t* la, u32x4_t* lb) {
   const bool real = j < t.nk;
   const int kb = j * KSB;
-  const int seg = kb / t.kseg;
-  const long boff = (long)seg * t.bstride_kb * 1024 + (kb - seg * t.kseg);
+  const int kw = FP8 ? j * (KSB / 2) : kb;  // weight bytes per step
+  const int seg = kw / t.kseg;
+  const long boff = (long)seg * t.bstride_kb * 1024 + (kw - seg * t.kseg);
   const char* z = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 7) * 16;
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_global_load_lds(real ? t.a[q] + kb : z, la + (w * 4 + q) * 64, 16, 0, 0);
+  if (FP8) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + (w * 8 + q) * 64, 16, 0, 0);
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 256 + q * 64, 16, 0, 0);
+    const char* zs = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 31) * 4;
+    __builtin_amdgcn_global_load_lds(real ? t.s + (long)j * t.sstep : zs,
+                                     lb + FP8_SCALES + w * 16, 4, 0, 0);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + (w * 8 + q) * 64, 16, 0, 0);
+  }
+}
+
+// Eight E4M3 codes (two dwords) -> eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// E8M0 byte -> a float whose exponent field is that byte (the conversion
+// reads only the exponent); byte 0 becomes the subnormal 2^-127 exactly.
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
 }
 
 // First weight row (within the 256-row tile) of block nb (0..3) of wave wn.
@@ -114,13 +169,45 @@ typedef floatx16_t Acc[2][4];
 
 // One K-step from one LDS stage.
 // bf16: 4 sub-steps of K=16; lane l reads row l%32, chunk 2*s + l/32.
-template <typename T, int KIND>
+// MXFP8 weights: lane l takes inputs 32q + 8s .. +7 (q = l/32): activation
+// chunk 4q + s, weight chunks 2q, 2q+1 and the scale of block q.
+template <typename T, int KIND, bool FP8>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 5, r = lane & 31;
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (FP8) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + FP8_SCALES);
+    u32x4_t wv[4][2];
+    float scale[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int row = wrow<KIND>(wn, nb) + r;
+      wv[nb][0] = lb[row * 4 + ((2 * q) ^ swz4(row))];
+      wv[nb][1] = lb[row * 4 + ((2 * q + 1) ^ swz4(row))];
+      scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * q + (row & 63)]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t fa[2], fb[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + r;
+        fa[mb] = __builtin_bit_cast(bf16x8_t, la[row * NCH + ((4 * q + s) ^ swz(row))]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4_t& c = wv[nb][s >> 1];
+        fb[nb] = (s & 1) ? fp8x8_to_bf16(c.z, c.w, scale[nb]) : fp8x8_to_bf16(c.x, c.y, scale[nb]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+    }
+  } else if constexpr (sizeof(T) == 2) {
     bf16x8_t fa[2][2], fb[2][4];
     auto read = [&](int s, int slot) {
 #pragma unroll
@@ -253,7 +340,7 @@ __device__ __forceinline__ void load_tokens(const GemmArgs& g, int4 p, int (&tok
   }
 }
 
-template <typename T, int KIND>
+template <typename T, int KIND, bool FP8>
 __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& t) {
   constexpr int EPC = Elem<T>::EPC;
   const int H = g.H;
@@ -272,18 +359,41 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
       const int token = t.shared ? tok[j] : div_k(tok[j], g.k, g.kmagic);
       t.a[j] = reinterpret_cast<const char*>(x + (size_t)token * H + lane_chunk(row) * EPC);
     }
-    const T* wg = static_cast<const T*>(t.shared ? g.ws0 : g.w0);
-    const T* wu = static_cast<const T*>(t.shared ? g.ws1 : g.w1);
-    const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * H;
+    if (FP8) {
+      // codes [., N, H] (one byte per weight); scales [., H/32, N_s] per
+      // matrix, the shared experts' matrices of width Is one after another
+      const char* wg = static_cast<const char*>(t.shared ? g.ws0 : g.w0);
+      const char* wu = static_cast<const char*>(t.shared ? g.ws1 : g.w1);
+      const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * H;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = b_row(j);
-      const int n = min(t.n0 + (row & 127), t.N - 1);
-      t.b[j] = reinterpret_cast<const char*>((row < 128 ? wg : wu) + ebase + (size_t)n * H +
-                                             lane_chunk(row) * EPC);
+      for (int j = 0; j < 4; ++j) {
+        const int row = b_row_fp8(j);
+        const int n = min(t.n0 + (row & 127), t.N - 1);
+        t.b[j] = (row < 128 ? wg : wu) + ebase + (size_t)n * H + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+      }
+      const int w = threadIdx.x >> 6;
+      const int ns = t.shared ? g.Is : g.I;
+      const uint8_t* sm = w < 2 ? (t.shared ? g.sws0 : g.sw0) : (t.shared ? g.sws1 : g.sw1);
+      const int n = min(t.n0 + (scale_lane_row() & 127), t.N - 4);
+      const int se = t.shared ? n / ns : 0;
+      const size_t mat = t.shared ? (size_t)se * (H / 32) * ns : (size_t)t.e * (H / 32) * ns;
+      t.s = reinterpret_cast<const char*>(sm) + mat + (n - se * ns) + (size_t)scale_lane_block() * ns;
+      t.sstep = 2 * ns;
+      t.kseg = H;
+    } else {
+      const T* wg = static_cast<const T*>(t.shared ? g.ws0 : g.w0);
+      const T* wu = static_cast<const T*>(t.shared ? g.ws1 : g.w1);
+      const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * H;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = b_row(j);
+        const int n = min(t.n0 + (row & 127), t.N - 1);
+        t.b[j] = reinterpret_cast<const char*>((row < 128 ? wg : wu) + ebase + (size_t)n * H +
+                                               lane_chunk(row) * EPC);
+      }
+      t.kseg = H * (int)sizeof(T);
     }
     t.nk = H / (NCH * EPC);
-    t.kseg = H * (int)sizeof(T);
     t.bstride_kb = 0;
   } else {
     // down: shared tiles read h_shared [T, S*Is] against the S shared down
@@ -293,8 +403,6 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
     const int Ks = sh ? g.S * g.Is : g.I;  // row length of the activations
     const int ldb = sh ? g.Is : g.I;       // row length of a weight K segment
     const T* act = static_cast<const T*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
-    const T* wd = sh ? static_cast<const T*>(g.ws0)
-                     : static_cast<const T*>(g.w0) + (size_t)t.e * H * g.I;
     t.n0 = nt * BR;
     t.N = H;
 #pragma unroll
@@ -303,15 +411,35 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
       t.a[j] = reinterpret_cast<const char*>(act + (size_t)(t.row0 + min(row, t.nrows - 1)) * Ks +
                                              lane_chunk(row) * EPC);
     }
+    if (FP8) {
+      // scales [K/32, H]: the S shared matrices' blocks follow one another
+      // along K, so K-step j of a shared tile reads blocks 2j, 2j+1
+      const char* wd = sh ? static_cast<const char*>(g.ws0)
+                          : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = b_row(j);
-      t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * ldb +
-                                             lane_chunk(row) * EPC);
+      for (int j = 0; j < 4; ++j) {
+        const int row = b_row_fp8(j);
+        t.b[j] = wd + (size_t)min(t.n0 + row, H - 1) * ldb + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+      }
+      const uint8_t* sm = sh ? g.sws0 : g.sw0 + (size_t)t.e * (g.I / 32) * H;
+      const int n = min(t.n0 + scale_lane_row(), H - 4);
+      t.s = reinterpret_cast<const char*>(sm) + n + (size_t)scale_lane_block() * H;
+      t.sstep = 2 * H;
+      t.kseg = ldb;
+      t.bstride_kb = sh ? (int)(((long)H * g.Is) >> 10) : 0;
+    } else {
+      const T* wd = sh ? static_cast<const T*>(g.ws0)
+                       : static_cast<const T*>(g.w0) + (size_t)t.e * H * g.I;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = b_row(j);
+        t.b[j] = reinterpret_cast<const char*>(wd + (size_t)min(t.n0 + row, H - 1) * ldb +
+                                               lane_chunk(row) * EPC);
+      }
+      t.kseg = ldb * (int)sizeof(T);
+      t.bstride_kb = sh ? (int)(((long)H * g.Is * (long)sizeof(T)) >> 10) : 0;
     }
     t.nk = Ks / (NCH * EPC);
-    t.kseg = ldb * (int)sizeof(T);
-    t.bstride_kb = sh ? (int)(((long)H * g.Is * (long)sizeof(T)) >> 10) : 0;
   }
   t.nk3 = (t.nk + 2) / 3 * 3;
 }
@@ -324,15 +452,15 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
 // stage's loads are younger), barrier (all waves' loads of stage j are in LDS
 // and every wave is done with stage j-1's set), issue the loads of the stage
 // two ahead into that set, compute stage j.
-#define MOE_STEP(TL, J, LA, LB, NA, NB)          \
-  {                                              \
-    wait_vmcnt<LOADS_PER_STAGE>();               \
-    __builtin_amdgcn_s_barrier();                \
-    issue_stage(TL, J, NA, NB);                  \
-    compute_stage<T, KIND>(LA, LB, acc);         \
+#define MOE_STEP(TL, J, LA, LB, NA, NB)                       \
+  {                                                           \
+    wait_vmcnt<FP8 ? LOADS_FP8 : LOADS_BF16>();               \
+    __builtin_amdgcn_s_barrier();                             \
+    issue_stage<FP8>(TL, J, NA, NB);                          \
+    compute_stage<T, KIND, FP8>(LA, LB, acc);                 \
   }
 
-template <typename T, int KIND, bool ATOMIC>
+template <typename T, int KIND, bool ATOMIC, bool FP8>
 __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   MOE_LDS_STAGES
   __shared__ int offs[MAX_EXPERTS + 1];
@@ -369,13 +497,13 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   int tok[4] = {0, 0, 0, 0};
   load_tokens<KIND>(g, place(0), tok);
   Tile cur, nxt;
-  make_tile<T, KIND>(g, place(0), tok, cur);
+  make_tile<T, KIND, FP8>(g, place(0), tok, cur);
   load_tokens<KIND>(g, place(1), tok);
   int ep_r = 0;  // routed down epilogue: the sorted row id of row threadIdx.x
   if (KIND == DOWN_ROUTED && threadIdx.x < BM)
     ep_r = g.sorted_rows[cur.row0 + min((int)threadIdx.x, cur.nrows - 1)];
-  issue_stage(cur, 0, lds_a0, lds_b0);
-  issue_stage(cur, 1, lds_a1, lds_b1);
+  issue_stage<FP8>(cur, 0, lds_a0, lds_b0);
+  issue_stage<FP8>(cur, 1, lds_a1, lds_b1);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
@@ -405,7 +533,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
       if (ATOMIC) ep_wt = g.topk_w[ep_r];
       ep_t = div_k(ep_r, g.k, g.kmagic);
     }
-    make_tile<T, KIND>(g, place(li + 1), tok, nxt);
+    make_tile<T, KIND, FP8>(g, place(li + 1), tok, nxt);
     // ids of the tile after next, then (below) the next tile's first stages
     load_tokens<KIND>(g, place(li + 2), tok);
     if (KIND == DOWN_ROUTED && threadIdx.x < BM)
@@ -544,22 +672,22 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
 }
 #undef MOE_STEP
 
-// one entry per kind, so that profiles name them
-template <typename T>
+// one entry per kind, so that profiles name them (FP8: MXFP8 weights)
+template <typename T, bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_kernel(GemmArgs g) {
-  moe_gemm_body<T, GATE_UP, false>(g);
+  moe_gemm_body<T, GATE_UP, false, FP8>(g);
 }
-template <typename T>
+template <typename T, bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_SHARED, false>(g);
+  moe_gemm_body<T, DOWN_SHARED, false, FP8>(g);
 }
-template <typename T, bool ATOMIC>
+template <typename T, bool ATOMIC, bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_ROUTED, ATOMIC>(g);
+  moe_gemm_body<T, DOWN_ROUTED, ATOMIC, FP8>(g);
 }
-template <typename T>
+template <typename T, bool FP8>
 __global__ void __launch_bounds__(NTHR) moe_down_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_BOTH, false>(g);
+  moe_gemm_body<T, DOWN_BOTH, false, FP8>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -586,30 +714,36 @@ static int grid_for(long max_tiles) { return (int)(max_tiles < num_cus() ? max_t
 hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(moe_gate_up_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  if (g.fp8)
+    hipLaunchKernelGGL((moe_gate_up_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else if (dtype == MOE_BF16)
+    hipLaunchKernelGGL((moe_gate_up_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   else
-    hipLaunchKernelGGL(moe_gate_up_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+    hipLaunchKernelGGL((moe_gate_up_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared;
   if (n <= 0) return hipSuccess;
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(moe_down_shared_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  if (g.fp8)
+    hipLaunchKernelGGL((moe_down_shared_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else if (dtype == MOE_BF16)
+    hipLaunchKernelGGL((moe_down_shared_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   else
-    hipLaunchKernelGGL(moe_down_shared_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+    hipLaunchKernelGGL((moe_down_shared_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(moe_down_kernel<bf16_t>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  if (g.fp8)
+    hipLaunchKernelGGL((moe_down_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  else if (dtype == MOE_BF16)
+    hipLaunchKernelGGL((moe_down_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   else
-    hipLaunchKernelGGL(moe_down_kernel<float>, dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+    hipLaunchKernelGGL((moe_down_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }
 
@@ -617,12 +751,15 @@ hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStre
   const long n = (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
   const dim3 grid(grid_for(n));
-  if (dtype == MOE_BF16) {
-    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true>), grid, dim3(NTHR), 0, st, g);
-    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false>), grid, dim3(NTHR), 0, st, g);
+  if (g.fp8) {
+    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true, true>), grid, dim3(NTHR), 0, st, g);
+    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false, true>), grid, dim3(NTHR), 0, st, g);
+  } else if (dtype == MOE_BF16) {
+    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true, false>), grid, dim3(NTHR), 0, st, g);
+    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false, false>), grid, dim3(NTHR), 0, st, g);
   } else {
-    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<float, true>), grid, dim3(NTHR), 0, st, g);
-    else hipLaunchKernelGGL((moe_down_routed_kernel<float, false>), grid, dim3(NTHR), 0, st, g);
+    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<float, true, false>), grid, dim3(NTHR), 0, st, g);
+    else hipLaunchKernelGGL((moe_down_routed_kernel<float, false, false>), grid, dim3(NTHR), 0, st, g);
   }
   return hipGetLastError();
 }

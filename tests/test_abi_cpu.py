@@ -119,12 +119,12 @@ def _mx_cfg(**kw):
 
 
 def test_mxfp8_config_checks():
-    """MXFP8 weights need bf16 activations and K lengths the 32-row kernels
-    cover; the scales must be given."""
+    """MXFP8 weights need bf16 activations; the scales must be given."""
     assert moe.moe_workspace_size(_mx_cfg(), 64) > 0
+    assert moe.moe_workspace_size(_mx_cfg(hidden_size=6208, moe_intermediate_size=1408,
+                                          shared_intermediate_size=1408), 64) > 0
     for bad, status in ((dict(weight_format=2), moe.MOE_ERR_INVALID_ARG),
-                        (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED),
-                        (dict(hidden_size=6208), moe.MOE_ERR_UNSUPPORTED)):
+                        (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED)):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_workspace_size(_mx_cfg(**bad), 64)
         assert ei.value.status == status, bad

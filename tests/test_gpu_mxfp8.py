@@ -7,7 +7,8 @@ scales the GPU reads), fed the GPU's own router logits: routing and grouping
 exactly, h, h_shared and the output at the layer's bf16 bar
 (max|err| <= 2e-2 max|ref|). The GPU converts codes to bf16 exactly (a power-
 of-two scale on a 4-bit significand), so its arithmetic differs from the bf16
-path only in where the weights come from. Cases cover several tiles per
+path only in where the weights come from. Cases cover both tile kernels (32
+rows for decode-sized batches, 128 rows otherwise), several tiles per
 expert, two separate shared experts (their scale matrices side by side and
 the shared down projection's K segments), the packed shared slot with
 clamp-SwiGLU, no shared expert, one token, 128 experts, and both combine
@@ -69,9 +70,25 @@ MX = {
 }
 
 
-@pytest.mark.parametrize("name", list(MX))
-def test_mxfp8_layer_matches_oracle(name):
-    cfg = MX[name]
+# the 128-row tile kernel: batches beyond the decode size, K lengths that
+# are not multiples of 256 (the AFMoE width 1408), ragged last K-steps
+MX_128 = {
+    "afmoe_shape_two_shared": custom(T=700, hidden_size=512, num_experts=8, num_experts_per_tok=6,
+                                     moe_intermediate_size=448, num_shared_experts=2,
+                                     shared_intermediate_size=192, x_scale=22.6,
+                                     weight_format="mxfp8"),
+    "packed_clamp_prefill": custom(T=600, hidden_size=384, num_experts=4, num_experts_per_tok=2,
+                                   moe_intermediate_size=320, num_shared_experts=1,
+                                   shared_packed=1, hidden_act="swigluoai", route_scale=2.0,
+                                   w_std=0.2, x_scale=20.0, weight_format="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(MX) + list(MX_128))
+def test_mxfp8_layer_matches_oracle(name, monkeypatch):
+    cfg = MX.get(name) or MX_128[name]
+    if name in MX and cfg["T"] > 64:
+        monkeypatch.setenv("MOE_GEMM_TILE", "32")   # keep the 32-row kernel on the big edge case
     inp = synth.generate(cfg)
     assert inp.w_gate.dtype == np.uint8
     ov = oracle_view(inp)
