@@ -118,6 +118,8 @@ def _short(name: str) -> str:
     """Kernel name without template arguments and parameter list."""
     n = name.replace("(anonymous namespace)::", "").replace("void ", "")
     n = n.split("(")[0].split("<")[0].strip()
+    if n.startswith("_ZN12_GLOBAL__N_1"):  # mangled, anonymous namespace
+        n = "_Z" + n[len("_ZN12_GLOBAL__N_1"):]
     if n.startswith("_Z"):  # mangled: _Z<len><name>...
         i = 2
         while i < len(n) and n[i].isdigit():
