@@ -49,21 +49,35 @@ constexpr int NTHR = 256;
 // LDS stages: four (three K-steps of weights in flight while one is
 // computed); MXFP8 stages are smaller, so six when every K length of the
 // launch is a multiple of six steps.
-constexpr int LOADS_BF16 = 9;  // per thread per stage: 1 activation + 8 weight
-constexpr int LOADS_FP8 = 6;   // 1 activation + 4 weight + 1 scale
-constexpr int FP8_SCALES = 1024;  // u32x4 index of the scale bytes in an MXFP8 weight stage
+// Weight modes: W_BF16; W_FP8 (MXFP8, K-steps of 64 inputs: 64-byte weight
+// rows); W_FP8L (MXFP8, K-steps of 128 inputs: whole 128-byte weight rows,
+// 256-byte activation rows, the step's four scale blocks).
+constexpr int W_BF16 = 0, W_FP8 = 1, W_FP8L = 2;
+// loads per thread per stage: activation + weight (+ scale)
+template <int M>
+constexpr int loads_of() { return M == W_BF16 ? 1 + 8 : M == W_FP8 ? 1 + 4 + 1 : 2 + 8 + 1; }
+// u32x4 index of the scale bytes inside a stage's weight part
+template <int M>
+constexpr int scales_at() { return M == W_FP8 ? 1024 : DBR * NCH; }
+// inputs per K-step
+template <int M>
+constexpr int k_of() { return M == W_FP8L ? 128 : 64; }
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_WG_TILES = 128;
 constexpr int EPI_GU = 16;     // vector memory ops of a gate/up epilogue (per thread)
 constexpr int EPI_DN = 32;     // ... of a down epilogue
 
-// A stage: DBM activation rows, then the weight rows (bf16: DBR x 128 B;
-// MXFP8: DBR x 64 B and the step's scale bytes, 1 KiB), in 16-byte units.
-constexpr int STAGE_A = DBM * NCH;
-template <bool FP8>
-constexpr int stage_u4() { return STAGE_A + (FP8 ? 1024 + 64 : DBR * NCH); }
-static_assert(4 * stage_u4<false>() * 16 <= 144 * 1024, "bf16 stages exceed their LDS budget");
-static_assert(6 * stage_u4<true>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
+// A stage: the DBM activation rows (W_FP8L: two halves of 128 bytes per row,
+// each laid out like a 128-byte step), then the weight rows (bf16 and
+// W_FP8L: DBR x 128 B; W_FP8: DBR x 64 B) and, for MXFP8, the step's scale
+// bytes (1 KiB), in 16-byte units.
+template <int M>
+constexpr int stage_a() { return M == W_FP8L ? 2 * DBM * NCH : DBM * NCH; }
+template <int M>
+constexpr int stage_u4() { return stage_a<M>() + (M == W_BF16 ? DBR * NCH : scales_at<M>() + 64); }
+static_assert(4 * stage_u4<W_BF16>() * 16 <= 144 * 1024, "bf16 stages exceed their LDS budget");
+static_assert(6 * stage_u4<W_FP8>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
+static_assert(3 * stage_u4<W_FP8L>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
 
 // Wave w loads activation rows 8w .. 8w+7 (one instruction) and weight rows
 // 64w + 8j .. +7 (instruction j < 8); the lane's row is that base + lane/8
@@ -129,15 +143,16 @@ struct DTile {
   int shared, e, row0, nrows, n0, N;
 };
 
-// The 9 loads of this lane for step j of tile t into stage (la, lb). Every
-// K length is a multiple of four steps (the host checks), so there are no
-// padding steps and no branch here: a branch would merge two load states
-// and make the compiler wait for every load before the next LDS read.
-template <bool FP8>
+// The loads of this lane for step j of tile t into stage (la, lb). Every K
+// length is a multiple of the stage count in steps (the host checks), so
+// there are no padding steps and no branch here: a branch would merge two
+// load states and make the compiler wait for every load before the next LDS
+// read.
+template <int M>
 __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, u32x4_t* lb) {
   const int w = threadIdx.x >> 6;
-  const long kb = (long)j * KSB;                 // activation bytes per step
-  const long wb = FP8 ? (long)j * (KSB / 2) : kb;  // weight bytes per step
+  const long kb = (long)j * (M == W_FP8L ? 2 * KSB : KSB);  // activation bytes per step
+  const long wb = (long)j * (M == W_FP8 ? KSB / 2 : KSB);   // weight bytes per step
   long bk = wb;
   if (t.bstride) {
     const long seg = wb / t.kseg;
@@ -146,16 +161,20 @@ __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, 
   const char* ab = t.abase + kb;
   const char* bb = t.bbase + bk;
   dma16(ab, t.aoff, la + 8 * w * NCH);
-  if (FP8) {
+  if (M == W_FP8L) dma16(ab + KSB, t.aoff, la + DBM * NCH + 8 * w * NCH);
+  if (M == W_FP8) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(bb, t.boff[q], lb + (64 * w + 16 * q) * 4);
-    // wave w: lanes 0..31 the scales of rows 64w .. 64w+63 (block 0, then
-    // block 1), lanes 32..63 the same bytes again into the slot's unused half
-    dma4(t.sbase + (long)j * t.sstep, t.soff, reinterpret_cast<const char*>(lb + FP8_SCALES) + 256 * w);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
   }
+  // scales: wave w loads rows 64w .. 64w+63 (W_FP8: lanes 0..31 for blocks
+  // 0, 1, lanes 32..63 the same bytes again into the slot's unused half;
+  // W_FP8L: lanes 16b .. 16b+15 block b)
+  if (M != W_BF16)
+    dma4(t.sbase + (long)j * t.sstep, t.soff,
+         reinterpret_cast<const char*>(lb + scales_at<M>()) + 256 * w);
 }
 
 // First weight row (within the 256-row tile) of block nb (0..1) of wave w.
@@ -187,12 +206,44 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) {
 //   bf16 weights: lane l reads row l%32, chunk 2s + l/32.
 //   MXFP8 weights: lane l takes inputs 32q + 8s .. +7 (q = l/32): activation
 //   chunk 4q + s; weight bytes of chunks 2q, 2q+1 and the scale of block q.
-template <int KIND, bool FP8>
+template <int KIND, int M>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 5, r = lane & 31;
-  if (FP8) {
-    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + FP8_SCALES);
+  if (M == W_FP8L) {
+    // eight sub-steps: lane half q takes inputs 64q .. 64q+63 (activation
+    // half q, weight chunks 4q .. 4q+3, scale blocks 2q, 2q+1), sub-step s the
+    // eight at 64q + 8s
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + scales_at<M>());
+    const u32x4_t* lah = la + q * DBM * NCH;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t wv[2][2];
+      float scale[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = wrow<KIND>(w, nb) + r;
+        wv[nb][0] = lb[row * NCH + ((4 * q + 2 * h) ^ swz(row))];
+        wv[nb][1] = lb[row * NCH + ((4 * q + 2 * h + 1) ^ swz(row))];
+        scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * (2 * q + h) + (row & 63)]);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int s = 4 * h + s4;
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lah[r * NCH + (s ^ swz(r))]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4_t& c = wv[nb][s4 >> 1];
+          const bf16x8_t fb = (s4 & 1) ? fp8x8_to_bf16(c.z, c.w, scale[nb])
+                                       : fp8x8_to_bf16(c.x, c.y, scale[nb]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    return;
+  }
+  if (M == W_FP8) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + scales_at<M>());
     u32x4_t wv[2][2];
     float scale[2];
 #pragma unroll
@@ -286,10 +337,15 @@ __device__ __forceinline__ int scale_lane_row() { return 64 * (threadIdx.x >> 6)
 __device__ __forceinline__ int scale_lane_block() { return (threadIdx.x >> 4) & 1; }
 
 // tok: gate/up only, the token of this lane's activation row (token_of).
-template <int KIND, bool FP8>
+template <int KIND, int M>
 __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DTile& t) {
   constexpr int EPC = 8;
+  constexpr bool FP8 = M != W_BF16;
   constexpr uint32_t WES = FP8 ? 1u : 2u;  // weight element size
+  // W_FP8: lanes 32..63 repeat the scale bytes of lanes 0..31; W_FP8L: lane
+  // l takes block l / 16
+  const int sblock = M == W_FP8L ? (threadIdx.x & 63) >> 4 : scale_lane_block();
+  constexpr int SBLK = M == W_FP8L ? 4 : 2;  // scale blocks per K-step
   const int H = g.H;
   t.row0 = p.x;
   t.nrows = p.y & 0xFFFF;
@@ -307,13 +363,22 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? g.ws0 : g.w0)
                                                     : (t.shared ? g.ws1 : g.w1));
     t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * H * WES);
-    if (FP8) {
+    if (M == W_FP8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int br = b_row_fp8(j);
         const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
         t.boff[j] = n * (uint32_t)H + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int br = b_row(j);
+        const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
+        t.boff[j] = n * (uint32_t)H * WES + (uint32_t)(lane_chunk(br) * 16);
+      }
+    }
+    if (FP8) {
       // scales [., H/32, N_s] per matrix; the shared experts are S matrices
       // of width Is one after another (one, slot E, when packed), so a
       // shared column n is column n - s*Is of matrix s = n / Is
@@ -322,17 +387,10 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
       const int n = min(t.n0 + (scale_lane_row() & 127), t.N - 4);
       const int se = t.shared ? n / ns : 0;
       t.sbase = reinterpret_cast<const char*>(sm) + (t.shared ? 0 : (size_t)t.e * (H / 32) * ns);
-      t.soff = (uint32_t)((size_t)se * (H / 32) * ns + (n - se * ns) + (size_t)scale_lane_block() * ns);
-      t.sstep = 2 * ns;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int br = b_row(j);
-        const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
-        t.boff[j] = (n * (uint32_t)H + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
-      }
+      t.soff = (uint32_t)((size_t)se * (H / 32) * ns + (n - se * ns) + (size_t)sblock * ns);
+      t.sstep = SBLK * ns;
     }
-    t.nk = H / (NCH * EPC);
+    t.nk = H / k_of<M>();
     t.kseg = H * WES;
     t.bstride = 0;
   } else {
@@ -349,29 +407,31 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     t.N = H;
     const uint32_t arow = (uint32_t)(t.row0 + min(row, t.nrows - 1));
     t.aoff = (arow * (uint32_t)Ks + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
-    if (FP8) {
+    if (M == W_FP8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int br = b_row_fp8(j);
         const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
         t.boff[j] = n * (uint32_t)ldb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
       }
-      // scales [K/32, H]: the S shared matrices' blocks follow one another
-      // along K, so a shared tile's K-step j always reads blocks 2j, 2j+1
-      const uint8_t* sm = sh ? g.sws0 : g.sw0 + (size_t)t.e * (g.I / 32) * H;
-      const int n = min(t.n0 + scale_lane_row(), H - 4);
-      t.sbase = reinterpret_cast<const char*>(sm);
-      t.soff = (uint32_t)(n + scale_lane_block() * H);
-      t.sstep = 2 * H;
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int br = b_row(j);
         const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
-        t.boff[j] = (n * (uint32_t)ldb + (uint32_t)(lane_chunk(br) * EPC)) * 2u;
+        t.boff[j] = n * (uint32_t)ldb * WES + (uint32_t)(lane_chunk(br) * 16);
       }
     }
-    t.nk = Ks / (NCH * EPC);
+    if (FP8) {
+      // scales [K/32, H]: the S shared matrices' blocks follow one another
+      // along K, so a shared tile's K-step j always reads blocks 2j, 2j+1
+      const uint8_t* sm = sh ? g.sws0 : g.sw0 + (size_t)t.e * (g.I / 32) * H;
+      const int n = min(t.n0 + scale_lane_row(), H - 4);
+      t.sbase = reinterpret_cast<const char*>(sm);
+      t.soff = (uint32_t)(n + sblock * H);
+      t.sstep = SBLK * H;
+    }
+    t.nk = Ks / k_of<M>();
     t.kseg = ldb * WES;
     t.bstride = sh && g.S > 1 ? H * g.Is * WES : 0;
   }
@@ -464,9 +524,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const DTile& cur, co
 // epilogue stores in a tile's first three steps, may still be in flight),
 // barrier, issue the loads of step j+3 into the stage freed at step j-1
 // (the next tile's first stages when j+3 passes the end), compute stage j.
-template <int KIND, bool ATOMIC, bool FP8, int NST>
+template <int KIND, bool ATOMIC, int M, int NST>
 __device__ __forceinline__ void decode_body(const GemmArgs& g) {
-  constexpr int STAGE = stage_u4<FP8>();
+  constexpr int STAGE = stage_u4<M>();
+  constexpr int STAGE_A = stage_a<M>();
   __shared__ __align__(16) u32x4_t lds_st[NST][STAGE];
   __shared__ int offs[MAX_EXPERTS + 1];
   __shared__ int cum[MAX_EXPERTS + 1];
@@ -493,7 +554,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   };
 
   constexpr int EPI = KIND == GATE_UP ? EPI_GU : EPI_DN;
-  constexpr int LOADS = FP8 ? LOADS_FP8 : LOADS_BF16;
+  constexpr int LOADS = loads_of<M>();
   constexpr bool ROWS = KIND == GATE_UP || (KIND == DOWN_ROUTED && ATOMIC);
   if (ROWS) {
     gather_rows(g, place(0), rows_buf[0]);
@@ -505,16 +566,16 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     __syncthreads();
   }
   DTile cur, nxt;
-  make_tile<KIND, FP8>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
+  make_tile<KIND, M>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st) issue_stage<FP8>(cur, st, lds_st[st], lds_st[st] + STAGE_A);
+  for (int st = 0; st < NST - 1; ++st) issue_stage<M>(cur, st, lds_st[st], lds_st[st] + STAGE_A);
 
   bool first = true;
   for (int li = 0;; ++li) {
     const bool has_next = li + 1 < n_my;
     // the next tile (its row ids were gathered a tile ago), then the row ids
     // of the one after it
-    make_tile<KIND, FP8>(g, place(li + 1),
+    make_tile<KIND, M>(g, place(li + 1),
                     KIND == GATE_UP ? token_of(g, place(li + 1), rows_buf[(li + 1) % 3]) : 0, nxt);
     if (KIND == DOWN_ROUTED && ATOMIC && threadIdx.x < 64) {
       // this tile's rows: token and routing weight of each (the weights are
@@ -537,8 +598,8 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     if ((J) < NST - 1 && !first) wait_vmcnt<(NST - 2) * LOADS + EPI>();                \
     else wait_vmcnt<(NST - 2) * LOADS>();                                              \
     __builtin_amdgcn_s_barrier();                                                      \
-    issue_stage<FP8>(TL, JL, lds_st[SN], lds_st[SN] + STAGE_A);                        \
-    compute_stage<KIND, FP8>(lds_st[SC], lds_st[SC] + STAGE_A, acc);                   \
+    issue_stage<M>(TL, JL, lds_st[SN], lds_st[SN] + STAGE_A);                          \
+    compute_stage<KIND, M>(lds_st[SC], lds_st[SC] + STAGE_A, acc);                     \
   }
     // a group of NST steps uses stages 0 .. NST-1 and loads NST-1 steps ahead;
     // the tile's last group loads its last step and the next tile's first
@@ -562,21 +623,21 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   __builtin_amdgcn_s_barrier();
 }
 
-template <bool FP8, int NST>
+template <int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_decode_kernel(GemmArgs g) {
-  decode_body<GATE_UP, false, FP8, NST>(g);
+  decode_body<GATE_UP, false, M, NST>(g);
 }
-template <bool FP8, int NST>
+template <int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_BOTH, false, FP8, NST>(g);
+  decode_body<DOWN_BOTH, false, M, NST>(g);
 }
-template <bool FP8, int NST>
+template <int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_SHARED, false, FP8, NST>(g);
+  decode_body<DOWN_SHARED, false, M, NST>(g);
 }
-template <bool ATOMIC, bool FP8, int NST>
+template <bool ATOMIC, int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_ROUTED, ATOMIC, FP8, NST>(g);
+  decode_body<DOWN_ROUTED, ATOMIC, M, NST>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -617,37 +678,67 @@ static hipError_t launch_decode(void (*kern)(GemmArgs), long n, const GemmArgs& 
   return hipGetLastError();
 }
 
-// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1),
-// with six stages when every K length the launch streams is a multiple of
-// six 64-element steps.
-static bool six(int K) { return (K / 64) % 6 == 0; }
+// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1):
+// 128-input K-steps with three stages when every K length the launch streams
+// is a multiple of three such steps (and a separate shared expert's width a
+// multiple of 128), else 64-input steps with six stages (K a multiple of six
+// steps) or four.
+static bool steps_div(int K, int k_step, int n) { return K % k_step == 0 && (K / k_step) % n == 0; }
+
+enum Variant { V_BF16, V_FP8L3, V_FP8_6, V_FP8_4 };
+
+static Variant pick(const GemmArgs& g, bool gate_up, bool routed, bool shared) {
+  if (!g.fp8) return V_BF16;
+  bool l3 = true, six = true;
+  if (gate_up) {
+    l3 = steps_div(g.H, 128, 3);
+    six = steps_div(g.H, 64, 6);
+  } else {
+    if (routed) {
+      l3 = l3 && steps_div(g.I, 128, 3);
+      six = six && steps_div(g.I, 64, 6);
+    }
+    if (shared) {
+      l3 = l3 && steps_div(g.S * g.Is, 128, 3) && g.Is % 128 == 0;
+      six = six && steps_div(g.S * g.Is, 64, 6);
+    }
+  }
+  return l3 ? V_FP8L3 : six ? V_FP8_6 : V_FP8_4;
+}
+
+#define DEC_LAUNCH(KERN, V, n, g, st)                                                  \
+  ((V) == V_BF16    ? launch_decode(KERN<W_BF16, 4>, n, g, st)                          \
+   : (V) == V_FP8L3 ? launch_decode(KERN<W_FP8L, 3>, n, g, st)                          \
+   : (V) == V_FP8_6 ? launch_decode(KERN<W_FP8, 6>, n, g, st)                           \
+                    : launch_decode(KERN<W_FP8, 4>, n, g, st))
 
 hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
-  if (!g.fp8) return launch_decode(moe_gate_up_decode_kernel<false, 4>, n, g, st);
-  return six(g.H) ? launch_decode(moe_gate_up_decode_kernel<true, 6>, n, g, st)
-                  : launch_decode(moe_gate_up_decode_kernel<true, 4>, n, g, st);
+  return DEC_LAUNCH(moe_gate_up_decode_kernel, pick(g, true, true, g.S > 0), n, g, st);
 }
 hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
-  if (!g.fp8) return launch_decode(moe_down_decode_kernel<false, 4>, n, g, st);
-  return six(g.I) && six(g.S * g.Is) ? launch_decode(moe_down_decode_kernel<true, 6>, n, g, st)
-                                     : launch_decode(moe_down_decode_kernel<true, 4>, n, g, st);
+  return DEC_LAUNCH(moe_down_decode_kernel, pick(g, false, true, true), n, g, st);
 }
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared;
-  if (!g.fp8) return launch_decode(moe_down_shared_decode_kernel<false, 4>, n, g, st);
-  return six(g.S * g.Is) ? launch_decode(moe_down_shared_decode_kernel<true, 6>, n, g, st)
-                         : launch_decode(moe_down_shared_decode_kernel<true, 4>, n, g, st);
+  return DEC_LAUNCH(moe_down_shared_decode_kernel, pick(g, false, false, true), n, g, st);
 }
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st) {
   const long n = (long)g.mt_routed * g.nt_routed;
-  if (!g.fp8)
-    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, false, 4>, n, g, st)
-                  : launch_decode(moe_down_routed_decode_kernel<false, false, 4>, n, g, st);
-  if (six(g.I))
-    return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true, 6>, n, g, st)
-                  : launch_decode(moe_down_routed_decode_kernel<false, true, 6>, n, g, st);
-  return atomic ? launch_decode(moe_down_routed_decode_kernel<true, true, 4>, n, g, st)
-                : launch_decode(moe_down_routed_decode_kernel<false, true, 4>, n, g, st);
+  const Variant v = pick(g, false, true, false);
+  if (atomic) {
+    switch (v) {
+      case V_BF16: return launch_decode(moe_down_routed_decode_kernel<true, W_BF16, 4>, n, g, st);
+      case V_FP8L3: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8L, 3>, n, g, st);
+      case V_FP8_6: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8, 6>, n, g, st);
+      default: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8, 4>, n, g, st);
+    }
+  }
+  switch (v) {
+    case V_BF16: return launch_decode(moe_down_routed_decode_kernel<false, W_BF16, 4>, n, g, st);
+    case V_FP8L3: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8L, 3>, n, g, st);
+    case V_FP8_6: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8, 6>, n, g, st);
+    default: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8, 4>, n, g, st);
+  }
 }

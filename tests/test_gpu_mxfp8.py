@@ -67,6 +67,15 @@ MX = {
     "m3_like_128_experts": custom(T=48, hidden_size=768, num_experts=128, num_experts_per_tok=4,
                                   moe_intermediate_size=256, num_shared_experts=1,
                                   shared_packed=1, route_scale=2.0, weight_format="mxfp8"),
+    # K lengths that are multiples of three 128-input steps: the variant with
+    # whole 128-byte weight rows per K-step, routed and shared (packed, and
+    # two separate shared experts whose down projection is K-segmented)
+    "k128_packed": custom(T=40, hidden_size=768, num_experts=16, num_experts_per_tok=4,
+                          moe_intermediate_size=768, num_shared_experts=1, shared_packed=1,
+                          hidden_act="swigluoai", route_scale=2.0, weight_format="mxfp8"),
+    "k128_two_shared": custom(T=33, hidden_size=768, num_experts=8, num_experts_per_tok=2,
+                              moe_intermediate_size=768, num_shared_experts=2,
+                              shared_intermediate_size=384, weight_format="mxfp8"),
 }
 
 
