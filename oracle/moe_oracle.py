@@ -16,7 +16,11 @@ pages, one step per function, in the pages' order:
   3. selection key  key = s + expert_bias             (mlxcel #845 "Routing
      detail": bias added for selection only; mlxcel #763 "Architecture
      specification", MoE bullet: e_score_correction_bias, selection only)
-  4. top-k          first k experts in the order (key desc, index asc)
+  4. top-k          first k experts in the order (key desc, index asc);
+                    with n_group > 1 only experts of the topk_group groups
+                    with the largest sums of their two best keys
+                    (group_limit; mlxcel #845 "Routing detail" names group
+                    routing, the rule read from the DeepSeek MoE family)
   5. gather         g = s[idx]   (unbiased scores, mlxcel #845 "Routing detail")
   6. route_norm     w = g / sum(g)                    (mlxcel #845 "Routing detail")
   7. route_scale    w *= route_scale                  (mlxcel #845 "Routing
@@ -171,12 +175,33 @@ def route_weights(s: np.ndarray, idx: np.ndarray, route_norm: bool,
     return w * F64(route_scale)
 
 
+def group_limit(keys: np.ndarray, n_group: int, topk_group: int) -> np.ndarray:
+    """Group-limited selection (mlxcel #845 "Routing detail" names group
+    routing and n_group; read as the rule of the DeepSeek MoE family the page
+    derives AFMoE from): the E experts form n_group contiguous groups; a
+    group's score is the sum of its two largest selection keys; the
+    topk_group best groups (ties: lower group index) stay eligible and every
+    other expert's key becomes -inf, out of the top-k."""
+    if n_group <= 1:
+        return keys
+    T, E = keys.shape
+    gs = E // n_group
+    grp = np.asarray(keys, dtype=F64).reshape(T, n_group, gs)
+    top2 = -np.sort(-grp, axis=-1)[:, :, :2]
+    gscore = top2[:, :, 0] + top2[:, :, 1]
+    keep = np.argsort(-gscore, axis=-1, kind="stable")[:, :topk_group]
+    mask = np.zeros((T, n_group), bool)
+    np.put_along_axis(mask, keep, True, axis=-1)
+    return np.where(np.repeat(mask, gs, axis=1), keys, -np.inf)
+
+
 def route(logits: np.ndarray, expert_bias: np.ndarray | None, k: int,
           score_func: str = "sigmoid", route_norm: bool = True,
-          route_scale: float = 1.0):
-    """Steps 2-7: returns (s, keys, idx [T,k] int32, w [T,k] float64)."""
+          route_scale: float = 1.0, n_group: int = 1, topk_group: int = 1):
+    """Steps 2-7: returns (s, keys, idx [T,k] int32, w [T,k] float64). With
+    n_group > 1 the keys of experts outside the kept groups are -inf."""
     s = scores(logits, score_func)
-    keys = selection_keys(s, expert_bias)
+    keys = group_limit(selection_keys(s, expert_bias), n_group, topk_group)
     idx = select_topk(keys, k)
     w = route_weights(s, idx, route_norm, route_scale)
     return s, keys, idx, w
@@ -271,7 +296,8 @@ def moe_forward(inp, cfg: dict, logits: np.ndarray | None = None,
     x = as_f64(inp.x)
     L = router_logits(inp.x, inp.w_router) if logits is None else as_f64(logits)
     s, keys, idx, w = route(L, inp.expert_bias, k, cfg["score_func"],
-                            bool(cfg["route_norm"]), cfg["route_scale"])
+                            bool(cfg["route_norm"]), cfg["route_scale"],
+                            cfg.get("n_group", 1), cfg.get("topk_group", 1))
     counts, offsets, sorted_rows, row_pos = permute(idx, E)
     act = activation(cfg)
     out = np.zeros((T, x.shape[1]), F64)
@@ -312,7 +338,8 @@ def moe_forward_tokens(inp, cfg: dict, tokens, logits_rows: np.ndarray | None = 
     L = (as_f64(inp.x[tokens]) @ as_f64(inp.w_router).T if logits_rows is None
          else as_f64(logits_rows))
     s, keys, idx, w = route(L, inp.expert_bias, k, cfg["score_func"],
-                            bool(cfg["route_norm"]), cfg["route_scale"])
+                            bool(cfg["route_norm"]), cfg["route_scale"],
+                            cfg.get("n_group", 1), cfg.get("topk_group", 1))
     act = activation(cfg)
     out = np.zeros((tokens.size, x.shape[1]), F64)
     for e in np.unique(idx):

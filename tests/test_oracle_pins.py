@@ -610,3 +610,63 @@ def test_mx_layer_runs_on_the_dequantised_values():
     a, d = O.moe_forward(mx, cfg), O.moe_forward(dense, cfg)
     assert np.array_equal(a["idx"], d["idx"]) and np.array_equal(a["out"], d["out"])
 
+
+# --------------------------------------------------------------------------
+# group-limited routing (mlxcel #845 "Routing detail": group routing, n_group;
+# the rule read from the DeepSeek MoE family the page derives AFMoE from)
+
+def test_route_group_hand_example():
+    for c in _gold("route_group_hand_example.json")["cases"]:
+        L = np.array([[_logit(v) for v in c["logits"]]])
+        _, keys, idx, w = O.route(L, np.array(c["bias"], dtype=np.float32), c["k"], "sigmoid",
+                                  bool(c["route_norm"]), c["route_scale"], c["n_group"],
+                                  c["topk_group"])
+        assert idx[0].tolist() == c["idx"], c["why"]
+        assert np.allclose(w[0], c["w"], rtol=1e-12, atol=0), c["why"]
+        kept = sorted({int(e) // 2 for e in np.nonzero(np.isfinite(keys[0]))[0]})
+        assert kept == c["kept_groups"], c["why"]
+
+
+def _brute_group_route(key_row, n_group, topk_group, k):
+    """The rule by enumeration: the set of kept groups is the topk_group-subset
+    of groups ranked first by (score desc, index asc); top-k inside it by
+    (key desc, index asc)."""
+    E = key_row.size
+    gs = E // n_group
+    gscore = []
+    for g in range(n_group):
+        vals = sorted((float(v) for v in key_row[g * gs:(g + 1) * gs]), reverse=True)
+        gscore.append(vals[0] + vals[1])
+    ranked = sorted(range(n_group), key=lambda g: (-gscore[g], g))
+    kept = set(ranked[:topk_group])
+    cand = [e for e in range(E) if e // gs in kept]
+    return sorted(cand, key=lambda e: (-float(key_row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,k", [(8, 4, 2, 3), (12, 3, 1, 2), (16, 4, 3, 5),
+                                                    (256, 8, 4, 8), (10, 5, 5, 4)])
+def test_route_group_bruteforce(E, n_group, topk_group, k):
+    rng = np.random.default_rng(E + k)
+    L = rng.standard_normal((40, E))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    L[3, :] = 0.0                             # every key equal: ties everywhere
+    L[5, : E // 2] = L[5, E // 2:]            # mirrored halves: tied groups
+    _, keys, idx, w = O.route(L, bias, k, "sigmoid", True, 1.0, n_group, topk_group)
+    s = O.sigmoid(L)
+    raw = s + bias.astype(np.float64)[None, :]
+    for t in range(L.shape[0]):
+        assert idx[t].tolist() == _brute_group_route(raw[t], n_group, topk_group, k), t
+        assert len({int(e) // (E // n_group) for e in idx[t]}) <= topk_group
+    # weights are still the unbiased scores of the chosen experts, normalised
+    g = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    assert np.allclose(w, g / g.sum(1, keepdims=True), rtol=1e-14, atol=0)
+
+
+def test_route_all_groups_kept_is_plain_topk():
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((30, 32))
+    bias = rng.uniform(-0.05, 0.05, 32).astype(np.float32)
+    a = O.route(L, bias, 6, "softmax", True, 2.0)
+    b = O.route(L, bias, 6, "softmax", True, 2.0, n_group=8, topk_group=8)
+    assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+

@@ -55,7 +55,7 @@ def _cfg(**kw):
         route_scale=1.0, hidden_act="silu", act_alpha=1.702, act_limit=7.0,
         act_beta=1.0, x_scale=1.0, w_std=0.02, router_bf16_values=True,
         skew=None, rms_norm_eps=1e-5, norm_add_one=0, norm_w_std=0.1,
-        weight_format="dtype",
+        weight_format="dtype", n_group=1, topk_group=1,
     )
     base.update(kw)
     if base.get("shared_intermediate_size", 0) == 0:
@@ -144,7 +144,7 @@ def layer_keys(cfg: dict) -> dict:
             "num_shared_experts", "moe_intermediate_size",
             "shared_intermediate_size", "shared_packed", "score_func",
             "route_norm", "route_scale", "hidden_act", "act_alpha",
-            "act_limit", "act_beta", "dtype", "weight_format")
+            "act_limit", "act_beta", "dtype", "weight_format", "n_group", "topk_group")
     return {k: cfg[k] for k in keys}
 
 
