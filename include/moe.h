@@ -62,6 +62,15 @@ typedef enum {
  * gather of unbiased scores, route_norm and route_scale follow unchanged. */
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score_func;
 
+/* Group-limited routing (moe_config.n_group > 1; mlxcel #845 "Routing
+ * detail" names group routing and n_group, the rule is read from the
+ * DeepSeek MoE family the page derives AFMoE from): the E experts form
+ * n_group contiguous groups of E / n_group; a group's score is the sum of
+ * its two largest selection keys (fp64, the larger first); the topk_group
+ * groups with the largest scores (ties: lower group index) stay eligible and
+ * the top-k runs over their experts only. Weights, route_norm and
+ * route_scale are unchanged. */
+
 /* Expert activation: SiLU-SwiGLU (HF "AFMoE" doc, hidden_act "silu") or
  * clamp-SwiGLU (mlxcel #763 Activation bullet, hidden_act "swigluoai"):
  *   silu:      a = g * sigmoid(g) * u
@@ -127,6 +136,11 @@ typedef struct {
   int32_t dtype;                    /* moe_dtype of x, h, out (and the expert
                                        weights when weight_format is DTYPE)     */
   int32_t weight_format;            /* moe_weight_format of the expert weights   */
+  int32_t n_group;                  /* group-limited routing: 0 or 1 = off; else
+                                       E % n_group == 0, E / n_group >= 2,
+                                       n_group <= 64                             */
+  int32_t topk_group;               /* groups kept, 1..n_group; k <= topk_group *
+                                       E / n_group (used when n_group > 1)       */
 } moe_config;
 
 /* Bytes of device workspace that moe_layer_forward (and every stage entry

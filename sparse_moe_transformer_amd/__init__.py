@@ -50,6 +50,8 @@ class MoeConfig(ctypes.Structure):
         ("act_beta", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("weight_format", ctypes.c_int32),
+        ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32),
     ]
 
 
@@ -121,6 +123,8 @@ def make_config(cfg) -> MoeConfig:
     c.dtype = _DT.get(dt, dt) if isinstance(dt, str) else dt
     wf = cfg.get("weight_format", "dtype")
     c.weight_format = _WF.get(wf, wf) if isinstance(wf, str) else wf
+    c.n_group = int(cfg.get("n_group", 1))
+    c.topk_group = int(cfg.get("topk_group", 1))
     return c
 
 

@@ -48,6 +48,13 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
       !(std::isfinite(c->act_alpha) && std::isfinite(c->act_limit) && std::isfinite(c->act_beta)))
     return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->n_group < 0 || c->n_group > 64) return MOE_ERR_INVALID_ARG;
+  if (c->n_group > 1) {
+    const int gs = c->num_experts / c->n_group;
+    if (c->num_experts % c->n_group || gs < 2 || c->topk_group < 1 ||
+        c->topk_group > c->n_group || c->num_experts_per_tok > c->topk_group * gs)
+      return MOE_ERR_INVALID_ARG;
+  }
   if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_MXFP8)
     return MOE_ERR_INVALID_ARG;
   if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
@@ -320,7 +327,8 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
   // routing: one wavefront per token over many workgroups; grouping: one
   // workgroup for decode batches (T*k <= 1024), else three small kernels
   MOE_TRY(hip_ok(launch_route(logits, expert_bias, T, d.E, d.k, cfg->score_func,
-                              cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st)));
+                              cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st,
+                              cfg->n_group, cfg->topk_group)));
   MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
                                 w.local_rank, w.chunk_hist, st)));
   MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, mx, w.offsets, w.sorted_rows, w.h,
@@ -372,7 +380,7 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const float* logits,
   if (expert_counts) MOE_TRY(hip_ok(launch_fill_zero(expert_counts, (size_t)d.E * 4, st)));
   return hip_ok(launch_route(logits, expert_bias, (int)T, d.E, d.k, cfg->score_func,
                              cfg->route_norm, cfg->route_scale, topk_idx, topk_w, expert_counts,
-                             st));
+                             st, cfg->n_group, cfg->topk_group));
 }
 
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,

@@ -60,7 +60,8 @@ hipError_t launch_router_logits(const void* x, const float* w_router, float* log
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int score_func, int route_norm, float route_scale, int32_t* idx,
-                        float* w, int32_t* counts, hipStream_t st);
+                        float* w, int32_t* counts, hipStream_t st,
+                        int n_group = 1, int topk_group = 1);
 
 // permutation scratch: chunk histograms and per-row ranks
 int permute_chunk_rows();

@@ -21,6 +21,13 @@
 // row mirror: each pairs lanes symmetrically, so every lane ends with its
 // row's best), then combines the four row winners read with readlane. The
 // winner's lane retires it. No LDS round trip is involved.
+//
+// Group-limited selection (n_group > 1; mlxcel #845 "Routing detail" names
+// group routing, the rule read from the DeepSeek MoE family): the wave
+// writes its token's keys to LDS, lane g finds the two largest keys of group
+// g (experts g*gs .. g*gs+gs-1) and adds them in fp64 (largest first), the
+// topk_group best groups are picked by the same argmax rounds (ties: lower
+// group), and experts outside them drop out of the top-k rounds.
 #include <float.h>
 #include <limits.h>
 
@@ -77,15 +84,40 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// The wave's best (key desc, index asc) of the lanes' candidates c, as
+// uniform values: DPP exchanges within rows of 16 lanes, then the four row
+// winners by readlane.
+__device__ __forceinline__ void wave_best(Cand c, uint64_t& wk, int& wi) {
+  dpp_step<0xB1>(c);   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_step<0x4E>(c);   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_step<0x141>(c);  // row_half_mirror: i <-> 7 - i within 8 lanes
+  dpp_step<0x140>(c);  // row_mirror: i <-> 15 - i within 16 lanes
+  wk = 0;
+  wi = INT_MAX;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)c.k, 16 * row);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(c.k >> 32), 16 * row);
+    const int ri = __builtin_amdgcn_readlane(c.i, 16 * row);
+    const uint64_t rk = ((uint64_t)hi << 32) | lo;
+    if (better(rk, ri, wk, wi)) {
+      wk = rk;
+      wi = ri;
+    }
+  }
+}
+
 // Routes token row Lrow (one wavefront): writes its k indices and weights
 // (lanes < k, in selection order) and, if ex_row is given, the indices there.
+// gk: E doubles of LDS for this wave when n_group > 1 (else unused).
 template <int NPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
                                             const float* __restrict__ bias, int E, int k,
                                             int score_func, int route_norm, float route_scale,
                                             int32_t* __restrict__ idx_row,
                                             float* __restrict__ w_row, int* ex_row,
-                                            int32_t* __restrict__ counts) {
+                                            int32_t* __restrict__ counts, int n_group = 1,
+                                            int topk_group = 1, double* gk = nullptr) {
   const int lane = threadIdx.x & 63;
   double key[NPL], sc[NPL];
   bool live[NPL];
@@ -120,6 +152,46 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
     key[i] = live[i] ? (sc[i] + (bias ? (double)bias[e] : 0.0)) + 0.0 : 0.0;
     if (!live[i]) sc[i] = 0.0;
   }
+  if (n_group > 1 && gk) {
+    const int gs = E / n_group;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (live[i]) gk[lane + 64 * i] = key[i];
+    // this wave's LDS writes complete before its reads (and stay in order)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __asm__ __volatile__("" ::: "memory");
+    bool gcand = lane < n_group;
+    double gsc = 0.0;
+    if (gcand) {
+      double m1 = -INFINITY, m2 = -INFINITY;
+      for (int i = 0; i < gs; ++i) {
+        const double v = gk[lane * gs + i];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+      }
+      gsc = m1 + m2;
+    }
+    uint64_t kept = 0;
+    for (int j = 0; j < topk_group; ++j) {
+      Cand c{0ull, INT_MAX};
+      if (gcand) {
+        c.k = ordered_bits(gsc + 0.0);
+        c.i = lane;
+      }
+      uint64_t wk;
+      int wi;
+      wave_best(c, wk, wi);
+      kept |= 1ull << wi;
+      if (lane == wi) gcand = false;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (live[i] && !((kept >> ((lane + 64 * i) / gs)) & 1)) live[i] = false;
+  }
   double gsum = 0.0, my_g = 0.0;
   int my_idx = 0;
   for (int j = 0; j < k; ++j) {
@@ -136,24 +208,9 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
         }
       }
     }
-    dpp_step<0xB1>(c);   // quad_perm [1,0,3,2]: lane ^ 1
-    dpp_step<0x4E>(c);   // quad_perm [2,3,0,1]: lane ^ 2
-    dpp_step<0x141>(c);  // row_half_mirror: i <-> 7 - i within 8 lanes
-    dpp_step<0x140>(c);  // row_mirror: i <-> 15 - i within 16 lanes
-    // the four rows' winners (uniform values)
-    uint64_t wk = 0;
-    int wi = INT_MAX;
-#pragma unroll
-    for (int row = 0; row < 4; ++row) {
-      const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)c.k, 16 * row);
-      const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(c.k >> 32), 16 * row);
-      const int ri = __builtin_amdgcn_readlane(c.i, 16 * row);
-      const uint64_t rk = ((uint64_t)hi << 32) | lo;
-      if (better(rk, ri, wk, wi)) {
-        wk = rk;
-        wi = ri;
-      }
-    }
+    uint64_t wk;
+    int wi;
+    wave_best(c, wk, wi);
     const int wl = wi & 63, wslot = wi >> 6;
     double s_sel = 0.0;
 #pragma unroll
@@ -180,31 +237,47 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
   }
 }
 
-template <int NPL>
+template <int NPL, bool GROUPED>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int score_func, int route_norm,
                                                     float route_scale,
                                                     int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out,
-                                                    int32_t* __restrict__ counts) {
+                                                    int32_t* __restrict__ counts, int n_group,
+                                                    int topk_group) {
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // the whole wave leaves together
-  route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
-                   idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
+  if constexpr (GROUPED) {
+    __shared__ double gk[4][64 * NPL];
+    route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
+                     idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts, n_group,
+                     topk_group, gk[threadIdx.x >> 6]);
+  } else {
+    route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
+                     idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int score_func, int route_norm, float route_scale, int32_t* idx,
-                        float* w, int32_t* counts, hipStream_t st) {
+                        float* w, int32_t* counts, hipStream_t st, int n_group,
+                        int topk_group) {
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block), block(64 * waves_per_block);
   const int npl = (E + 63) / 64;
-#define MOE_ROUTE(N)                                                                        \
-  hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, st, logits, bias, T, E, k, score_func, \
-                     route_norm, route_scale, idx, w, counts)
+#define MOE_ROUTE(N)                                                                         \
+  do {                                                                                       \
+    if (n_group > 1)                                                                         \
+      hipLaunchKernelGGL((route_kernel<N, true>), grid, block, 0, st, logits, bias, T, E, k,  \
+                         score_func, route_norm, route_scale, idx, w, counts, n_group,       \
+                         topk_group);                                                        \
+    else                                                                                     \
+      hipLaunchKernelGGL((route_kernel<N, false>), grid, block, 0, st, logits, bias, T, E, k, \
+                         score_func, route_norm, route_scale, idx, w, counts, 1, 1);         \
+  } while (0)
   if (npl <= 1) MOE_ROUTE(1);
   else if (npl <= 2) MOE_ROUTE(2);
   else if (npl <= 4) MOE_ROUTE(4);

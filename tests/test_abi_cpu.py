@@ -133,3 +133,19 @@ def test_mxfp8_config_checks():
     m = moe.MoeMxScales(gate=0x2000, up=0x2000, down=None)
     assert _raw_forward(_mx_cfg(), 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
 
+
+@pytest.mark.parametrize("bad", [dict(n_group=3), dict(n_group=65), dict(n_group=8, topk_group=0),
+                                 dict(n_group=8, topk_group=9), dict(n_group=64),
+                                 dict(n_group=32, topk_group=2), dict(n_group=-1)])
+def test_group_routing_config_checks(bad):
+    """64 experts, top-6: groups must divide E into groups of at least two
+    experts, keep 1..n_group groups, and leave room for k experts."""
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(_cfg(**bad), 16)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_group_routing_accepted():
+    assert moe.moe_workspace_size(_cfg(n_group=8, topk_group=3), 16) > 0
+    assert moe.moe_workspace_size(_cfg(n_group=1, topk_group=0), 16) > 0   # off
+

@@ -36,7 +36,8 @@ def _check(dev, name, nsample, extra_tokens=()):
     Lref = O.router_logits(inp.x, inp.w_router)
     assert rel_err(res["logits"], Lref) <= 1e-5
     s, keys, idx, w = O.route(res["logits"], inp.expert_bias, k, cfg["score_func"],
-                              bool(cfg["route_norm"]), cfg["route_scale"])
+                              bool(cfg["route_norm"]), cfg["route_scale"],
+                              cfg.get("n_group", 1), cfg.get("topk_group", 1))
     assert np.array_equal(res["idx"], idx)
     assert np.max(np.abs(res["w"] - w) / np.maximum(np.abs(w), 1e-30)) <= 1e-6
     say(f"[full] {name} boundary key gap {O.boundary_gap(keys, k):.3e}")
@@ -109,7 +110,8 @@ def _check_block(dev, name, nsample):
     res = run_block(dev, nw, 1)
     k = cfg["num_experts_per_tok"]
     _, _, idx, _ = O.route(res["logits"], dev.inp.expert_bias, k, cfg["score_func"],
-                           bool(cfg["route_norm"]), cfg["route_scale"])
+                           bool(cfg["route_norm"]), cfg["route_scale"],
+                              cfg.get("n_group", 1), cfg.get("topk_group", 1))
     assert np.array_equal(res["idx"], idx)
     toks = _sample(dev.T, nsample, seed=1)
     worst = check_block(cfg, dev.inp, nw, res, tokens=toks)

@@ -63,6 +63,17 @@ EDGE = {
                                       route_norm=0, route_scale=2.0),
     "m2_shape_sigmoid": custom(T=70, hidden_size=128, num_experts=256, num_experts_per_tok=8,
                                moe_intermediate_size=64, num_shared_experts=1),
+    # group-limited routing (mlxcel #845 "Routing detail": n_group)
+    "grouped_e64_g8_keep3": custom(T=150, hidden_size=128, num_experts=64, num_experts_per_tok=6,
+                                   moe_intermediate_size=64, num_shared_experts=1, n_group=8,
+                                   topk_group=3),
+    "grouped_e256_g8_keep4_softmax": custom(T=90, hidden_size=128, num_experts=256,
+                                            num_experts_per_tok=8, moe_intermediate_size=64,
+                                            num_shared_experts=0, n_group=8, topk_group=4,
+                                            score_func="softmax", route_scale=2.5),
+    "grouped_pairs_keep1": custom(T=33, hidden_size=64, num_experts=12, num_experts_per_tok=2,
+                                  moe_intermediate_size=64, num_shared_experts=1, n_group=6,
+                                  topk_group=1),
 }
 
 
@@ -107,7 +118,8 @@ def run_stages(dev: Dev, deterministic=False):
 def check_routing(cfg, inp, st):
     k = cfg["num_experts_per_tok"]
     s, keys, idx, w = O.route(st["logits"], inp.expert_bias, k, cfg["score_func"],
-                              bool(cfg["route_norm"]), cfg["route_scale"])
+                              bool(cfg["route_norm"]), cfg["route_scale"],
+                              cfg.get("n_group", 1), cfg.get("topk_group", 1))
     assert np.array_equal(st["idx"], idx), "routing indices differ from the oracle"
     assert np.max(np.abs(st["w"] - w) / np.maximum(np.abs(w), 1e-30)) <= 1e-6
     return s, keys, idx, w
@@ -205,6 +217,31 @@ def test_route_exact_ties_from_host_logits(E, k, score_func):
     _, keys, ridx, rw = O.route(L, b, k, score_func, True, cfg["route_scale"])
     assert O.boundary_gap(keys, k) == 0.0
     assert np.array_equal(idx.view(T, k).cpu().numpy(), ridx)
+    assert np.allclose(w.view(T, k).cpu().numpy(), rw, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("E,k,n_group,topk_group", [(256, 8, 8, 4), (64, 6, 8, 3), (12, 2, 6, 1),
+                                                    (1024, 32, 64, 8), (96, 5, 32, 3)])
+def test_route_grouped_exact_ties_from_host_logits(E, k, n_group, topk_group):
+    """Host-built fp32 logits from four values, so keys and group scores tie
+    exactly: the kept groups and the selection match the oracle bit for bit
+    (lower group, then lower expert index, wins)."""
+    cfg = dict(synth.layer_keys(EDGE["e300_k8"]), num_experts=E, num_experts_per_tok=k,
+               n_group=n_group, topk_group=topk_group)
+    T = 64
+    rng = np.random.default_rng(E + k)
+    L = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[rng.choice(E, min(20, E // 2), replace=False)] = 0.25
+    idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, T, torch.from_numpy(L).cuda(), torch.from_numpy(b).cuda(), idx, w)
+    torch.cuda.synchronize()
+    _, keys, ridx, rw = O.route(L, b, k, "sigmoid", True, cfg["route_scale"], n_group, topk_group)
+    got = idx.view(T, k).cpu().numpy()
+    assert np.array_equal(got, ridx)
+    gs = E // n_group
+    assert all(len({int(e) // gs for e in row}) <= topk_group for row in got)
     assert np.allclose(w.view(T, k).cpu().numpy(), rw, rtol=1e-6, atol=0)
 
 
