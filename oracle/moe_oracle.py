@@ -45,6 +45,10 @@ checkpoint's MXFP8 export), read as the OCP Microscaling (MX) v1.0 format:
 every 32 consecutive inputs of a weight row share one E8M0 scale 2^(e-127)
 and each element is an OCP FP8 E4M3 code; a weight is code value x scale.
 The layer then runs unchanged on those exact values (mx_dequantize).
+The 4-bit weights of the Trinity checkpoints (mlxcel #845 "Checkpoint
+confirmed" and "Checkpoint weight layout": 4 bits per weight, the router at
+8) have no format on the pages; they are read as OCP MXFP4: E2M1 elements,
+two per byte, with the same E8M0 scales (the router stays fp32).
 
 Readings where the pages are silent are listed in the design notes: the bias
 is added to the post-sigmoid scores; normalise then scale; no epsilon in the
@@ -72,7 +76,7 @@ def as_f64(a: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# MXFP8 weights (OCP MX v1.0: E4M3 elements, one E8M0 scale per 32 inputs)
+# MX weights (OCP MX v1.0: E4M3 or E2M1 elements, one E8M0 scale per 32 inputs)
 
 MX_BLOCK = 32
 
@@ -95,29 +99,60 @@ def e8m0_value(e: np.ndarray) -> np.ndarray:
     return np.where(e == 255, np.nan, np.exp2(e - 127.0))
 
 
-def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Weight values of one MXFP8 matrix: codes [N, K] (uint8), scales
-    [K/32, N] (uint8, block-major: the scales of all N rows for each block of
-    32 inputs) -> float64 [N, K], w[n, k] = e4m3(codes[n, k]) * 2^(s[k/32, n] - 127)."""
-    N, K = codes.shape
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP4 E2M1 codes (the low four bits): sign bit 3, two
+    exponent bits (bias 1), one mantissa bit; exponent field 0 is subnormal
+    (m/2); no infinities or NaN (largest 6)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    ef = (c >> 1) & 0x3
+    m = (c & 0x1).astype(F64)
+    mag = np.where(ef == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(ef.astype(F64) - 1.0))
+    return sign * mag
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """[N, K/2] bytes -> [N, K] 4-bit codes: input 2j is the low nibble of
+    byte j, input 2j+1 the high nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, elem: str = "e4m3") -> np.ndarray:
+    """Weight values of one MX matrix -> float64 [N, K], with scales [K/32, N]
+    (uint8, block-major: the scales of all N rows for each block of 32
+    inputs): w[n, k] = element(n, k) * 2^(s[k/32, n] - 127).
+    elem "e4m3" (MXFP8): codes [N, K], one byte per input;
+    elem "e2m1" (MXFP4): codes [N, K/2], two inputs per byte (unpack_fp4)."""
+    if elem == "e2m1":
+        vals = e2m1_value(unpack_fp4(codes))
+    elif elem == "e4m3":
+        vals = e4m3_value(codes)
+    else:
+        raise ValueError(f"unknown MX element format {elem!r}")
+    K = vals.shape[1]
     sc = e8m0_value(scales).T                                   # [N, K/32]
-    return e4m3_value(codes) * np.repeat(sc, MX_BLOCK, axis=1)[:, :K]
+    return vals * np.repeat(sc, MX_BLOCK, axis=1)[:, :K]
 
 
 class MxStacked:
-    """Stacked MXFP8 matrices ([E, N, K] codes, [E, K/32, N] scales) whose
-    item e is the float64 dequantised matrix of expert e (computed on access,
-    one expert at a time)."""
+    """Stacked MX matrices ([E, N, K] MXFP8 codes or [E, N, K/2] packed MXFP4
+    codes, [E, K/32, N] scales) whose item e is the float64 dequantised
+    matrix of expert e (computed on access, one expert at a time)."""
 
-    def __init__(self, codes: np.ndarray, scales: np.ndarray):
-        self.codes, self.scales = codes, scales
-        self.shape = codes.shape
+    def __init__(self, codes: np.ndarray, scales: np.ndarray, elem: str = "e4m3"):
+        self.codes, self.scales, self.elem = codes, scales, elem
+        E, N, Kc = codes.shape
+        self.shape = (E, N, 2 * Kc if elem == "e2m1" else Kc)
 
     def __len__(self):
         return self.codes.shape[0]
 
     def __getitem__(self, e):
-        return mx_dequantize(self.codes[e], self.scales[e])
+        return mx_dequantize(self.codes[e], self.scales[e], self.elem)
 
 
 # ----------------------------------------------------------------------------

@@ -612,6 +612,79 @@ def test_mx_layer_runs_on_the_dequantised_values():
 
 
 # --------------------------------------------------------------------------
+# MXFP4 expert weights (OCP MX v1.0 E2M1; the 4-bit Trinity checkpoints of
+# mlxcel #845 "Checkpoint confirmed")
+
+def test_e2m1_hand_values():
+    g = _gold("mxfp4_hand_example.json")
+    for code, val in g["e2m1"]:
+        got = O.e2m1_value(np.array([int(code, 16)], np.uint8))[0]
+        assert got == val and np.signbit(got) == np.signbit(val), code
+    # only the low nibble is a code
+    assert O.e2m1_value(np.array([0xF7], np.uint8))[0] == 6.0
+
+
+def test_e2m1_values_are_exact_in_e4m3():
+    """Every E2M1 value is an E4M3 value (both OCP minifloats): decoding the
+    E4M3 code with the same sign, exponent (rebiased 1 -> 7) and mantissa
+    (shifted into the top bit) gives the same number for the normal codes."""
+    for c in range(16):
+        ef, m, sgn = (c >> 1) & 3, c & 1, c >> 3
+        if ef == 0:
+            continue
+        e4 = (sgn << 7) | ((ef - 1 + 7) << 3) | (m << 2)
+        assert O.e2m1_value(np.array([c], np.uint8))[0] == O.e4m3_value(np.array([e4], np.uint8))[0]
+
+
+def test_mxfp4_dequantize_nibble_order_and_block_major_scales():
+    d = _gold("mxfp4_hand_example.json")["dequant"]
+    packed = np.full((2, 32), int(d["bytes_fill"], 16), np.uint8)
+    for r, j, c in d["bytes_set"]:
+        packed[r, j] = int(c, 16)
+    w = O.mx_dequantize(packed, np.array(d["scales"], np.uint8), "e2m1")
+    assert w.shape == (2, 64)
+    for row in d["rows"]:
+        r = row["row"]
+        expect = np.concatenate([np.full(32, row["first32"]), np.full(32, row["last32"])])
+        for k, v in row.get("at", []):
+            expect[k] = v
+        assert np.array_equal(w[r], expect), r
+
+
+def test_mxfp4_stacked_layer_equals_dense():
+    """The layer with stacked MXFP4 experts (two inputs per byte, lazy
+    per-expert dequantisation, packed shared slot included) equals the layer
+    given the dequantised matrices as plain float64 tensors."""
+    cfg = _tiny_cfg(hidden_size=64, moe_intermediate_size=64, shared_packed=1,
+                    hidden_act="swigluoai", route_scale=2.0)
+    rng = np.random.default_rng(5)
+    T, H, E, I = 6, 64, 3, 64
+    codes = {k: rng.integers(0, 256, (E + 1, n, kk // 2), dtype=np.uint8)
+             for k, (n, kk) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I)))}
+    scales = {k: rng.integers(122, 128, (E + 1, 2 * c.shape[2] // 32, c.shape[1]), dtype=np.uint8)
+              for k, c in codes.items()}
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    st = {k: O.MxStacked(codes[k], scales[k], "e2m1") for k in codes}
+    assert st["gate"].shape == (E + 1, I, H) and st["down"].shape == (E + 1, H, I)
+    mx = synth.MoeInputs(cfg=cfg, x=x, w_router=wr, expert_bias=b,
+                         w_gate=st["gate"], w_up=st["up"], w_down=st["down"])
+    dense = synth.MoeInputs(cfg=cfg, x=x, w_router=wr, expert_bias=b,
+                            w_gate=np.stack([st["gate"][e] for e in range(E + 1)]),
+                            w_up=np.stack([st["up"][e] for e in range(E + 1)]),
+                            w_down=np.stack([st["down"][e] for e in range(E + 1)]))
+    a, d = O.moe_forward(mx, cfg), O.moe_forward(dense, cfg)
+    assert np.array_equal(a["idx"], d["idx"]) and np.array_equal(a["out"], d["out"])
+    # element (n, k) of expert e by hand from its byte and scale
+    e, n, k = 2, 5, 37
+    byte = int(codes["gate"][e, n, k // 2])
+    nib = byte & 0xF if k % 2 == 0 else byte >> 4
+    val = O.e2m1_value(np.array([nib], np.uint8))[0] * 2.0 ** (int(scales["gate"][e, k // 32, n]) - 127)
+    assert st["gate"][e][n, k] == val
+
+
+# --------------------------------------------------------------------------
 # group-limited routing (mlxcel #845 "Routing detail": group routing, n_group;
 # the rule read from the DeepSeek MoE family the page derives AFMoE from)
 

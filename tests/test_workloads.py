@@ -84,3 +84,58 @@ def test_mxfp8_quantiser():
     assert np.array_equal(synth.f32_to_bf16_bits(tmp), b.w_gate[5])
     g, gs = synth.quantize_mxfp8(tmp)
     assert np.array_equal(a.w_gate[5], g) and np.array_equal(a.mx["gate"][5], gs)
+
+
+def test_mxfp4_quantiser():
+    """OCP rule (scale 2^(floor(log2 amax) - 2), clamp to +-6, nearest E2M1
+    value, ties to the even code) against the hand-worked block and against
+    a brute-force nearest-value search; input 2j in the low nibble."""
+    import json
+    import os
+    from oracle import moe_oracle as O
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "mxfp4_hand_example.json")))["quantise"]
+    w = np.zeros((1, 32), np.float32)
+    w[0, :5] = g["inputs"]
+    p, sc = synth.quantize_mxfp4(w)
+    assert p.shape == (1, 16) and sc.shape == (1, 1) and sc[0, 0] == g["scale_byte"]
+    codes = O.unpack_fp4(p)[0]
+    assert [int(c) for c in codes[:5]] == [int(c, 16) for c in g["codes"]]
+    assert np.all(codes[5:] == 0)
+
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((24, 256)) * 0.02).astype(np.float32)
+    w[2, 64:96] = 0.0                                   # an all-zero block
+    w[5, 0:32] = 7.0                                    # saturates: amax 7 -> scale 1, 7 -> 6
+    w[5, 0] = 6.0
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = (mags[1:] + mags[:-1]) / 2
+    w[6, 0:8] = np.r_[6.0, mids]                         # every tie, scale 2^0
+    w[6, 8:16] = -np.r_[mids[:7], 0.0]
+    p, sc = synth.quantize_mxfp4(w)
+    assert p.shape == (24, 128) and sc.shape == (8, 24)
+    amax = np.abs(w.astype(np.float64)).reshape(24, 8, 32).max(2)
+    nz = amax > 0
+    assert np.array_equal(sc.T[nz].astype(np.int64),
+                          np.floor(np.log2(amax[nz])).astype(np.int64) - 2 + 127)
+    assert np.all(sc.T[~nz] == 0)
+    v = w.astype(np.float64).reshape(24, 8, 32) / np.exp2(sc.T.astype(np.float64) - 127)[:, :, None]
+    a = np.minimum(np.abs(v), 6.0)
+    dist = np.abs(a[..., None] - mags)
+    best = dist.min(-1, keepdims=True)
+    cand = dist == best                                  # one or two nearest codes
+    even = cand & (np.arange(8) % 2 == 0)
+    ref = np.where(even.any(-1), np.argmax(even, -1), np.argmax(cand, -1))
+    ref = (ref | np.where(np.signbit(v), 8, 0)).reshape(24, 256)
+    got = O.unpack_fp4(p)
+    assert np.array_equal(got, ref)
+    assert np.all(got[5, :32] & 7 == 7)
+    cfg = synth.config("trinity_nano_decode_T32_mxfp4")
+    a4 = synth.generate(cfg)
+    a8 = synth.generate(synth.config("trinity_nano_decode_T32_mxfp8"))
+    assert np.array_equal(a4.x, a8.x) and a4.w_gate.shape == (128, 256, 512)
+    assert a4.mx["down"].shape == (128, 256 // 32, 1024) and a4.ws_down.shape == (1, 1024, 128)
+    tmp = np.empty((256, 1024), np.float32)
+    synth._fill_normal(tmp, synth._stream(0, synth.TID_GATE, 5), cfg["w_std"], False)
+    q, qs = synth.quantize_mxfp4(tmp)
+    assert np.array_equal(a4.w_gate[5], q) and np.array_equal(a4.mx["gate"][5], qs)

@@ -128,6 +128,24 @@ CONFIGS: dict[str, dict] = {
         moe_intermediate_size=256, num_shared_experts=1,
         shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
         route_scale=2.826, router_bf16_values=False, weight_format="mxfp8"),
+    # 4-bit expert weights (the Trinity checkpoints are 4-bit, router at 8
+    # bits; read as MXFP4), and the M3 decode layer with the same format
+    "trinity_nano_decode_T32_mxfp4": _cfg(
+        T=32, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
+        moe_intermediate_size=256, num_shared_experts=1,
+        shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
+        route_scale=2.826, router_bf16_values=False, weight_format="mxfp4"),
+    "trinity_nano_prefill_T8192_mxfp4": _cfg(
+        T=8192, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
+        moe_intermediate_size=256, num_shared_experts=1,
+        shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
+        route_scale=2.826, router_bf16_values=False, weight_format="mxfp4"),
+    "minimax_m3_decode_T64_mxfp4": _cfg(
+        T=64, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
+        moe_intermediate_size=3072, num_shared_experts=1,
+        shared_intermediate_size=3072, shared_packed=1, dtype="bf16",
+        bias_limit=0.05, w_std=0.01, route_scale=2.0, hidden_act="swigluoai",
+        norm_add_one=1, weight_format="mxfp4"),
 }
 
 
@@ -220,10 +238,11 @@ class MoeInputs:
     ws_up: np.ndarray | None = None
     ws_down: np.ndarray | None = None  # [S, H, I_s]
     meta: dict = field(default_factory=dict)
-    # MXFP8 expert weights: the w_* / ws_* arrays hold E4M3 codes (uint8) and
-    # mx holds their E8M0 scales, block-major: [E_tot or S, K/32, N] for a
-    # stack of [N, K] matrices (keys gate, up, down, shared_gate, shared_up,
-    # shared_down)
+    # MX expert weights: the w_* / ws_* arrays hold E4M3 codes (MXFP8, uint8
+    # [., N, K]) or packed E2M1 codes (MXFP4, uint8 [., N, K/2], input 2j in
+    # the low nibble of byte j) and mx holds their E8M0 scales, block-major:
+    # [E_tot or S, K/32, N] for a stack of [N, K] matrices (keys gate, up,
+    # down, shared_gate, shared_up, shared_down)
     mx: dict | None = None
 
 
@@ -248,7 +267,11 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
                 cfg["shared_intermediate_size"])
     bf16 = cfg["dtype"] == "bf16"
     wdt = np.uint16 if bf16 else np.float32
-    mx = cfg.get("weight_format", "dtype") == "mxfp8"
+    wf = cfg.get("weight_format", "dtype")
+    if wf not in ("dtype", "mxfp8", "mxfp4"):
+        raise ValueError(f"unknown weight_format {wf!r}")
+    mx = wf != "dtype"
+    kdiv = 2 if wf == "mxfp4" else 1      # MXFP4: two inputs per byte
     xdt = wdt
     std = cfg["w_std"]
 
@@ -285,20 +308,21 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
     jobs = [(_xblock, b) for b in range(nblk)]
 
     def _matrix(arr, sc, tid, e):
-        # one expert's matrix: fp32 draws, then bf16 rounding or MXFP8 quantisation
+        # one expert's matrix: fp32 draws, then bf16 rounding or MX quantisation
         if sc is None:
             _fill_normal(arr[e], _stream(seed, tid, e), std, bf16)
             return
-        tmp = np.empty(arr.shape[1:], np.float32)
+        n, kc = arr.shape[1:]
+        tmp = np.empty((n, kc * kdiv), np.float32)
         _fill_normal(tmp, _stream(seed, tid, e), std, False)
-        arr[e], sc[e] = quantize_mxfp8(tmp)
+        arr[e], sc[e] = (quantize_mxfp4 if kdiv == 2 else quantize_mxfp8)(tmp)
 
     if experts:
         Etot = E + (1 if cfg["shared_packed"] else 0)
         edt = np.uint8 if mx else wdt
-        inp.w_gate = np.empty((Etot, I, H), edt)
-        inp.w_up = np.empty((Etot, I, H), edt)
-        inp.w_down = np.empty((Etot, H, I), edt)
+        inp.w_gate = np.empty((Etot, I, H // kdiv), edt)
+        inp.w_up = np.empty((Etot, I, H // kdiv), edt)
+        inp.w_down = np.empty((Etot, H, I // kdiv), edt)
         if mx:
             inp.mx = {"gate": np.empty((Etot, H // 32, I), np.uint8),
                       "up": np.empty((Etot, H // 32, I), np.uint8),
@@ -309,9 +333,9 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
             for e in range(Etot):
                 jobs.append((lambda e, arr=arr, sc=scl(key), tid=tid: _matrix(arr, sc, tid, e), e))
         if S > 0 and not cfg["shared_packed"]:
-            inp.ws_gate = np.empty((S, Is, H), edt)
-            inp.ws_up = np.empty((S, Is, H), edt)
-            inp.ws_down = np.empty((S, H, Is), edt)
+            inp.ws_gate = np.empty((S, Is, H // kdiv), edt)
+            inp.ws_up = np.empty((S, Is, H // kdiv), edt)
+            inp.ws_down = np.empty((S, H, Is // kdiv), edt)
             if mx:
                 inp.mx.update({"shared_gate": np.empty((S, H // 32, Is), np.uint8),
                                "shared_up": np.empty((S, H // 32, Is), np.uint8),
@@ -364,6 +388,37 @@ def quantize_mxfp8(w: np.ndarray):
     code = np.where(a >= np.float32(2.0 ** -6), normal, sub)
     code |= (v.view(np.uint32) >> 24) & np.uint32(0x80)
     return code.astype(np.uint8).reshape(N, K), np.ascontiguousarray(sbyte.T)
+
+
+# MXFP4 (OCP Microscaling v1.0: E2M1 elements, one E8M0 scale per 32 inputs)
+
+# midpoints between neighbouring E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """float32 [N, K] -> (packed codes uint8 [N, K/2], scales uint8 [K/32, N]).
+
+    Per block of 32 inputs of a row: scale 2^(floor(log2 amax) - 2) (2 is
+    E2M1's largest exponent); each element, divided by the scale (exact) and
+    clamped to +-6, goes to the nearest E2M1 magnitude, ties to the even code
+    (code i + 1 past midpoint i; at the midpoint only when i + 1 is even); the
+    sign is bit 3. Input 2j is the low nibble of byte j, input 2j+1 the high."""
+    N, K = w.shape
+    blk = np.ascontiguousarray(w, dtype=np.float32).reshape(N, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
+    ex = np.where(amax > 0, ex - 1, -125)        # floor(log2 amax); zero block: scale byte 0
+    sbyte = np.clip(ex - 2 + 127, 0, 254).astype(np.uint8)
+    v = blk * np.ldexp(np.float32(1.0), 127 - sbyte.astype(np.int32))[:, :, None]
+    a = np.minimum(np.abs(v), np.float32(6.0))
+    code = np.zeros(a.shape, np.uint8)
+    for i, m in enumerate(_E2M1_MID):
+        code += (a > m) | ((a == m) & ((i + 1) % 2 == 0))
+    code |= ((v.view(np.uint32) >> 28) & np.uint32(0x8)).astype(np.uint8)
+    code = code.reshape(N, K)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return np.ascontiguousarray(packed, dtype=np.uint8), np.ascontiguousarray(sbyte.T)
 
 
 def norm_weights(cfg: dict) -> dict:
