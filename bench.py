@@ -47,7 +47,8 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
     Is = cfg["shared_intermediate_size"] or I
     bx = 2 if cfg["dtype"] == "bf16" else 4
     # expert weight bytes per weight: MXFP8 is one code plus 1/32 of a scale byte
-    bw = 1 + 1 / 32 if cfg.get("weight_format") == "mxfp8" else bx
+    # bytes per expert weight: MX codes plus one E8M0 scale byte per 32
+    bw = {"mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}.get(cfg.get("weight_format"), bx)
     flops = T * (2 * H * E + 6 * k * H * I + 6 * S * H * Is)
     touched = E if idx is None else int(np.unique(idx).size)
     bytes_ = touched * 3 * H * I * bw + S * 3 * H * Is * bw + 4 * E * H + 2 * T * H * bx + 4 * E
@@ -214,10 +215,11 @@ def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     wts = {n: getattr(inp, n) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
-    if inp.mx is not None:  # MXFP8 stacks, dequantised one expert at a time
+    if inp.mx is not None:  # MX stacks, dequantised one expert at a time
         keys = {"w_gate": "gate", "w_up": "up", "w_down": "down", "ws_gate": "shared_gate",
                 "ws_up": "shared_up", "ws_down": "shared_down"}
-        wts = {n: (O.MxStacked(a, inp.mx[keys[n]]) if a is not None else None)
+        elem = "e2m1" if cfg.get("weight_format") == "mxfp4" else "e4m3"
+        wts = {n: (O.MxStacked(a, inp.mx[keys[n]], elem) if a is not None else None)
                for n, a in wts.items()}
     sub = synth.MoeInputs(cfg=dict(cfg, T=sample_tokens), x=inp.x[:sample_tokens],
                           w_router=inp.w_router, expert_bias=inp.expert_bias, **wts)
@@ -523,7 +525,8 @@ def main():
                    "num_experts_per_tok": k, "moe_intermediate_size": I,
                    "num_shared_experts": S, "shared_intermediate_size": Is,
                    "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"],
-                   "expert_weights": ("mxfp8" if cfg.get("weight_format") == "mxfp8"
+                   "expert_weights": (cfg["weight_format"]
+                                      if cfg.get("weight_format", "dtype") != "dtype"
                                       else cfg["dtype"]),
                    "combine": args.combine, "graph": args.graph, "entry": "moe_layer_forward"},
         "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,

@@ -92,12 +92,27 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *                      tensors keep the weights' shapes and layout; the
  *                      scales are passed in moe_mx_scales. Needs dtype bf16
  *                      (activations stay bf16, accumulation fp32; else
- *                      MOE_ERR_UNSUPPORTED). */
-typedef enum { MOE_WEIGHTS_DTYPE = 0, MOE_WEIGHTS_MXFP8 = 1 } moe_weight_format;
+ *                      MOE_ERR_UNSUPPORTED).
+ *   MOE_WEIGHTS_MXFP4  OCP MX v1.0 MXFP4, read as the format of the 4-bit
+ *                      Trinity checkpoints (mlxcel #845 "Checkpoint
+ *                      confirmed", "Checkpoint weight layout": 4-bit experts,
+ *                      no format given): each weight is one E2M1 code (sign,
+ *                      2 exponent bits with bias 1, 1 mantissa bit: values
+ *                      +-{0, .5, 1, 1.5, 2, 3, 4, 6}), two per byte along
+ *                      the weight row, input 2j in the low nibble of byte j,
+ *                      so an [N, K] matrix is [N, K/2] bytes (gate, up
+ *                      [E_tot, I, H/2], down [E_tot, H, I/2], shared
+ *                      likewise); the same E8M0 scales per 32 inputs in
+ *                      moe_mx_scales. Needs dtype bf16, as MXFP8. */
+typedef enum {
+  MOE_WEIGHTS_DTYPE = 0,
+  MOE_WEIGHTS_MXFP8 = 1,
+  MOE_WEIGHTS_MXFP4 = 2
+} moe_weight_format;
 
-/* E8M0 scales of MXFP8 expert weights, block-major: for an [N, K] weight
- * matrix the scales are [K/32, N] (for every block of 32 inputs, the scales
- * of all N rows), stacked like the weights:
+/* E8M0 scales of MX (MXFP8, MXFP4) expert weights, block-major: for an
+ * [N, K] weight matrix the scales are [K/32, N] (for every block of 32
+ * inputs, the scales of all N rows), stacked like the weights:
  *   gate, up      [E_tot, H/32, I]     down        [E_tot, I/32, H]
  *   shared_gate,  [S, H/32, I_s]       shared_down [S, I_s/32, H]
  *   shared_up                          (NULL when S == 0 or packed: the
@@ -190,7 +205,7 @@ moe_status moe_permute(const moe_config* cfg, int64_t T,
  *   h_shared[t, s*I_s:(s+1)*I_s] = act(x[t] . Ws_g[s]^T, x[t] . Ws_u[s]^T)
  *   x [T,H]; w_gate, w_up [E_tot,I,H]; ws_gate, ws_up [S,I_s,H] (NULL when
  *   S == 0 or the shared expert is packed: then slot E of w_gate/w_up is
- *   used); mx: host pointer to the scales when weight_format is MXFP8
+ *   used); mx: host pointer to the scales when weight_format is MXFP8 or MXFP4
  *   (ignored otherwise, may be NULL); h [T*k, I] out; h_shared [T, S*I_s]
  *   out (NULL iff S == 0). */
 moe_status moe_grouped_gate_up_swiglu(
@@ -232,7 +247,7 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
  * down + combine, cast.
  *   x [T,H] dtype; w_router [E,H] fp32; expert_bias [E] fp32 or NULL;
  *   w_gate, w_up, w_down stacked experts; ws_* separate shared experts or
- *   NULL; mx: scales of MXFP8 weights (host pointer) or NULL;
+ *   NULL; mx: scales of MX weights (host pointer) or NULL;
  *   router_logits_in [T,E] or NULL (when given, the router GEMM is
  *   skipped and these logits are routed); router_logits_out [T,E] or NULL;
  *   topk_idx_out [T,k] / topk_w_out [T,k] or NULL; out [T,H] dtype.

@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLUOAI = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MXFP8 = 0, 1
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MXFP8, MOE_WEIGHTS_MXFP4 = 0, 1, 2
 
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
@@ -57,7 +57,7 @@ class MoeConfig(ctypes.Structure):
 
 class MoeMxScales(ctypes.Structure):
     """Mirror of moe_mx_scales (include/moe.h): device pointers of the E8M0
-    scale tensors of MXFP8 expert weights."""
+    scale tensors of MX (MXFP8, MXFP4) expert weights."""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")]
 
@@ -95,7 +95,7 @@ def make_norm_config(norm) -> MoeNormConfig:
 _SCORE = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 _ACT = {"silu": MOE_ACT_SILU, "swigluoai": MOE_ACT_SWIGLUOAI}
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16}
-_WF = {"dtype": MOE_WEIGHTS_DTYPE, "mxfp8": MOE_WEIGHTS_MXFP8}
+_WF = {"dtype": MOE_WEIGHTS_DTYPE, "mxfp8": MOE_WEIGHTS_MXFP8, "mxfp4": MOE_WEIGHTS_MXFP4}
 
 
 def make_config(cfg) -> MoeConfig:
@@ -265,7 +265,7 @@ def moe_permute(cfg, T, topk_idx, expert_offsets, sorted_rows, row_pos, ws, stre
 
 def moe_grouped_gate_up_swiglu(cfg, T, x, w_gate, w_up, ws_gate, ws_up, expert_offsets,
                                sorted_rows, h, h_shared, ws, stream=None, mx=None):
-    """mx: MXFP8 scales (dict of device tensors or MoeMxScales), in the C
+    """mx: MX scales (dict of device tensors or MoeMxScales), in the C
     argument list after ws_up."""
     c = make_config(cfg)
     m = make_mx_scales(mx)
@@ -277,7 +277,7 @@ def moe_grouped_gate_up_swiglu(cfg, T, x, w_gate, w_up, ws_gate, ws_up, expert_o
 
 def moe_grouped_down(cfg, T, h, w_down, h_shared, ws_down, expert_offsets, sorted_rows, topk_w,
                      acc, y_perm, ws, stream=None, mx=None):
-    """mx: MXFP8 scales, in the C argument list after ws_down."""
+    """mx: MX scales, in the C argument list after ws_down."""
     c = make_config(cfg)
     m = make_mx_scales(mx)
     _need(acc, T * c.hidden_size, "acc")
@@ -297,7 +297,7 @@ def moe_combine(cfg, T, acc, y_perm, row_pos, topk_w, out, stream=None):
 def moe_layer_forward(cfg, T, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                       ws_down, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
                       out, deterministic, ws, stream=None, mx=None):
-    """mx: MXFP8 scales, in the C argument list after ws_down."""
+    """mx: MX scales, in the C argument list after ws_down."""
     c = make_config(cfg)
     m = make_mx_scales(mx)
     k = c.num_experts_per_tok
@@ -347,7 +347,7 @@ def moe_block_workspace_size(cfg, T: int) -> int:
 def moe_block_forward(cfg, norm, T, h, pre_norm_w, post_norm_w, w_router, expert_bias, w_gate,
                       w_up, w_down, ws_gate, ws_up, ws_down, router_logits_out, topk_idx_out,
                       topk_w_out, out, deterministic, ws, stream=None, mx=None):
-    """mx: MXFP8 scales, in the C argument list after ws_down."""
+    """mx: MX scales, in the C argument list after ws_down."""
     c = make_config(cfg)
     m = make_mx_scales(mx)
     n = make_norm_config(norm)

@@ -17,8 +17,8 @@ struct Dims {
   int64_t T;
   int H, E, k, S, I, Is, packed, dtype;
   size_t es;   // element size of dtype tensors
-  int fp8;     // MXFP8 expert weights
-  size_t wes;  // element size of expert weights (1 for MXFP8)
+  int wfmt;    // expert weight format (WF_DTYPE, WF_MXFP8, WF_MXFP4)
+  int wbits;   // bits per expert weight (dtype: 8 * es; MXFP8 8; MXFP4 4)
 };
 
 constexpr int64_t kMaxTokens = 1 << 24;
@@ -55,7 +55,8 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
         c->topk_group > c->n_group || c->num_experts_per_tok > c->topk_group * gs)
       return MOE_ERR_INVALID_ARG;
   }
-  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_MXFP8)
+  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_MXFP8 &&
+      c->weight_format != MOE_WEIGHTS_MXFP4)
     return MOE_ERR_INVALID_ARG;
   if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   d->T = T;
@@ -68,10 +69,12 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
   d->packed = c->shared_packed;
   d->dtype = c->dtype;
   d->es = c->dtype == MOE_BF16 ? 2 : 4;
-  d->fp8 = c->weight_format == MOE_WEIGHTS_MXFP8;
-  d->wes = d->fp8 ? 1 : d->es;
-  // MXFP8 weights take bf16 activations
-  if (d->fp8 && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  d->wfmt = c->weight_format == MOE_WEIGHTS_MXFP8   ? WF_MXFP8
+            : c->weight_format == MOE_WEIGHTS_MXFP4 ? WF_MXFP4
+                                                    : WF_DTYPE;
+  d->wbits = d->wfmt == WF_MXFP8 ? 8 : d->wfmt == WF_MXFP4 ? 4 : 8 * (int)d->es;
+  // MX weights take bf16 activations
+  if (d->wfmt != WF_DTYPE && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -158,12 +161,12 @@ GemmArgs base_args(const moe_config* c, const Dims& d) {
 }
 
 const void* shared_slot(const void* stacked, const Dims& d, size_t per_expert_elems) {
-  return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.wes;
+  return static_cast<const char*>(stacked) + (size_t)d.E * per_expert_elems * d.wbits / 8;
 }
 
-// MXFP8 scales: present and complete exactly when the weights are MXFP8
+// MX scales: present and complete exactly when the weights are MXFP8 or MXFP4
 moe_status check_mx(const Dims& d, const moe_mx_scales* mx, bool gate_up, bool down) {
-  if (!d.fp8) return MOE_OK;
+  if (d.wfmt == WF_DTYPE) return MOE_OK;
   if (!mx) return MOE_ERR_INVALID_ARG;
   if (gate_up && (!mx->gate || !mx->up)) return MOE_ERR_INVALID_ARG;
   if (down && !mx->down) return MOE_ERR_INVALID_ARG;
@@ -183,7 +186,7 @@ const uint8_t* scale_slot(const uint8_t* stacked, const Dims& d, size_t per_expe
 // K-steps in flight per compute unit. MOE_GEMM_TILE=32 or =128 forces one
 // kernel (a testing knob; 32 still needs bf16 and gemm_decode_fits).
 bool use_decode(const Dims& d) {
-  if (d.dtype != MOE_BF16 || !gemm_decode_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
+  if (d.dtype != MOE_BF16 || !gemm_decode_fits(d.T, d.H, d.I, d.k, d.S, d.Is, d.wfmt)) return false;
   if (const char* e = std::getenv("MOE_GEMM_TILE")) {
     if (std::strcmp(e, "128") == 0) return false;
     if (std::strcmp(e, "32") == 0) return true;
@@ -198,8 +201,8 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
                       const moe_mx_scales* mx, const int32_t* offsets,
                       const int32_t* sorted_rows, void* h, void* h_shared, hipStream_t st) {
   GemmArgs g = base_args(c, d);
-  if (d.fp8) {
-    g.fp8 = 1;
+  if (d.wfmt != WF_DTYPE) {
+    g.wfmt = d.wfmt;
     g.sw0 = mx->gate;
     g.sw1 = mx->up;
     const size_t per = (size_t)(d.H / 32) * d.I;
@@ -238,8 +241,8 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
                    const int32_t* offsets, const int32_t* sorted_rows, const float* topk_w,
                    float* acc, void* y_perm, hipStream_t st) {
   GemmArgs g = base_args(c, d);
-  if (d.fp8) {
-    g.fp8 = 1;
+  if (d.wfmt != WF_DTYPE) {
+    g.wfmt = d.wfmt;
     g.sw0 = mx->down;
     g.sws0 = d.packed ? scale_slot(mx->down, d, (size_t)(d.I / 32) * d.H) : mx->shared_down;
   }
@@ -552,6 +555,6 @@ const char* moe_status_string(moe_status s) {
   return "unknown moe_status";
 }
 
-const char* moe_build_info(void) { return "libmoe 0.1 gfx950 (bf16/fp32 MFMA, MXFP8 weights)"; }
+const char* moe_build_info(void) { return "libmoe 0.1 gfx950 (bf16/fp32 MFMA, MXFP8 and MXFP4 weights)"; }
 
 }  // extern "C"

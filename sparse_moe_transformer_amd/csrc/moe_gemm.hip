@@ -45,6 +45,12 @@
 // the codes into bf16 with the scaled conversion (exact for these values)
 // and runs the bf16 MFMAs; per step the LDS moves a third less than with
 // bf16 weights (stage writes 33 KiB, fragment reads 64 KiB).
+//
+// MXFP4 expert weights (E2M1 codes, two per byte, input 2j in the low nibble
+// of byte j; the same scales): a weight row holds 32 bytes per K-step (2
+// chunks, chunk c of row r at c ^ ((r >> 3) & 1)), so chunk q is exactly
+// lane half q's 32 inputs and one scale block; sub-step s takes its dword s
+// (eight codes) through the scaled fp4 conversion.
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
@@ -61,7 +67,13 @@ constexpr int NTHR = 256;
 constexpr int MAX_EXPERTS = 1024;
 constexpr int LOADS_BF16 = 12;  // per thread: 4 activation + 8 weight
 constexpr int LOADS_FP8 = 9;    // 4 activation + 4 weight + 1 scale
+constexpr int LOADS_FP4 = 7;    // 4 activation + 2 weight + 1 scale
 constexpr int FP8_SCALES = 1024;  // u32x4 index of the scale bytes in an MXFP8 weight stage
+constexpr int FP4_SCALES = 512;   // ... in an MXFP4 weight stage
+template <int WM>
+constexpr int loads_of() { return WM == WF_MXFP8 ? LOADS_FP8 : WM == WF_MXFP4 ? LOADS_FP4 : LOADS_BF16; }
+template <int WM>
+constexpr int scales_at() { return WM == WF_MXFP4 ? FP4_SCALES : FP8_SCALES; }
 
 template <typename T>
 struct Elem;
@@ -94,6 +106,12 @@ __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int b_row_fp8(int j) {
   return (threadIdx.x >> 6) * 64 + 16 * j + ((threadIdx.x & 63) >> 2);
 }
+// MXFP4 weight rows: instruction j of wave w fills rows 64w+32j .. +31, two
+// lanes per row; chunk c of row r is stored at c ^ swz2(r)
+__device__ __forceinline__ int swz2(int row) { return (row >> 3) & 1; }
+__device__ __forceinline__ int b_row_fp4(int j) {
+  return (threadIdx.x >> 6) * 64 + 32 * j + ((threadIdx.x & 63) >> 1);
+}
 // the scale bytes a lane loads: lanes 0..31 of wave w take 4 rows from
 // 64w + 4 (l % 16) of block l / 16 (lanes 32..63 repeat them into the unused
 // half of the wave's 256-byte slot)
@@ -103,9 +121,9 @@ __device__ __forceinline__ int scale_lane_block() { return (threadIdx.x >> 4) & 
 // One tile: where its rows and weights are and how many K-steps it has.
 struct Tile {
   const char* a[4];  // activation row pointers (+ lane chunk offset), bytes
-  const char* b[8];  // weight row pointers (+ lane chunk offset), bytes (MXFP8: 4)
-  const char* s;     // MXFP8: this lane's scale bytes of the first K-step
-  int sstep;         // MXFP8: scale bytes per K-step
+  const char* b[8];  // weight row pointers (+ lane chunk offset), bytes (MXFP8: 4, MXFP4: 2)
+  const char* s;     // MX: this lane's scale bytes of the first K-step
+  int sstep;         // MX: scale bytes per K-step
   int nk;            // real K-steps
   int nk3;           // steps padded to a multiple of 3
   int kseg;          // weight K segment length in bytes (K-split of shared down)
@@ -116,11 +134,12 @@ struct Tile {
 // Load this lane's chunks for step j of tile t into LDS stage (la, lb) (the
 // zero line for padding steps j >= nk: zero codes and zero activations add
 // exactly zero).
-template <bool FP8>
+template <int WM>
 __device__ __forceinline__ void issue_stage(const Tile& t, int j, u32x4_t* la, u32x4_t* lb) {
   const bool real = j < t.nk;
   const int kb = j * KSB;
-  const int kw = FP8 ? j * (KSB / 2) : kb;  // weight bytes per step
+  // weight bytes per step
+  const int kw = WM == WF_MXFP8 ? j * (KSB / 2) : WM == WF_MXFP4 ? j * (KSB / 4) : kb;
   const int seg = kw / t.kseg;
   const long boff = (long)seg * t.bstride_kb * 1024 + (kw - seg * t.kseg);
   const char* z = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 7) * 16;
@@ -128,13 +147,19 @@ __device__ __forceinline__ void issue_stage(const Tile& t, int j, u32x4_t* la, u
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_global_load_lds(real ? t.a[q] + kb : z, la + (w * 4 + q) * 64, 16, 0, 0);
-  if (FP8) {
+  if (WM != WF_DTYPE) {
+    if (WM == WF_MXFP8) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 256 + q * 64, 16, 0, 0);
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 256 + q * 64, 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 128 + q * 64, 16, 0, 0);
+    }
     const char* zs = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 31) * 4;
     __builtin_amdgcn_global_load_lds(real ? t.s + (long)j * t.sstep : zs,
-                                     lb + FP8_SCALES + w * 16, 4, 0, 0);
+                                     lb + scales_at<WM>() + w * 16, 4, 0, 0);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -149,6 +174,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, floa
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Eight E2M1 codes (one dword, input 2b in the low nibble of byte b) ->
+// eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3))};
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -171,13 +207,43 @@ typedef floatx16_t Acc[2][4];
 // bf16: 4 sub-steps of K=16; lane l reads row l%32, chunk 2*s + l/32.
 // MXFP8 weights: lane l takes inputs 32q + 8s .. +7 (q = l/32): activation
 // chunk 4q + s, weight chunks 2q, 2q+1 and the scale of block q.
-template <typename T, int KIND, bool FP8>
+// MXFP4 weights: the same inputs; weight chunk q (dword s) and its scale.
+template <typename T, int KIND, int WM>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 5, r = lane & 31;
-  if constexpr (FP8) {
+  if constexpr (WM == WF_MXFP4) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + FP4_SCALES);
+    u32x4_t wv[4];
+    float scale[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int row = wrow<KIND>(wn, nb) + r;
+      wv[nb] = lb[row * 2 + (q ^ swz2(row))];
+      scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * q + (row & 63)]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t fa[2], fb[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + r;
+        fa[mb] = __builtin_bit_cast(bf16x8_t, la[row * NCH + ((4 * q + s) ^ swz(row))]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4_t& c = wv[nb];
+        fb[nb] = fp4x8_to_bf16(s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w, scale[nb]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+    }
+  } else if constexpr (WM == WF_MXFP8) {
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + FP8_SCALES);
     u32x4_t wv[4][2];
     float scale[4];
@@ -340,7 +406,7 @@ __device__ __forceinline__ void load_tokens(const GemmArgs& g, int4 p, int (&tok
   }
 }
 
-template <typename T, int KIND, bool FP8>
+template <typename T, int KIND, int WM>
 __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& t) {
   constexpr int EPC = Elem<T>::EPC;
   const int H = g.H;
@@ -359,17 +425,28 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
       const int token = t.shared ? tok[j] : div_k(tok[j], g.k, g.kmagic);
       t.a[j] = reinterpret_cast<const char*>(x + (size_t)token * H + lane_chunk(row) * EPC);
     }
-    if (FP8) {
-      // codes [., N, H] (one byte per weight); scales [., H/32, N_s] per
-      // matrix, the shared experts' matrices of width Is one after another
+    if (WM != WF_DTYPE) {
+      // codes [., N, H] (MXFP8: one byte per weight; MXFP4: [., N, H/2]);
+      // scales [., H/32, N_s] per matrix, the shared experts' matrices of
+      // width Is one after another
       const char* wg = static_cast<const char*>(t.shared ? g.ws0 : g.w0);
       const char* wu = static_cast<const char*>(t.shared ? g.ws1 : g.w1);
-      const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * H;
+      const int rb = WM == WF_MXFP4 ? H / 2 : H;  // bytes per weight row
+      const size_t ebase = t.shared ? 0 : (size_t)t.e * g.I * rb;
+      if (WM == WF_MXFP8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = b_row_fp8(j);
-        const int n = min(t.n0 + (row & 127), t.N - 1);
-        t.b[j] = (row < 128 ? wg : wu) + ebase + (size_t)n * H + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+        for (int j = 0; j < 4; ++j) {
+          const int row = b_row_fp8(j);
+          const int n = min(t.n0 + (row & 127), t.N - 1);
+          t.b[j] = (row < 128 ? wg : wu) + ebase + (size_t)n * rb + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = b_row_fp4(j);
+          const int n = min(t.n0 + (row & 127), t.N - 1);
+          t.b[j] = (row < 128 ? wg : wu) + ebase + (size_t)n * rb + ((threadIdx.x & 1) ^ swz2(row)) * 16;
+        }
       }
       const int w = threadIdx.x >> 6;
       const int ns = t.shared ? g.Is : g.I;
@@ -379,7 +456,7 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
       const size_t mat = t.shared ? (size_t)se * (H / 32) * ns : (size_t)t.e * (H / 32) * ns;
       t.s = reinterpret_cast<const char*>(sm) + mat + (n - se * ns) + (size_t)scale_lane_block() * ns;
       t.sstep = 2 * ns;
-      t.kseg = H;
+      t.kseg = rb;
     } else {
       const T* wg = static_cast<const T*>(t.shared ? g.ws0 : g.w0);
       const T* wu = static_cast<const T*>(t.shared ? g.ws1 : g.w1);
@@ -411,22 +488,32 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
       t.a[j] = reinterpret_cast<const char*>(act + (size_t)(t.row0 + min(row, t.nrows - 1)) * Ks +
                                              lane_chunk(row) * EPC);
     }
-    if (FP8) {
+    if (WM != WF_DTYPE) {
       // scales [K/32, H]: the S shared matrices' blocks follow one another
       // along K, so K-step j of a shared tile reads blocks 2j, 2j+1
+      const int half = WM == WF_MXFP4 ? 1 : 0;  // MXFP4: two weights per byte
       const char* wd = sh ? static_cast<const char*>(g.ws0)
-                          : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I;
+                          : static_cast<const char*>(g.w0) + (((size_t)t.e * H * g.I) >> half);
+      const int rb = ldb >> half;  // bytes per weight row of a K segment
+      if (WM == WF_MXFP8) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = b_row_fp8(j);
-        t.b[j] = wd + (size_t)min(t.n0 + row, H - 1) * ldb + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+        for (int j = 0; j < 4; ++j) {
+          const int row = b_row_fp8(j);
+          t.b[j] = wd + (size_t)min(t.n0 + row, H - 1) * rb + ((threadIdx.x & 3) ^ swz4(row)) * 16;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = b_row_fp4(j);
+          t.b[j] = wd + (size_t)min(t.n0 + row, H - 1) * rb + ((threadIdx.x & 1) ^ swz2(row)) * 16;
+        }
       }
       const uint8_t* sm = sh ? g.sws0 : g.sw0 + (size_t)t.e * (g.I / 32) * H;
       const int n = min(t.n0 + scale_lane_row(), H - 4);
       t.s = reinterpret_cast<const char*>(sm) + n + (size_t)scale_lane_block() * H;
       t.sstep = 2 * H;
-      t.kseg = ldb;
-      t.bstride_kb = sh ? (int)(((long)H * g.Is) >> 10) : 0;
+      t.kseg = rb;
+      t.bstride_kb = sh ? (int)((((long)H * g.Is) >> half) >> 10) : 0;
     } else {
       const T* wd = sh ? static_cast<const T*>(g.ws0)
                        : static_cast<const T*>(g.w0) + (size_t)t.e * H * g.I;
@@ -454,13 +541,13 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
 // two ahead into that set, compute stage j.
 #define MOE_STEP(TL, J, LA, LB, NA, NB)                       \
   {                                                           \
-    wait_vmcnt<FP8 ? LOADS_FP8 : LOADS_BF16>();               \
+    wait_vmcnt<loads_of<WM>()>();                             \
     __builtin_amdgcn_s_barrier();                             \
-    issue_stage<FP8>(TL, J, NA, NB);                          \
-    compute_stage<T, KIND, FP8>(LA, LB, acc);                 \
+    issue_stage<WM>(TL, J, NA, NB);                           \
+    compute_stage<T, KIND, WM>(LA, LB, acc);                  \
   }
 
-template <typename T, int KIND, bool ATOMIC, bool FP8>
+template <typename T, int KIND, bool ATOMIC, int WM>
 __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   MOE_LDS_STAGES
   __shared__ int offs[MAX_EXPERTS + 1];
@@ -497,13 +584,13 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   int tok[4] = {0, 0, 0, 0};
   load_tokens<KIND>(g, place(0), tok);
   Tile cur, nxt;
-  make_tile<T, KIND, FP8>(g, place(0), tok, cur);
+  make_tile<T, KIND, WM>(g, place(0), tok, cur);
   load_tokens<KIND>(g, place(1), tok);
   int ep_r = 0;  // routed down epilogue: the sorted row id of row threadIdx.x
   if (KIND == DOWN_ROUTED && threadIdx.x < BM)
     ep_r = g.sorted_rows[cur.row0 + min((int)threadIdx.x, cur.nrows - 1)];
-  issue_stage<FP8>(cur, 0, lds_a0, lds_b0);
-  issue_stage<FP8>(cur, 1, lds_a1, lds_b1);
+  issue_stage<WM>(cur, 0, lds_a0, lds_b0);
+  issue_stage<WM>(cur, 1, lds_a1, lds_b1);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 5, r = lane & 31;
@@ -533,7 +620,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
       if (ATOMIC) ep_wt = g.topk_w[ep_r];
       ep_t = div_k(ep_r, g.k, g.kmagic);
     }
-    make_tile<T, KIND, FP8>(g, place(li + 1), tok, nxt);
+    make_tile<T, KIND, WM>(g, place(li + 1), tok, nxt);
     // ids of the tile after next, then (below) the next tile's first stages
     load_tokens<KIND>(g, place(li + 2), tok);
     if (KIND == DOWN_ROUTED && threadIdx.x < BM)
@@ -672,22 +759,22 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
 }
 #undef MOE_STEP
 
-// one entry per kind, so that profiles name them (FP8: MXFP8 weights)
-template <typename T, bool FP8>
+// one entry per kind, so that profiles name them (WM: the weight format)
+template <typename T, int WM>
 __global__ void __launch_bounds__(NTHR) moe_gate_up_kernel(GemmArgs g) {
-  moe_gemm_body<T, GATE_UP, false, FP8>(g);
+  moe_gemm_body<T, GATE_UP, false, WM>(g);
 }
-template <typename T, bool FP8>
+template <typename T, int WM>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_SHARED, false, FP8>(g);
+  moe_gemm_body<T, DOWN_SHARED, false, WM>(g);
 }
-template <typename T, bool ATOMIC, bool FP8>
+template <typename T, bool ATOMIC, int WM>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_ROUTED, ATOMIC, FP8>(g);
+  moe_gemm_body<T, DOWN_ROUTED, ATOMIC, WM>(g);
 }
-template <typename T, bool FP8>
+template <typename T, int WM>
 __global__ void __launch_bounds__(NTHR) moe_down_kernel(GemmArgs g) {
-  moe_gemm_body<T, DOWN_BOTH, false, FP8>(g);
+  moe_gemm_body<T, DOWN_BOTH, false, WM>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -711,55 +798,63 @@ static int num_cus() {
 
 static int grid_for(long max_tiles) { return (int)(max_tiles < num_cus() ? max_tiles : num_cus()); }
 
+// The kernel instance for the weight format and dtype: MX weights always
+// take bf16 activations (the host checks).
+#define GEMM_LAUNCH(KERN, n, g, dtype, st)                                                       \
+  do {                                                                                           \
+    const dim3 grid_(grid_for(n));                                                               \
+    if ((g).wfmt == WF_MXFP8)                                                                    \
+      hipLaunchKernelGGL((KERN<bf16_t, WF_MXFP8>), grid_, dim3(NTHR), 0, st, g);                 \
+    else if ((g).wfmt == WF_MXFP4)                                                               \
+      hipLaunchKernelGGL((KERN<bf16_t, WF_MXFP4>), grid_, dim3(NTHR), 0, st, g);                 \
+    else if ((dtype) == MOE_BF16)                                                                \
+      hipLaunchKernelGGL((KERN<bf16_t, WF_DTYPE>), grid_, dim3(NTHR), 0, st, g);                 \
+    else                                                                                         \
+      hipLaunchKernelGGL((KERN<float, WF_DTYPE>), grid_, dim3(NTHR), 0, st, g);                  \
+  } while (0)
+
+template <bool ATOMIC>
+struct RoutedKernel {
+  template <typename T, int WM>
+  static void launch(dim3 grid, const GemmArgs& g, hipStream_t st) {
+    hipLaunchKernelGGL((moe_down_routed_kernel<T, ATOMIC, WM>), grid, dim3(NTHR), 0, st, g);
+  }
+};
+
 hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
-  if (g.fp8)
-    hipLaunchKernelGGL((moe_gate_up_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else if (dtype == MOE_BF16)
-    hipLaunchKernelGGL((moe_gate_up_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else
-    hipLaunchKernelGGL((moe_gate_up_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  GEMM_LAUNCH(moe_gate_up_kernel, n, g, dtype, st);
   return hipGetLastError();
 }
 
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared;
   if (n <= 0) return hipSuccess;
-  if (g.fp8)
-    hipLaunchKernelGGL((moe_down_shared_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else if (dtype == MOE_BF16)
-    hipLaunchKernelGGL((moe_down_shared_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else
-    hipLaunchKernelGGL((moe_down_shared_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  GEMM_LAUNCH(moe_down_shared_kernel, n, g, dtype, st);
   return hipGetLastError();
 }
 
 hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
-  if (g.fp8)
-    hipLaunchKernelGGL((moe_down_kernel<bf16_t, true>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else if (dtype == MOE_BF16)
-    hipLaunchKernelGGL((moe_down_kernel<bf16_t, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
-  else
-    hipLaunchKernelGGL((moe_down_kernel<float, false>), dim3(grid_for(n)), dim3(NTHR), 0, st, g);
+  GEMM_LAUNCH(moe_down_kernel, n, g, dtype, st);
   return hipGetLastError();
+}
+
+template <bool ATOMIC>
+static void launch_routed(const GemmArgs& g, int dtype, dim3 grid, hipStream_t st) {
+  if (g.wfmt == WF_MXFP8) RoutedKernel<ATOMIC>::template launch<bf16_t, WF_MXFP8>(grid, g, st);
+  else if (g.wfmt == WF_MXFP4) RoutedKernel<ATOMIC>::template launch<bf16_t, WF_MXFP4>(grid, g, st);
+  else if (dtype == MOE_BF16) RoutedKernel<ATOMIC>::template launch<bf16_t, WF_DTYPE>(grid, g, st);
+  else RoutedKernel<ATOMIC>::template launch<float, WF_DTYPE>(grid, g, st);
 }
 
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st) {
   const long n = (long)g.mt_routed * g.nt_routed;
   if (n <= 0) return hipSuccess;
   const dim3 grid(grid_for(n));
-  if (g.fp8) {
-    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true, true>), grid, dim3(NTHR), 0, st, g);
-    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false, true>), grid, dim3(NTHR), 0, st, g);
-  } else if (dtype == MOE_BF16) {
-    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, true, false>), grid, dim3(NTHR), 0, st, g);
-    else hipLaunchKernelGGL((moe_down_routed_kernel<bf16_t, false, false>), grid, dim3(NTHR), 0, st, g);
-  } else {
-    if (atomic) hipLaunchKernelGGL((moe_down_routed_kernel<float, true, false>), grid, dim3(NTHR), 0, st, g);
-    else hipLaunchKernelGGL((moe_down_routed_kernel<float, false, false>), grid, dim3(NTHR), 0, st, g);
-  }
+  if (atomic) launch_routed<true>(g, dtype, grid, st);
+  else launch_routed<false>(g, dtype, grid, st);
   return hipGetLastError();
 }

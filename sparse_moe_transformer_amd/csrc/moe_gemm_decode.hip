@@ -33,6 +33,14 @@
 // per row and step. Codes become bf16 with the scaled conversion
 // (v_cvt_scalef32_pk_bf16_fp8: exact for these values, the scale's exponent
 // taken as the E8M0 value) and the bf16 MFMAs run unchanged.
+//
+// MXFP4 expert weights (E2M1 codes, two per byte, input 2j in the low nibble
+// of byte j; the same scales): K-steps of 128 inputs, so a weight row holds
+// 64 bytes per step in the MXFP8 64-input layout, the activation rows are
+// stored as two 128-byte halves and the step's four scale blocks ride along
+// as in the 128-input MXFP8 mode. Each 16-byte weight chunk is one scale
+// block of 32 inputs; sub-step s of lane half q takes dword s % 4 of chunk
+// 2q + s / 4 through the scaled fp4 conversion.
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
@@ -51,17 +59,30 @@ constexpr int NTHR = 256;
 // launch is a multiple of six steps.
 // Weight modes: W_BF16; W_FP8 (MXFP8, K-steps of 64 inputs: 64-byte weight
 // rows); W_FP8L (MXFP8, K-steps of 128 inputs: whole 128-byte weight rows,
-// 256-byte activation rows, the step's four scale blocks).
-constexpr int W_BF16 = 0, W_FP8 = 1, W_FP8L = 2;
+// 256-byte activation rows, the step's four scale blocks); W_FP4 (MXFP4,
+// K-steps of 128 inputs: 64-byte weight rows, 256-byte activation rows,
+// four scale blocks).
+constexpr int W_BF16 = 0, W_FP8 = 1, W_FP8L = 2, W_FP4 = 3;
+// activation rows of a K-step stored as two 128-byte halves
+template <int M>
+constexpr bool halves() { return M == W_FP8L || M == W_FP4; }
+// 64-byte weight rows per K-step (4 chunks, swz4 layout)
+template <int M>
+constexpr bool row64() { return M == W_FP8 || M == W_FP4; }
+// bytes of a weight row of K inputs
+template <int M>
+__host__ __device__ constexpr int row_bytes(int K) { return M == W_BF16 ? 2 * K : M == W_FP4 ? K / 2 : K; }
 // loads per thread per stage: activation + weight (+ scale)
 template <int M>
-constexpr int loads_of() { return M == W_BF16 ? 1 + 8 : M == W_FP8 ? 1 + 4 + 1 : 2 + 8 + 1; }
+constexpr int loads_of() {
+  return M == W_BF16 ? 1 + 8 : M == W_FP8 ? 1 + 4 + 1 : M == W_FP4 ? 2 + 4 + 1 : 2 + 8 + 1;
+}
 // u32x4 index of the scale bytes inside a stage's weight part
 template <int M>
-constexpr int scales_at() { return M == W_FP8 ? 1024 : DBR * NCH; }
+constexpr int scales_at() { return row64<M>() ? 1024 : DBR * NCH; }
 // inputs per K-step
 template <int M>
-constexpr int k_of() { return M == W_FP8L ? 128 : 64; }
+constexpr int k_of() { return halves<M>() ? 128 : 64; }
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_WG_TILES = 128;
 constexpr int EPI_GU = 16;     // vector memory ops of a gate/up epilogue (per thread)
@@ -72,12 +93,13 @@ constexpr int EPI_DN = 32;     // ... of a down epilogue
 // W_FP8L: DBR x 128 B; W_FP8: DBR x 64 B) and, for MXFP8, the step's scale
 // bytes (1 KiB), in 16-byte units.
 template <int M>
-constexpr int stage_a() { return M == W_FP8L ? 2 * DBM * NCH : DBM * NCH; }
+constexpr int stage_a() { return halves<M>() ? 2 * DBM * NCH : DBM * NCH; }
 template <int M>
 constexpr int stage_u4() { return stage_a<M>() + (M == W_BF16 ? DBR * NCH : scales_at<M>() + 64); }
 static_assert(4 * stage_u4<W_BF16>() * 16 <= 144 * 1024, "bf16 stages exceed their LDS budget");
 static_assert(6 * stage_u4<W_FP8>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
 static_assert(3 * stage_u4<W_FP8L>() * 16 <= 128 * 1024, "MXFP8 stages exceed their LDS budget");
+static_assert(4 * stage_u4<W_FP4>() * 16 <= 128 * 1024, "MXFP4 stages exceed their LDS budget");
 
 // Wave w loads activation rows 8w .. 8w+7 (one instruction) and weight rows
 // 64w + 8j .. +7 (instruction j < 8); the lane's row is that base + lane/8
@@ -151,8 +173,8 @@ struct DTile {
 template <int M>
 __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, u32x4_t* lb) {
   const int w = threadIdx.x >> 6;
-  const long kb = (long)j * (M == W_FP8L ? 2 * KSB : KSB);  // activation bytes per step
-  const long wb = (long)j * (M == W_FP8 ? KSB / 2 : KSB);   // weight bytes per step
+  const long kb = (long)j * (halves<M>() ? 2 * KSB : KSB);  // activation bytes per step
+  const long wb = (long)j * (row64<M>() ? KSB / 2 : KSB);    // weight bytes per step
   long bk = wb;
   if (t.bstride) {
     const long seg = wb / t.kseg;
@@ -161,8 +183,8 @@ __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, 
   const char* ab = t.abase + kb;
   const char* bb = t.bbase + bk;
   dma16(ab, t.aoff, la + 8 * w * NCH);
-  if (M == W_FP8L) dma16(ab + KSB, t.aoff, la + DBM * NCH + 8 * w * NCH);
-  if (M == W_FP8) {
+  if (halves<M>()) dma16(ab + KSB, t.aoff, la + DBM * NCH + 8 * w * NCH);
+  if (row64<M>()) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) dma16(bb, t.boff[q], lb + (64 * w + 16 * q) * 4);
   } else {
@@ -171,7 +193,7 @@ __device__ __forceinline__ void issue_stage(const DTile& t, int j, u32x4_t* la, 
   }
   // scales: wave w loads rows 64w .. 64w+63 (W_FP8: lanes 0..31 for blocks
   // 0, 1, lanes 32..63 the same bytes again into the slot's unused half;
-  // W_FP8L: lanes 16b .. 16b+15 block b)
+  // W_FP8L, W_FP4: lanes 16b .. 16b+15 block b)
   if (M != W_BF16)
     dma4(t.sbase + (long)j * t.sstep, t.soff,
          reinterpret_cast<const char*>(lb + scales_at<M>()) + 256 * w);
@@ -196,6 +218,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, floa
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// Eight E2M1 codes (one dword, input 2b in the low nibble of byte b) ->
+// eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 // E8M0 byte -> a float whose exponent field is that byte (the conversion
 // reads only the exponent); byte 0 becomes the subnormal 2^-127 exactly.
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
@@ -210,6 +243,37 @@ template <int KIND, int M>
 __device__ __forceinline__ void compute_stage(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 5, r = lane & 31;
+  if (M == W_FP4) {
+    // eight sub-steps: lane half q takes inputs 64q .. 64q+63 (activation
+    // half q, weight chunks 2q, 2q+1 = scale blocks 2q, 2q+1), sub-step
+    // s = 4h + s4 the eight at 64q + 8s: dword s4 of chunk 2q + h
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + scales_at<M>());
+    const u32x4_t* lah = la + q * DBM * NCH;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t wv[2];
+      float scale[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = wrow<KIND>(w, nb) + r;
+        wv[nb] = lb[row * 4 + ((2 * q + h) ^ swz4(row))];
+        scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * (2 * q + h) + (row & 63)]);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int s = 4 * h + s4;
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lah[r * NCH + (s ^ swz(r))]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4_t& c = wv[nb];
+          const bf16x8_t fb =
+              fp4x8_to_bf16(s4 == 0 ? c.x : s4 == 1 ? c.y : s4 == 2 ? c.z : c.w, scale[nb]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    return;
+  }
   if (M == W_FP8L) {
     // eight sub-steps: lane half q takes inputs 64q .. 64q+63 (activation
     // half q, weight chunks 4q .. 4q+3, scale blocks 2q, 2q+1), sub-step s the
@@ -340,12 +404,11 @@ __device__ __forceinline__ int scale_lane_block() { return (threadIdx.x >> 4) & 
 template <int KIND, int M>
 __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DTile& t) {
   constexpr int EPC = 8;
-  constexpr bool FP8 = M != W_BF16;
-  constexpr uint32_t WES = FP8 ? 1u : 2u;  // weight element size
-  // W_FP8: lanes 32..63 repeat the scale bytes of lanes 0..31; W_FP8L: lane
-  // l takes block l / 16
-  const int sblock = M == W_FP8L ? (threadIdx.x & 63) >> 4 : scale_lane_block();
-  constexpr int SBLK = M == W_FP8L ? 4 : 2;  // scale blocks per K-step
+  constexpr bool FP8 = M != W_BF16;  // MX weights (MXFP8 or MXFP4)
+  // W_FP8: lanes 32..63 repeat the scale bytes of lanes 0..31; W_FP8L and
+  // W_FP4: lane l takes block l / 16
+  const int sblock = halves<M>() ? (threadIdx.x & 63) >> 4 : scale_lane_block();
+  constexpr int SBLK = halves<M>() ? 4 : 2;  // scale blocks per K-step
   const int H = g.H;
   t.row0 = p.x;
   t.nrows = p.y & 0xFFFF;
@@ -362,20 +425,21 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     // waves 0, 1 load gate rows (weight rows 0..127), waves 2, 3 the up rows
     const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? g.ws0 : g.w0)
                                                     : (t.shared ? g.ws1 : g.w1));
-    t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * H * WES);
-    if (M == W_FP8) {
+    const uint32_t rb = (uint32_t)row_bytes<M>(H);
+    t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * rb);
+    if (row64<M>()) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int br = b_row_fp8(j);
         const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
-        t.boff[j] = n * (uint32_t)H + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
+        t.boff[j] = n * rb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int br = b_row(j);
         const uint32_t n = (uint32_t)min(t.n0 + (br & 127), t.N - 1);
-        t.boff[j] = n * (uint32_t)H * WES + (uint32_t)(lane_chunk(br) * 16);
+        t.boff[j] = n * rb + (uint32_t)(lane_chunk(br) * 16);
       }
     }
     if (FP8) {
@@ -391,7 +455,7 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
       t.sstep = SBLK * ns;
     }
     t.nk = H / k_of<M>();
-    t.kseg = H * WES;
+    t.kseg = (int)rb;
     t.bstride = 0;
   } else {
     // down: shared tiles read h_shared [T, S*Is] against the S shared down
@@ -401,25 +465,26 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
     const int Ks = sh ? g.S * g.Is : g.I;
     const int ldb = sh ? g.Is : g.I;
     t.abase = static_cast<const char*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
+    const uint32_t rb = (uint32_t)row_bytes<M>(ldb);  // bytes per weight row of a K segment
     t.bbase = sh ? static_cast<const char*>(g.ws0)
-                 : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I * WES;
+                 : static_cast<const char*>(g.w0) + (size_t)t.e * H * row_bytes<M>(g.I);
     t.n0 = nt * DBR;
     t.N = H;
     const uint32_t arow = (uint32_t)(t.row0 + min(row, t.nrows - 1));
     t.aoff = (arow * (uint32_t)Ks + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
-    if (M == W_FP8) {
+    if (row64<M>()) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int br = b_row_fp8(j);
         const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
-        t.boff[j] = n * (uint32_t)ldb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
+        t.boff[j] = n * rb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int br = b_row(j);
         const uint32_t n = (uint32_t)min(t.n0 + br, H - 1);
-        t.boff[j] = n * (uint32_t)ldb * WES + (uint32_t)(lane_chunk(br) * 16);
+        t.boff[j] = n * rb + (uint32_t)(lane_chunk(br) * 16);
       }
     }
     if (FP8) {
@@ -432,8 +497,8 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
       t.sstep = SBLK * H;
     }
     t.nk = Ks / k_of<M>();
-    t.kseg = ldb * WES;
-    t.bstride = sh && g.S > 1 ? H * g.Is * WES : 0;
+    t.kseg = (int)rb;
+    t.bstride = sh && g.S > 1 ? H * (int)rb : 0;
   }
 }
 
@@ -635,9 +700,13 @@ template <int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_shared_decode_kernel(GemmArgs g) {
   decode_body<DOWN_SHARED, false, M, NST>(g);
 }
-template <bool ATOMIC, int M, int NST>
+template <int M, int NST>
 __global__ void __launch_bounds__(NTHR) moe_down_routed_decode_kernel(GemmArgs g) {
-  decode_body<DOWN_ROUTED, ATOMIC, M, NST>(g);
+  decode_body<DOWN_ROUTED, false, M, NST>(g);
+}
+template <int M, int NST>
+__global__ void __launch_bounds__(NTHR) moe_down_routed_atomic_decode_kernel(GemmArgs g) {
+  decode_body<DOWN_ROUTED, true, M, NST>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,8 +717,10 @@ int gemm_decode_bm() { return DBM; }
 // Every K length is a whole number of four K-steps, and the per-lane 32-bit
 // offsets reach every row: x, h, h_shared, one expert's weights, the shared
 // weights, and acc rows of the atomic epilogue (< 2^31).
-bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is) {
+bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is, int wfmt) {
   if (H % 256 || I % 256 || (S && (S * Is) % 256)) return false;
+  // MXFP4 K-steps of 128 inputs must not straddle two shared experts
+  if (wfmt == WF_MXFP4 && S > 1 && Is % 128) return false;
   const uint64_t lim = 1ull << 32;
   const uint64_t x = (uint64_t)T * H * 2, h = (uint64_t)T * k * I * 2,
                  hs = (uint64_t)T * S * Is * 2, w = (uint64_t)H * I * 2,
@@ -678,17 +749,29 @@ static hipError_t launch_decode(void (*kern)(GemmArgs), long n, const GemmArgs& 
   return hipGetLastError();
 }
 
-// g.fp8 selects the MXFP8-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1):
-// 128-input K-steps with three stages when every K length the launch streams
-// is a multiple of three such steps (and a separate shared expert's width a
-// multiple of 128), else 64-input steps with six stages (K a multiple of six
-// steps) or four.
+// g.wfmt selects the MX-weight kernels (scales in g.sw0 / sw1 / sws0 / sws1).
+// MXFP8: 128-input K-steps with three stages when every K length the launch
+// streams is a multiple of three such steps (and a separate shared expert's
+// width a multiple of 128), else 64-input steps with six stages (K a
+// multiple of six steps) or four. MXFP4: 128-input K-steps with four stages
+// when every K length is a multiple of four steps, else two (every K length
+// is a multiple of 256, and a K-split shared width a multiple of 128: the
+// host checks with gemm_decode_fits).
 static bool steps_div(int K, int k_step, int n) { return K % k_step == 0 && (K / k_step) % n == 0; }
 
-enum Variant { V_BF16, V_FP8L3, V_FP8_6, V_FP8_4 };
+enum Variant { V_BF16, V_FP8L3, V_FP8_6, V_FP8_4, V_FP4_4, V_FP4_2 };
 
 static Variant pick(const GemmArgs& g, bool gate_up, bool routed, bool shared) {
-  if (!g.fp8) return V_BF16;
+  if (g.wfmt == WF_DTYPE) return V_BF16;
+  if (g.wfmt == WF_MXFP4) {
+    bool four = true;
+    if (gate_up) four = steps_div(g.H, 128, 4);
+    else {
+      if (routed) four = four && steps_div(g.I, 128, 4);
+      if (shared) four = four && steps_div(g.S * g.Is, 128, 4);
+    }
+    return four ? V_FP4_4 : V_FP4_2;
+  }
   bool l3 = true, six = true;
   if (gate_up) {
     l3 = steps_div(g.H, 128, 3);
@@ -710,7 +793,9 @@ static Variant pick(const GemmArgs& g, bool gate_up, bool routed, bool shared) {
   ((V) == V_BF16    ? launch_decode(KERN<W_BF16, 4>, n, g, st)                          \
    : (V) == V_FP8L3 ? launch_decode(KERN<W_FP8L, 3>, n, g, st)                          \
    : (V) == V_FP8_6 ? launch_decode(KERN<W_FP8, 6>, n, g, st)                           \
-                    : launch_decode(KERN<W_FP8, 4>, n, g, st))
+   : (V) == V_FP8_4 ? launch_decode(KERN<W_FP8, 4>, n, g, st)                           \
+   : (V) == V_FP4_4 ? launch_decode(KERN<W_FP4, 4>, n, g, st)                           \
+                    : launch_decode(KERN<W_FP4, 2>, n, g, st))
 
 hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st) {
   const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
@@ -727,18 +812,6 @@ hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st) {
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st) {
   const long n = (long)g.mt_routed * g.nt_routed;
   const Variant v = pick(g, false, true, false);
-  if (atomic) {
-    switch (v) {
-      case V_BF16: return launch_decode(moe_down_routed_decode_kernel<true, W_BF16, 4>, n, g, st);
-      case V_FP8L3: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8L, 3>, n, g, st);
-      case V_FP8_6: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8, 6>, n, g, st);
-      default: return launch_decode(moe_down_routed_decode_kernel<true, W_FP8, 4>, n, g, st);
-    }
-  }
-  switch (v) {
-    case V_BF16: return launch_decode(moe_down_routed_decode_kernel<false, W_BF16, 4>, n, g, st);
-    case V_FP8L3: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8L, 3>, n, g, st);
-    case V_FP8_6: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8, 6>, n, g, st);
-    default: return launch_decode(moe_down_routed_decode_kernel<false, W_FP8, 4>, n, g, st);
-  }
+  if (atomic) return DEC_LAUNCH(moe_down_routed_atomic_decode_kernel, v, n, g, st);
+  return DEC_LAUNCH(moe_down_routed_decode_kernel, v, n, g, st);
 }

@@ -6,6 +6,8 @@
 
 #include "moe_common.h"
 
+enum WeightFormat { WF_DTYPE = 0, WF_MXFP8 = 1, WF_MXFP4 = 2 };
+
 // Arguments of the grouped expert GEMMs (passed by value to the kernels).
 struct GemmArgs {
   const void* a;      // activations: x (gate/up), h (routed down), h_shared (shared down)
@@ -25,10 +27,13 @@ struct GemmArgs {
   int mt_routed, nt_routed, mt_shared, nt_shared;
   int gm_routed, gm_shared;  // m-slots per group of the tile order
   ActParams act;
-  // MXFP8 weights (fp8 != 0): E8M0 scales, block-major [K/32, N] per matrix,
-  // of the stacked gate (or down) and up weights and of the shared gate (or
-  // down) and up weights (the shared ones start at slot E when packed)
-  int fp8;
+  // Expert weight format (wfmt): WF_DTYPE (the layer dtype), WF_MXFP8 (E4M3
+  // codes, one byte per weight) or WF_MXFP4 (E2M1 codes, two weights per
+  // byte, input 2j in the low nibble of byte j). MX formats carry E8M0
+  // scales, block-major [K/32, N] per matrix, of the stacked gate (or down)
+  // and up weights and of the shared gate (or down) and up weights (the
+  // shared ones start at slot E when packed).
+  int wfmt;
   const uint8_t* sw0;
   const uint8_t* sw1;
   const uint8_t* sws0;
@@ -43,10 +48,10 @@ hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_both(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_routed(const GemmArgs& g, int dtype, bool atomic, hipStream_t st);
 
-// 32-row tile kernels for decode-sized batches (bf16; every K length a
-// multiple of 256; per-lane 32-bit offsets: gemm_decode_fits).
+// 32-row tile kernels for decode-sized batches (bf16 activations; every K
+// length a multiple of 256; per-lane 32-bit offsets: gemm_decode_fits).
 int gemm_decode_bm();
-bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is);
+bool gemm_decode_fits(int64_t T, int H, int I, int k, int S, int Is, int wfmt);
 hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st);

@@ -123,8 +123,10 @@ def test_mxfp8_config_checks():
     assert moe.moe_workspace_size(_mx_cfg(), 64) > 0
     assert moe.moe_workspace_size(_mx_cfg(hidden_size=6208, moe_intermediate_size=1408,
                                           shared_intermediate_size=1408), 64) > 0
-    for bad, status in ((dict(weight_format=2), moe.MOE_ERR_INVALID_ARG),
-                        (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED)):
+    for bad, status in ((dict(weight_format=3), moe.MOE_ERR_INVALID_ARG),
+                        (dict(weight_format=-1), moe.MOE_ERR_INVALID_ARG),
+                        (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED),
+                        (dict(dtype="f32", weight_format="mxfp4"), moe.MOE_ERR_UNSUPPORTED)):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_workspace_size(_mx_cfg(**bad), 64)
         assert ei.value.status == status, bad
@@ -132,6 +134,18 @@ def test_mxfp8_config_checks():
     assert _raw_forward(_mx_cfg(), 8) == moe.MOE_ERR_INVALID_ARG
     m = moe.MoeMxScales(gate=0x2000, up=0x2000, down=None)
     assert _raw_forward(_mx_cfg(), 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_mxfp4_config_checks():
+    """MXFP4 weights: accepted with bf16 activations, scales required; the
+    weights are half a byte each, so the workspace (no weights in it) is the
+    same as for MXFP8."""
+    c4 = synth.layer_keys(synth.config("minimax_m3_decode_T64_mxfp4"))
+    assert c4["weight_format"] == "mxfp4"
+    assert moe.moe_workspace_size(c4, 64) == moe.moe_workspace_size(_mx_cfg(), 64)
+    assert _raw_forward(c4, 8) == moe.MOE_ERR_INVALID_ARG
+    m = moe.MoeMxScales(gate=0x2000, up=0x2000, down=None)
+    assert _raw_forward(c4, 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("bad", [dict(n_group=3), dict(n_group=65), dict(n_group=8, topk_group=0),

@@ -1,6 +1,6 @@
-"""The whole layer (bf16 and MXFP8 weights, decode- and prefill-sized) and the
-MoE block captured in a HIP graph (through torch's graph capture) and
-replayed: every replay must equal an eager call on the same inputs. Also:
+"""The whole layer (bf16, MXFP8 and MXFP4 weights, decode- and
+prefill-sized) and the MoE block captured in a HIP graph (through torch's
+graph capture) and replayed: every replay must equal an eager call on the same inputs. Also:
 layer calls on two streams at once, with their own workspaces, equal the
 same calls made one after the other.
 
@@ -39,6 +39,9 @@ CASES = {
     "mxfp8_prefill": custom(T=400, hidden_size=256, num_experts=8, num_experts_per_tok=2,
                             moe_intermediate_size=256, num_shared_experts=2,
                             shared_intermediate_size=128, weight_format="mxfp8"),
+    "mxfp4_decode": custom(T=48, hidden_size=1024, num_experts=16, num_experts_per_tok=4,
+                           moe_intermediate_size=256, num_shared_experts=1, shared_packed=1,
+                           hidden_act="swigluoai", route_scale=2.0, weight_format="mxfp4"),
 }
 
 

@@ -36,14 +36,15 @@ def _gpu():
 
 
 def oracle_view(inp):
-    """The inputs with every MXFP8 weight stack replaced by its lazily
-    dequantised float64 view."""
+    """The inputs with every MX (MXFP8 or MXFP4) weight stack replaced by its
+    lazily dequantised float64 view."""
+    elem = "e2m1" if inp.cfg.get("weight_format") == "mxfp4" else "e4m3"
     d = dict(inp.__dict__)
     for w, key in (("w_gate", "gate"), ("w_up", "up"), ("w_down", "down"),
                    ("ws_gate", "shared_gate"), ("ws_up", "shared_up"),
                    ("ws_down", "shared_down")):
         if d[w] is not None:
-            d[w] = O.MxStacked(d[w], inp.mx[key])
+            d[w] = O.MxStacked(d[w], inp.mx[key], elem)
     return synth.MoeInputs(**d)
 
 
