@@ -44,6 +44,15 @@ def _c(**kw):
 
 # the 32-row kernel (every K length a multiple of 256)
 MX4 = {
+    # K lengths of six 128-input steps (two stages), the packed shared slot;
+    # three separate shared experts of width 256, whose down projection is
+    # K-segmented
+    "k768_packed": _c(T=40, hidden_size=768, num_experts=16, num_experts_per_tok=4,
+                         moe_intermediate_size=768, num_shared_experts=1, shared_packed=1,
+                         hidden_act="swigluoai", route_scale=2.0),
+    "k768_three_shared": _c(T=33, hidden_size=768, num_experts=8, num_experts_per_tok=2,
+                               moe_intermediate_size=768, num_shared_experts=3,
+                               shared_intermediate_size=256),
     "k512_packed_four_stages": _c(T=40, hidden_size=1024, num_experts=16, num_experts_per_tok=4,
                                   moe_intermediate_size=512, num_shared_experts=1, shared_packed=1,
                                   hidden_act="swigluoai", route_scale=2.0),
