@@ -46,7 +46,6 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
     I, S = cfg["moe_intermediate_size"], cfg["num_shared_experts"]
     Is = cfg["shared_intermediate_size"] or I
     bx = 2 if cfg["dtype"] == "bf16" else 4
-    # expert weight bytes per weight: MXFP8 is one code plus 1/32 of a scale byte
     # bytes per expert weight: MX codes plus one E8M0 scale byte per 32
     bw = {"mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}.get(cfg.get("weight_format"), bx)
     flops = T * (2 * H * E + 6 * k * H * I + 6 * S * H * Is)
@@ -90,6 +89,36 @@ def _traffic_records() -> list:
             return json.load(f).get("records", [])
     except (OSError, ValueError):
         return []
+
+
+def routing_report(cfg: dict, idx: np.ndarray, logits: np.ndarray, bias: np.ndarray) -> dict:
+    """What the routing did on this batch (from the GPU's own outputs): the
+    expert-load histogram in summary, and the smallest gap between the k-th
+    and (k+1)-th selection key of any token (keys formed in float64 from the
+    fp32 logits, as the selection does; zero means an exact tie at the
+    boundary, decided by the lower index). With group-limited routing the gap
+    is that of the ungrouped keys."""
+    E, k = cfg["num_experts"], cfg["num_experts_per_tok"]
+    T = idx.shape[0]
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    L = logits.astype(np.float64)
+    if cfg.get("score_func", "sigmoid") == "softmax":
+        z = np.exp(L - L.max(axis=1, keepdims=True))
+        sc = z / z.sum(axis=1, keepdims=True)
+    else:
+        sc = 1.0 / (1.0 + np.exp(-L))
+    keys = sc + bias.astype(np.float64)[None, :]
+    gap = None
+    if k < E and T:
+        part = -np.sort(-keys, axis=1)[:, k - 1:k + 1]
+        g = part[:, 0] - part[:, 1]
+        gap = {"min": float(g.min()), "tied_tokens": int((g == 0).sum())}
+    order = np.sort(counts)[::-1]
+    n10 = max(1, E // 10)
+    return {"touched_experts": int((counts > 0).sum()), "empty_experts": int((counts == 0).sum()),
+            "max_rows": int(counts.max()), "mean_rows": T * k / E,
+            "top10pct_share": float(order[:n10].sum() / max(1, T * k)),
+            "boundary_key_gap": gap}
 
 
 def traffic_from_profile(kernel: str, workload: str, src_sha: str):
@@ -463,8 +492,19 @@ def main():
     del flush
     ms_cold = float(np.median(cold))
 
+    # the spread of single warm calls (each timed alone with events)
+    per_call = []
+    for _ in range(args.steps):
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        layer()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(p0.elapsed_time(p1))
+
     idx_h = idx.view(T, k).cpu().numpy()
     alg = algorithmic(cfg, T, idx_h)
+    routing = routing_report(cfg, idx_h, logits.view(T, E).cpu().numpy(), inp.expert_bias)
     tflops = alg["flops"] / (ms * 1e-3) / 1e12
     gbs = alg["bytes"] / (ms * 1e-3) / 1e9
     peak_mm = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_MFMA_TFLOPS
@@ -538,7 +578,11 @@ def main():
                   "ms_per_step_eager": ms_eager, "ms_per_step_stage_calls": ms_stages,
                   "ms_per_step_hbm_cold": ms_cold,
                   "gbs_hbm_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9,
-                  "frac_hbm_peak_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                  "frac_hbm_peak_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "single_call_ms": {"median": float(np.median(per_call)),
+                                     "min": float(np.min(per_call)),
+                                     "max": float(np.max(per_call))},
+                  "routing": routing},
         "roofline": roof,
         "block": blk,
         "cpu_baseline": cpu,
