@@ -512,18 +512,14 @@ def main():
     ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
 
     # roofline of the dominant kernel: the grouped gate/up GEMM + activation,
-    # timed over back-to-back launches on the bench stream (dispatch overlaps
-    # the previous launch, so the average is the kernel's own duration, the
-    # figure a kernel trace reports)
-    n_rl = max(args.steps, 10)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for _ in range(n_rl):
-        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, stream,
-                                       mx=mx)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    gu_ms = r0.elapsed_time(r1) / n_rl
+    # its average duration over the K timed steps of the stage-call pass (HIP
+    # events on the bench stream around each gate/up launch, inside whole
+    # layer steps). Not back-to-back launches of the kernel alone: run without
+    # the layer's other kernels in between, the dense MFMA load lowers the
+    # clock within a few launches (gate/up on the AFMoE workload: 410 us in
+    # the layer, up to 600 us back to back), a state the layer never reaches.
+    gu_ms = stage_ms["gate_up"]
+    n_rl = args.steps
     sha = gemm_source_sha()
     gu_ai = alg["gate_up_flops"] / alg["gate_up_bytes"]
     if gu_ai >= ridge:

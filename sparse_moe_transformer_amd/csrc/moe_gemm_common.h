@@ -22,6 +22,35 @@ __device__ __align__(128) uint32_t g_zero_line[32] = {};
 // No bank conflicts for the 32x32 MFMA fragment reads (measured on gfx950).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// MX weight conversions (exact): E4M3 and E2M1 codes to bf16, times the
+// block's E8M0 scale. The scaled conversions read only the exponent field of
+// the scale operand, so e8m0_scale builds a float whose exponent field is the
+// E8M0 byte (byte 0 becomes the subnormal 2^-127 exactly).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
+}
+
+// Eight E4M3 codes (two dwords) -> eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Eight E2M1 codes (one dword, input 2b in the low nibble of byte b) ->
+// eight bf16, times the block scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
+  const u32x4_t u = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3))};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

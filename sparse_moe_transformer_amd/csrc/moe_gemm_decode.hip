@@ -208,33 +208,6 @@ __device__ __forceinline__ int wrow(int w, int nb) {
 
 typedef floatx16_t Acc2[2];
 
-// Eight E4M3 codes (two dwords) -> eight bf16, times the block scale.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1, float scale) {
-  const u32x4_t u = {
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, scale, true)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, false)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, scale, true))};
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// Eight E2M1 codes (one dword, input 2b in the low nibble of byte b) ->
-// eight bf16, times the block scale.
-__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t d, float scale) {
-  const u32x4_t u = {
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2)),
-      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3))};
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// E8M0 byte -> a float whose exponent field is that byte (the conversion
-// reads only the exponent); byte 0 becomes the subnormal 2^-127 exactly.
-__device__ __forceinline__ float e8m0_scale(uint32_t e) {
-  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
-}
-
 // One K-step (4 sub-steps of K = 16).
 //   bf16 weights: lane l reads row l%32, chunk 2s + l/32.
 //   MXFP8 weights: lane l takes inputs 32q + 8s .. +7 (q = l/32): activation
