@@ -9,7 +9,8 @@ w + 1 scales for MiniMax-M3, mlxcel #763 Norms bullet), through the C ABI:
     followed by the oracle's RMSNorm, both combine modes, in place;
   * moe_block_forward against the oracle's block fed the GPU's own router
     logits: routing exactly; the output within the layer's bar on the
-    normalised branch plus the final rounding of out.
+    normalised branch plus the final rounding of out; also with MXFP8 and
+    MXFP4 expert weights (the oracle on their exact values).
 
 Bars: the RMSNorm stages are elementwise, so each element may carry the
 storage rounding of its own value (2^-8 relative for bf16 stores of a value
@@ -22,6 +23,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from tests.moe_harness import TOL, Dev, custom, say
+from tests.test_gpu_mxfp8 import oracle_view
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +147,16 @@ BLOCK = {
     "one_token_softmax": custom(T=1, hidden_size=256, num_experts=8, num_experts_per_tok=3,
                                 moe_intermediate_size=256, num_shared_experts=1,
                                 score_func="softmax"),
+    # MX expert weights inside the block: MXFP8 on the 128-row tiles, MXFP4 on
+    # the 32-row decode tiles
+    "m3_like_mxfp8": custom(T=300, hidden_size=768, num_experts=16, num_experts_per_tok=4,
+                            moe_intermediate_size=256, num_shared_experts=1, shared_packed=1,
+                            hidden_act="swigluoai", route_scale=2.0, norm_add_one=1,
+                            weight_format="mxfp8"),
+    "trinity_like_mxfp4_decode": custom(T=32, hidden_size=1024, num_experts=64,
+                                        num_experts_per_tok=8, moe_intermediate_size=256,
+                                        num_shared_experts=1, shared_intermediate_size=256,
+                                        route_scale=2.826, weight_format="mxfp4"),
 }
 
 
@@ -161,7 +173,7 @@ def run_block(dev, nw, deterministic, h=None, out=None):
     moe.moe_block_forward(c, nw, T, h, moe.to_device(nw["pre"]), moe.to_device(nw["post"]),
                           dev.w_router, dev.expert_bias, dev.w_gate, dev.w_up, dev.w_down,
                           dev.ws_gate, dev.ws_up, dev.ws_down, logits, idx, w, out,
-                          deterministic, ws)
+                          deterministic, ws, mx=dev.mx)
     torch.cuda.synchronize()
     return dict(logits=logits.view(T, E).cpu().numpy(), idx=idx.view(T, k).cpu().numpy(),
                 w=w.view(T, k).cpu().numpy(), out=_host(out, (T, H)))
@@ -169,6 +181,8 @@ def run_block(dev, nw, deterministic, h=None, out=None):
 
 def check_block(cfg, inp, nw, res, tokens=None):
     """Routing exactly and out within the block's bar (see the module text)."""
+    if inp.mx is not None:   # MX weights: the oracle runs on their exact values
+        inp = oracle_view(inp)
     if tokens is not None:
         inp = synth.MoeInputs(**{**inp.__dict__, "x": inp.x[tokens]})
         res = {key: v[tokens] for key, v in res.items()}
