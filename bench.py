@@ -102,11 +102,12 @@ def routing_report(cfg: dict, idx: np.ndarray, logits: np.ndarray, bias: np.ndar
     T = idx.shape[0]
     counts = np.bincount(idx.reshape(-1), minlength=E)
     L = logits.astype(np.float64)
-    if cfg.get("score_func", "sigmoid") == "softmax":
-        z = np.exp(L - L.max(axis=1, keepdims=True))
-        sc = z / z.sum(axis=1, keepdims=True)
-    else:
-        sc = 1.0 / (1.0 + np.exp(-L))
+    with np.errstate(over="ignore"):  # exp(-L) -> inf gives the exact score 0
+        if cfg.get("score_func", "sigmoid") == "softmax":
+            z = np.exp(L - L.max(axis=1, keepdims=True))
+            sc = z / z.sum(axis=1, keepdims=True)
+        else:
+            sc = 1.0 / (1.0 + np.exp(-L))
     keys = sc + bias.astype(np.float64)[None, :]
     gap = None
     if k < E and T:
