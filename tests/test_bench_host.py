@@ -1,0 +1,107 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic FLOPs and bytes the
+roofline divides by, the routing report, kernel-name shortening of profiler
+output, the HBM traffic summary built from PMC counter files (calibration
+scaling included) and its source fingerprint, and the one-GPU contract."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_formulas_by_hand():
+    cfg = dict(hidden_size=64, num_experts=4, num_experts_per_tok=2, moe_intermediate_size=32,
+               num_shared_experts=1, shared_intermediate_size=16, dtype="bf16",
+               weight_format="dtype")
+    T = 3
+    idx = np.array([[0, 1], [1, 2], [0, 2]])          # experts 0, 1, 2 touched (3 of 4)
+    a = bench.algorithmic(cfg, T, idx)
+    H, E, k, I, S, Is = 64, 4, 2, 32, 1, 16
+    assert a["flops"] == T * (2 * H * E + 6 * k * H * I + 6 * S * H * Is)
+    assert a["touched"] == 3
+    assert a["bytes"] == 3 * 3 * H * I * 2 + S * 3 * H * Is * 2 + 4 * E * H + 2 * T * H * 2 + 4 * E
+    assert a["gate_up_flops"] == 4 * T * H * (k * I + S * Is)
+    # MX weights: codes plus one scale byte per 32 weights
+    a8 = bench.algorithmic(dict(cfg, weight_format="mxfp8"), T, idx)
+    a4 = bench.algorithmic(dict(cfg, weight_format="mxfp4"), T, idx)
+    w = 3 * 3 * H * I + S * 3 * H * Is                 # weights moved
+    assert a8["bytes"] - a4["bytes"] == pytest.approx(w * 0.5)
+    assert a["bytes"] - a8["bytes"] == pytest.approx(w * (2 - 1 - 1 / 32))
+
+
+def test_routing_report_by_hand():
+    cfg = dict(num_experts=4, num_experts_per_tok=2)
+    # token 0: keys sigmoid(0) + b = 0.5 each for experts 0 and 3 with bias 0,
+    # expert 1 higher: top-2 = {1, 0 or 3}; the 2nd and 3rd keys tie exactly
+    L = np.array([[0.0, 2.0, -3.0, 0.0], [4.0, -1.0, 3.0, -2.0]], np.float32)
+    idx = np.array([[1, 0], [0, 2]])
+    r = bench.routing_report(cfg, idx, L, np.zeros(4, np.float32))
+    assert r["touched_experts"] == 3 and r["empty_experts"] == 1
+    assert r["max_rows"] == 2 and r["mean_rows"] == 1.0
+    assert r["top10pct_share"] == 0.5                  # the top max(1, E // 10) = 1 expert: 2 of 4 rows
+    assert r["boundary_key_gap"]["tied_tokens"] == 1 and r["boundary_key_gap"]["min"] == 0.0
+    s = 1 / (1 + np.exp(-np.array([4.0, 3.0, -1.0])))
+    r2 = bench.routing_report(cfg, idx[1:], L[1:], np.zeros(4, np.float32))
+    assert r2["boundary_key_gap"]["min"] == pytest.approx(s[1] - s[2], rel=1e-12)
+
+
+@pytest.mark.parametrize("name,short", [
+    ("_ZN12_GLOBAL__N_118moe_gate_up_kernelIDF16bLi0EEEv8GemmArgs", "moe_gate_up_kernel"),
+    ("_Z25moe_gate_up_decode_kernelILi3ELi4EEv8GemmArgs", "moe_gate_up_decode_kernel"),
+    ("void (anonymous namespace)::moe_down_kernel<__bf16, 0>(GemmArgs)", "moe_down_kernel"),
+    ("combine_kernel(float const*, void const*)", "combine_kernel"),
+])
+def test_kernel_name_shortening(name, short):
+    assert bench._short(name) == short
+
+
+def _counter_csv(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for k, c, v in rows:
+            w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_traffic_summary_scaling_and_fingerprint(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled so that a plain copy of
+    256 MiB reads and writes 256 MiB; records carry the GEMM sources'
+    fingerprint and are ignored once it changes."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    d = tmp_path / "run"
+    kern = "_Z18moe_gate_up_kernelIDF16bLi0EEv8GemmArgs"
+    line = {"roofline": {"kernel": "moe_gate_up_kernel"},
+            "layer": {"gate_up_bytes": 1000 * 1024},
+            "config": {"workload": "wl"}}
+    os.makedirs(d)
+    (d / "bench.json").write_text(json.dumps(line) + "\n")
+    _counter_csv(d / "pmc_FETCH_SIZE", [(kern, "FETCH_SIZE", 900), (kern, "FETCH_SIZE", 1100)])
+    _counter_csv(d / "pmc_WRITE_SIZE", [(kern, "WRITE_SIZE", 100)])
+    copy = "__amd_rocclr_copyBuffer"
+    _counter_csv(d / "cal_FETCH_SIZE", [(copy, "FETCH_SIZE", 131072)])    # half of 256 MiB
+    _counter_csv(d / "cal_WRITE_SIZE", [(copy, "WRITE_SIZE", 262144)])
+    monkeypatch.setattr(bench, "gemm_source_sha", lambda: "sha-a")
+    text = bench.summarize_traffic(str(d))
+    rec = json.load(open(tmp_path / "profiles" / "traffic.json"))["records"][0]
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == (1000 * 2 + 100) * 1024
+    assert "ratio 2.10" in text
+    assert bench.traffic_from_profile("moe_gate_up_kernel", "wl", "sha-a") == rec["hbm_bytes_per_launch"]
+    assert bench.traffic_from_profile("moe_gate_up_kernel", "wl", "sha-b") is None
+    assert bench.traffic_from_profile("moe_gate_up_kernel", "other", "sha-a") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
