@@ -245,14 +245,17 @@ def cpu_baseline(name: str, cfg: dict, inp, sample_tokens: int):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     wts = {n: getattr(inp, n) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
-    if inp.mx is not None:  # MX stacks, dequantised one expert at a time
+    if cfg.get("weight_format", "dtype") != "dtype":  # MX stacks, one expert at a time
         keys = {"w_gate": "gate", "w_up": "up", "w_down": "down", "ws_gate": "shared_gate",
                 "ws_up": "shared_up", "ws_down": "shared_down"}
         elem = "e2m1" if cfg.get("weight_format") == "mxfp4" else "e4m3"
         wts = {n: (O.MxStacked(a, inp.mx[keys[n]], elem) if a is not None else None)
                for n, a in wts.items()}
+    wr = inp.w_router
+    if cfg.get("router_format", "f32") == "mxfp8":   # the 8-bit router's exact values
+        wr = O.mx_dequantize(inp.w_router, inp.mx["router"])
     sub = synth.MoeInputs(cfg=dict(cfg, T=sample_tokens), x=inp.x[:sample_tokens],
-                          w_router=inp.w_router, expert_bias=inp.expert_bias, **wts)
+                          w_router=wr, expert_bias=inp.expert_bias, **wts)
     t0 = time.perf_counter()
     O.moe_forward(sub, cfg)
     dt = time.perf_counter() - t0
@@ -420,7 +423,7 @@ def main():
         st = torch.cuda.current_stream()
         rec = (lambda i: events[i].record(st)) if events else (lambda i: None)
         rec(0)
-        moe.moe_router_logits(keys, T, x, wr, logits, ws, st)
+        moe.moe_router_logits(keys, T, x, wr, logits, ws, st, mx=mx)
         rec(1)
         moe.moe_route(keys, T, logits, b, idx, w, None, st)
         rec(2)

@@ -126,7 +126,19 @@ typedef struct {
   const uint8_t* shared_gate;
   const uint8_t* shared_up;
   const uint8_t* shared_down;
+  const uint8_t* router;  /* [H/32, E], when router_format is MXFP8     */
 } moe_mx_scales;
+
+/* Storage of the router weights:
+ *   MOE_ROUTER_F32    fp32 [E, H]
+ *   MOE_ROUTER_MXFP8  E4M3 codes [E, H] (uint8) with E8M0 scales per 32
+ *                     inputs in moe_mx_scales.router, block-major [H/32, E]:
+ *                     the 8-bit router of the 4-bit Trinity checkpoints
+ *                     (mlxcel #845 "Checkpoint weight layout": the router
+ *                     gate at 8 bits, the rest at 4), read as MXFP8 like the
+ *                     experts. The codes are dequantised exactly to fp32 in
+ *                     the workspace and the router GEMM runs unchanged. */
+typedef enum { MOE_ROUTER_F32 = 0, MOE_ROUTER_MXFP8 = 1 } moe_router_format;
 
 /* Layer configuration (host struct, passed by const pointer). Field names
  * follow the pages' config keys. */
@@ -156,6 +168,7 @@ typedef struct {
                                        n_group <= 64                             */
   int32_t topk_group;               /* groups kept, 1..n_group; k <= topk_group *
                                        E / n_group (used when n_group > 1)       */
+  int32_t router_format;            /* moe_router_format of w_router             */
 } moe_config;
 
 /* Bytes of device workspace that moe_layer_forward (and every stage entry
@@ -163,14 +176,16 @@ typedef struct {
  * 256-byte aligned. */
 moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
 
-/* Router GEMM: logits[T,E] (fp32) = x[T,H] . w_router[E,H]^T (fp32 weights),
- * fp32 accumulation. The router is a bias-free linear map (mlxcel #845
+/* Router GEMM: logits[T,E] (fp32) = x[T,H] . w_router[E,H]^T, fp32
+ * accumulation. The router is a bias-free linear map (mlxcel #845
  * "Checkpoint weight layout": mlp.router.gate). The result does not depend on
  * timing, and identical router rows give bitwise identical logit columns.
+ * w_router: fp32 [E,H], or E4M3 codes [E,H] when router_format is MXFP8 (mx:
+ * host pointer to the scales, mx->router; else mx may be NULL).
  * ws, ws_bytes: workspace of at least moe_workspace_size bytes (scratch). */
 moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
-                             const float* w_router, float* logits, void* ws,
-                             size_t ws_bytes, moe_stream_t stream);
+                             const void* w_router, const moe_mx_scales* mx, float* logits,
+                             void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Routing (mlxcel #845 "Routing detail"; mlxcel #763 MoE bullet): sigmoid
  * (or softmax) scores, selection key s + expert_bias formed in fp64, top-k by
@@ -245,7 +260,8 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
 
 /* The whole layer: router GEMM, routing, grouping, gate/up + activation,
  * down + combine, cast.
- *   x [T,H] dtype; w_router [E,H] fp32; expert_bias [E] fp32 or NULL;
+ *   x [T,H] dtype; w_router [E,H] fp32 (or MXFP8 codes, router_format);
+ *   expert_bias [E] fp32 or NULL;
  *   w_gate, w_up, w_down stacked experts; ws_* separate shared experts or
  *   NULL; mx: scales of MX weights (host pointer) or NULL;
  *   router_logits_in [T,E] or NULL (when given, the router GEMM is
@@ -253,7 +269,7 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
  *   topk_idx_out [T,k] / topk_w_out [T,k] or NULL; out [T,H] dtype.
  *   deterministic: 0 = fp32 atomic combine, 1 = fixed-order combine. */
 moe_status moe_layer_forward(
-    const moe_config* cfg, int64_t T, const void* x, const float* w_router,
+    const moe_config* cfg, int64_t T, const void* x, const void* w_router,
     const float* expert_bias, const void* w_gate, const void* w_up,
     const void* w_down, const void* ws_gate, const void* ws_up,
     const void* ws_down, const moe_mx_scales* mx, const float* router_logits_in,
@@ -313,7 +329,7 @@ moe_status moe_block_workspace_size(const moe_config* cfg, int64_t T,
 moe_status moe_block_forward(
     const moe_config* cfg, const moe_norm_config* norm, int64_t T,
     const void* h, const float* pre_norm_w, const float* post_norm_w,
-    const float* w_router, const float* expert_bias, const void* w_gate,
+    const void* w_router, const float* expert_bias, const void* w_gate,
     const void* w_up, const void* w_down, const void* ws_gate,
     const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
     float* router_logits_out,

@@ -48,7 +48,8 @@ The layer then runs unchanged on those exact values (mx_dequantize).
 The 4-bit weights of the Trinity checkpoints (mlxcel #845 "Checkpoint
 confirmed" and "Checkpoint weight layout": 4 bits per weight, the router at
 8) have no format on the pages; they are read as OCP MXFP4: E2M1 elements,
-two per byte, with the same E8M0 scales (the router stays fp32).
+two per byte, with the same E8M0 scales; the 8-bit router as MXFP8. The
+layer runs on the exact dequantised values (mx_dequantize).
 
 Readings where the pages are silent are listed in the design notes: the bias
 is added to the post-sigmoid scores; normalise then scale; no epsilon in the
@@ -69,7 +70,12 @@ F64 = np.float64
 # storage decoding (exact)
 
 def as_f64(a: np.ndarray) -> np.ndarray:
-    """Exact float64 value of a stored tensor (uint16 = bf16 bits)."""
+    """Exact float64 value of a stored tensor (uint16 = bf16 bits). MX codes
+    (uint8) have no value without their scales: dequantise them first
+    (mx_dequantize, MxStacked)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint8:
+        raise ValueError("uint8 MX codes: dequantise them with their scales first")
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(F64)
     return np.asarray(a, dtype=F64)

@@ -21,6 +21,7 @@ MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLUOAI = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_MXFP8, MOE_WEIGHTS_MXFP4 = 0, 1, 2
+MOE_ROUTER_F32, MOE_ROUTER_MXFP8 = 0, 1
 
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
@@ -52,14 +53,16 @@ class MoeConfig(ctypes.Structure):
         ("weight_format", ctypes.c_int32),
         ("n_group", ctypes.c_int32),
         ("topk_group", ctypes.c_int32),
+        ("router_format", ctypes.c_int32),
     ]
 
 
 class MoeMxScales(ctypes.Structure):
     """Mirror of moe_mx_scales (include/moe.h): device pointers of the E8M0
-    scale tensors of MX (MXFP8, MXFP4) expert weights."""
+    scale tensors of MX (MXFP8, MXFP4) expert weights and of an MXFP8
+    router."""
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("gate", "up", "down", "shared_gate", "shared_up", "shared_down")]
+                ("gate", "up", "down", "shared_gate", "shared_up", "shared_down", "router")]
 
 
 def make_mx_scales(mx):
@@ -96,6 +99,7 @@ _SCORE = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 _ACT = {"silu": MOE_ACT_SILU, "swigluoai": MOE_ACT_SWIGLUOAI}
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16}
 _WF = {"dtype": MOE_WEIGHTS_DTYPE, "mxfp8": MOE_WEIGHTS_MXFP8, "mxfp4": MOE_WEIGHTS_MXFP4}
+_RF = {"f32": MOE_ROUTER_F32, "mxfp8": MOE_ROUTER_MXFP8}
 
 
 def make_config(cfg) -> MoeConfig:
@@ -125,6 +129,8 @@ def make_config(cfg) -> MoeConfig:
     c.weight_format = _WF.get(wf, wf) if isinstance(wf, str) else wf
     c.n_group = int(cfg.get("n_group", 1))
     c.topk_group = int(cfg.get("topk_group", 1))
+    rf = cfg.get("router_format", "f32")
+    c.router_format = _RF.get(rf, rf) if isinstance(rf, str) else rf
     return c
 
 
@@ -152,7 +158,7 @@ def lib() -> ctypes.CDLL:
         i64, sz, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
         sig = {
             "moe_workspace_size": [cp, i64, ctypes.POINTER(sz)],
-            "moe_router_logits": [cp, i64, _vp, _vp, _vp, _vp, sz, _vp],
+            "moe_router_logits": [cp, i64, _vp, _vp, _vp, _vp, _vp, sz, _vp],
             "moe_route": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
             "moe_permute": [cp, i64, _vp, _vp, _vp, _vp, _vp, sz, _vp],
             "moe_grouped_gate_up_swiglu": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
@@ -231,11 +237,14 @@ def moe_workspace_size(cfg, T: int) -> int:
     return n.value
 
 
-def moe_router_logits(cfg, T, x, w_router, logits, ws, stream=None):
+def moe_router_logits(cfg, T, x, w_router, logits, ws, stream=None, mx=None):
+    """mx: MX scales (an MXFP8 router's in mx["router"]), in the C argument
+    list after w_router."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     _need(logits, T * c.num_experts, "logits")
     _need(x, T * c.hidden_size, "x")
-    _call("moe_router_logits", ctypes.byref(c), int(T), _p(x), _p(w_router), _p(logits),
+    _call("moe_router_logits", ctypes.byref(c), int(T), _p(x), _p(w_router), _mxp(m), _p(logits),
           _p(ws), ws.numel() if ws is not None else 0, _stream(stream))
 
 

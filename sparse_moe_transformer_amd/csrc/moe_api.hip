@@ -19,6 +19,7 @@ struct Dims {
   size_t es;   // element size of dtype tensors
   int wfmt;    // expert weight format (WF_DTYPE, WF_MXFP8, WF_MXFP4)
   int wbits;   // bits per expert weight (dtype: 8 * es; MXFP8 8; MXFP4 4)
+  int rq;      // MXFP8 router weights
 };
 
 constexpr int64_t kMaxTokens = 1 << 24;
@@ -58,6 +59,8 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
   if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_MXFP8 &&
       c->weight_format != MOE_WEIGHTS_MXFP4)
     return MOE_ERR_INVALID_ARG;
+  if (c->router_format != MOE_ROUTER_F32 && c->router_format != MOE_ROUTER_MXFP8)
+    return MOE_ERR_INVALID_ARG;
   if (T * c->num_experts_per_tok > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   d->T = T;
   d->H = c->hidden_size;
@@ -73,6 +76,7 @@ moe_status check_cfg(const moe_config* c, int64_t T, Dims* d) {
             : c->weight_format == MOE_WEIGHTS_MXFP4 ? WF_MXFP4
                                                     : WF_DTYPE;
   d->wbits = d->wfmt == WF_MXFP8 ? 8 : d->wfmt == WF_MXFP4 ? 4 : 8 * (int)d->es;
+  d->rq = c->router_format == MOE_ROUTER_MXFP8;
   // MX weights take bf16 activations
   if (d->wfmt != WF_DTYPE && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -83,6 +87,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 // Workspace carving (every segment 256-byte aligned).
 struct Ws {
   void* router;  // router GEMM scratch
+  float* router_f32;  // MXFP8 router weights, dequantised (or NULL)
   float* logits;
   int32_t* idx;
   float* w;
@@ -110,6 +115,7 @@ Ws carve(const Dims& d, void* base) {
     return p;
   };
   w.router = take(router_ws_bytes(d.T, d.E, d.H, d.dtype));
+  w.router_f32 = d.rq ? (float*)take((size_t)d.E * d.H * 4) : nullptr;
   w.logits = (float*)take((size_t)d.T * d.E * 4);
   w.idx = (int32_t*)take(rows * 4);
   w.w = (float*)take(rows * 4);
@@ -284,12 +290,14 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 
-moe_status check_layer_args(const Dims& d, const void* x, const float* w_router,
+moe_status check_layer_args(const Dims& d, const void* x, const void* w_router,
                             const void* w_gate, const void* w_up, const void* w_down,
                             const void* ws_gate, const void* ws_up, const void* ws_down,
-                            const float* router_logits_in, int32_t deterministic) {
+                            const float* router_logits_in, int32_t deterministic,
+                            const moe_mx_scales* mx) {
   if (!x || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
   if (!router_logits_in && !w_router) return MOE_ERR_INVALID_ARG;
+  if (!router_logits_in && d.rq && (!mx || !mx->router)) return MOE_ERR_INVALID_ARG;
   if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
   if (deterministic != 0 && deterministic != 1) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -311,8 +319,22 @@ struct LayerOut {
   void* y_perm;   // unweighted routed rows (fixed-order combine) or NULL
 };
 
+// The router weights the router GEMM reads: as given (fp32), or MXFP8 codes
+// dequantised exactly into the workspace first.
+moe_status router_weights(const Dims& d, const void* w_router, const moe_mx_scales* mx,
+                          const Ws& w, hipStream_t st, const float** out) {
+  if (!d.rq) {
+    *out = static_cast<const float*>(w_router);
+    return MOE_OK;
+  }
+  MOE_TRY(hip_ok(launch_router_dequant_mx(static_cast<const uint8_t*>(w_router), mx->router,
+                                          w.router_f32, d.E, d.H, st)));
+  *out = w.router_f32;
+  return MOE_OK;
+}
+
 // Router GEMM through the down projection; the caller finalises from w.acc.
-moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const float* w_router,
+moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const void* w_router,
                      const float* expert_bias, const void* w_gate, const void* w_up,
                      const void* w_down, const void* ws_gate, const void* ws_up,
                      const void* ws_down, const moe_mx_scales* mx, const float* router_logits_in,
@@ -322,7 +344,9 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
   const float* logits = router_logits_in;
   if (!logits) {
     float* lo = router_logits_out ? router_logits_out : w.logits;
-    MOE_TRY(hip_ok(launch_router_logits(x, w_router, lo, T, d.H, d.E, d.dtype, w.router, st)));
+    const float* wr = nullptr;
+    MOE_TRY(router_weights(d, w_router, mx, w, st, &wr));
+    MOE_TRY(hip_ok(launch_router_logits(x, wr, lo, T, d.H, d.E, d.dtype, w.router, st)));
     logits = lo;
   }
   int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
@@ -357,15 +381,18 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
 }
 
 moe_status moe_router_logits(const moe_config* cfg, int64_t T, const void* x,
-                             const float* w_router, float* logits, void* ws, size_t ws_bytes,
-                             moe_stream_t stream) {
+                             const void* w_router, const moe_mx_scales* mx, float* logits,
+                             void* ws, size_t ws_bytes, moe_stream_t stream) {
   Dims d;
   MOE_TRY(check_cfg(cfg, T, &d));
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  if (d.rq && (!mx || !mx->router)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(d, ws, ws_bytes));
   Ws w = carve(d, ws);
-  return hip_ok(launch_router_logits(x, w_router, logits, (int)T, d.H, d.E, d.dtype, w.router,
+  const float* wr = nullptr;
+  MOE_TRY(router_weights(d, w_router, mx, w, (hipStream_t)stream, &wr));
+  return hip_ok(launch_router_logits(x, wr, logits, (int)T, d.H, d.E, d.dtype, w.router,
                                      (hipStream_t)stream));
 }
 
@@ -451,7 +478,7 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc, const
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
-                             const float* w_router, const float* expert_bias, const void* w_gate,
+                             const void* w_router, const float* expert_bias, const void* w_gate,
                              const void* w_up, const void* w_down, const void* ws_gate,
                              const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
                              const float* router_logits_in, float* router_logits_out,
@@ -463,7 +490,7 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   if (T == 0) return MOE_OK;
   if (!out) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_layer_args(d, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                           router_logits_in, deterministic));
+                           router_logits_in, deterministic, mx));
   MOE_TRY(check_mx(d, mx, true, true));
   MOE_TRY(check_ws(d, ws, ws_bytes));
   hipStream_t st = (hipStream_t)stream;
@@ -513,7 +540,7 @@ moe_status moe_block_workspace_size(const moe_config* cfg, int64_t T, size_t* by
 
 moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm, int64_t T,
                              const void* h, const float* pre_norm_w, const float* post_norm_w,
-                             const float* w_router, const float* expert_bias, const void* w_gate,
+                             const void* w_router, const float* expert_bias, const void* w_gate,
                              const void* w_up, const void* w_down, const void* ws_gate,
                              const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
                              float* router_logits_out,
@@ -526,7 +553,7 @@ moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm,
   if (T == 0) return MOE_OK;
   if (!pre_norm_w || !post_norm_w || !out) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_layer_args(d, h, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                           nullptr, deterministic));
+                           nullptr, deterministic, mx));
   MOE_TRY(check_mx(d, mx, true, true));
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < block_ws_bytes(d)) return MOE_ERR_WORKSPACE;

@@ -60,6 +60,9 @@ hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t
 // router GEMM scratch: bf16 split planes of the router weight + K-chunk partials
 int router_kchunks(int64_t T, int E, int H, int dtype);
 size_t router_ws_bytes(int64_t T, int E, int H, int dtype);
+// MXFP8 router weights (codes [E,H], scales [H/32,E]) -> fp32 [E,H], exactly
+hipError_t launch_router_dequant_mx(const uint8_t* codes, const uint8_t* scales, float* out, int E,
+                                    int H, hipStream_t st);
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
                                 int H, int E, int dtype, void* ws, hipStream_t st);
 

@@ -387,6 +387,26 @@ __global__ void __launch_bounds__(64 * RS_WAVES) router_small_kernel(
   if (t < T && e < E) logits[(size_t)t * E + e] = sum;
 }
 
+// MXFP8 router weights (E4M3 codes [E, H], E8M0 scales block-major
+// [H/32, E]) -> their exact fp32 values, one element per thread: code
+// (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+// subnormal) times 2^(scale - 127), formed as one exact ldexp of the
+// integer significand (at least 2^-136: an fp32 value).
+__global__ void __launch_bounds__(256) router_dequant_mx_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ out, int E,
+                                                                 int H) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)E * H) return;
+  const int e = (int)(i / H), k = (int)(i % H);
+  const uint32_t c = codes[i];
+  const int s = scales[(size_t)(k / 32) * E + e];
+  const int ef = (c >> 3) & 15, m = c & 7;
+  float v = ldexpf((float)(ef == 0 ? m : 8 + m), (ef == 0 ? -9 : ef - 10) + s - 127);
+  if ((c & 0x7F) == 0x7F || s == 255) v = __builtin_nanf("");
+  out[i] = (c & 0x80) ? -v : v;
+}
+
 inline int grid_blocks(size_t n) {
   size_t b = (n + 255) / 256;
   return (int)(b > 4096 ? 4096 : (b ? b : 1));
@@ -419,6 +439,15 @@ size_t router_ws_bytes(int64_t T, int E, int H, int dtype) {
   if (dtype != MOE_BF16 || router_small(T, H)) return 0;
   const int kc = router_kchunks(T, E, H, dtype);
   return (size_t)3 * E * H * 2 + 256 + (kc > 1 ? (size_t)kc * T * E * 4 : 0);
+}
+
+hipError_t launch_router_dequant_mx(const uint8_t* codes, const uint8_t* scales, float* out, int E,
+                                    int H, hipStream_t st) {
+  const size_t n = (size_t)E * H;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_dequant_mx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     codes, scales, out, E, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,

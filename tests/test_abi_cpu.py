@@ -148,6 +148,28 @@ def test_mxfp4_config_checks():
     assert _raw_forward(c4, 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_mxfp8_router_checks():
+    """An MXFP8 router (the 8-bit router of the 4-bit checkpoints): its scales
+    are required unless router logits are passed in, the format is validated,
+    and the workspace grows by the dequantised fp32 router (E*H*4, aligned)."""
+    c = synth.layer_keys(synth.config("trinity_nano_decode_T32_q4r8"))
+    assert c["router_format"] == "mxfp8"
+    base = moe.moe_workspace_size(dict(c, router_format="f32"), 32)
+    assert moe.moe_workspace_size(c, 32) - base == -(-(128 * 1024 * 4) // 256) * 256
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(dict(c, router_format=2), 32)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    # expert scales present, router scales missing: rejected before any launch
+    m = moe.MoeMxScales(gate=0x2000, up=0x2000, down=0x2000, router=None)
+    assert _raw_forward(c, 8, mx=ctypes.byref(m)) == moe.MOE_ERR_INVALID_ARG
+    cr = dict(c, weight_format="dtype")
+    assert _raw_forward(cr, 8) == moe.MOE_ERR_INVALID_ARG
+    L = moe.lib()
+    cc = moe.make_config(cr)
+    assert L.moe_router_logits(ctypes.byref(cc), 8, 0x1000, 0x1000, None, 0x1000, 0x100000,
+                               1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("bad", [dict(n_group=3), dict(n_group=65), dict(n_group=8, topk_group=0),
                                  dict(n_group=8, topk_group=9), dict(n_group=64),
                                  dict(n_group=32, topk_group=2), dict(n_group=-1)])

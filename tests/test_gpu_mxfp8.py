@@ -36,15 +36,20 @@ def _gpu():
 
 
 def oracle_view(inp):
-    """The inputs with every MX (MXFP8 or MXFP4) weight stack replaced by its
-    lazily dequantised float64 view."""
-    elem = "e2m1" if inp.cfg.get("weight_format") == "mxfp4" else "e4m3"
+    """The inputs with every MX (MXFP8 or MXFP4) expert weight stack replaced
+    by its lazily dequantised float64 view, and an MXFP8 router by its
+    dequantised values."""
     d = dict(inp.__dict__)
-    for w, key in (("w_gate", "gate"), ("w_up", "up"), ("w_down", "down"),
-                   ("ws_gate", "shared_gate"), ("ws_up", "shared_up"),
-                   ("ws_down", "shared_down")):
-        if d[w] is not None:
-            d[w] = O.MxStacked(d[w], inp.mx[key], elem)
+    wf = inp.cfg.get("weight_format", "dtype")
+    if wf != "dtype":
+        elem = "e2m1" if wf == "mxfp4" else "e4m3"
+        for w, key in (("w_gate", "gate"), ("w_up", "up"), ("w_down", "down"),
+                       ("ws_gate", "shared_gate"), ("ws_up", "shared_up"),
+                       ("ws_down", "shared_down")):
+            if d[w] is not None:
+                d[w] = O.MxStacked(d[w], inp.mx[key], elem)
+    if inp.cfg.get("router_format", "f32") == "mxfp8":
+        d["w_router"] = O.mx_dequantize(inp.w_router, inp.mx["router"])
     return synth.MoeInputs(**d)
 
 

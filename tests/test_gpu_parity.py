@@ -97,7 +97,7 @@ def run_stages(dev: Dev, deterministic=False):
     acc, out = z(T * H, f32), z(T * H, dt)
     yp = z(T * k * H, dt) if deterministic else None
     say(f"[stages] {c['hidden_size']}x{E}x{k} T={T} {c['dtype']}")
-    moe.moe_router_logits(c, T, dev.x, dev.w_router, logits, dev.ws)
+    moe.moe_router_logits(c, T, dev.x, dev.w_router, logits, dev.ws, mx=dev.mx)
     moe.moe_route(c, T, logits, dev.expert_bias, idx, w, counts)
     moe.moe_permute(c, T, idx, offs, sr, rp, dev.ws)
     moe.moe_grouped_gate_up_swiglu(c, T, dev.x, dev.w_gate, dev.w_up, dev.ws_gate, dev.ws_up,

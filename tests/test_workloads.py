@@ -139,3 +139,25 @@ def test_mxfp4_quantiser():
     synth._fill_normal(tmp, synth._stream(0, synth.TID_GATE, 5), cfg["w_std"], False)
     q, qs = synth.quantize_mxfp4(tmp)
     assert np.array_equal(a4.w_gate[5], q) and np.array_equal(a4.mx["gate"][5], qs)
+
+
+def test_mxfp8_router_is_the_quantised_fp32_router():
+    """The 8-bit router of the q4r8 workloads is the MXFP8 quantisation of the
+    same fp32 draw the fp32-router workload uses; the oracle refuses raw
+    codes (they have no value without their scales)."""
+    from oracle import moe_oracle as O
+    a = synth.generate(synth.config("trinity_nano_decode_T32_q4r8"))
+    b = synth.generate(synth.config("trinity_nano_decode_T32_mxfp4"))
+    codes, sc = synth.quantize_mxfp8(b.w_router)
+    assert np.array_equal(a.w_router, codes) and np.array_equal(a.mx["router"], sc)
+    assert np.array_equal(a.w_gate, b.w_gate) and np.array_equal(a.x, b.x)
+    with pytest.raises(ValueError):
+        O.as_f64(a.w_router)
+    wr = O.mx_dequantize(a.w_router, a.mx["router"])
+    # within MXFP8's error on the fp32 draw: half a step of 3 mantissa bits
+    # (2^-4 of an element), or the OCP rule's clip of a block maximum that
+    # lands in (448, 512) x scale to 448 (at most 1/8 of the block maximum)
+    w64 = b.w_router.astype(np.float64)
+    blk_max = np.abs(w64).reshape(128, -1, 32).max(2, keepdims=True)
+    err = np.abs(wr - w64).reshape(128, -1, 32)
+    assert np.all(err <= np.maximum(np.abs(w64).reshape(128, -1, 32) * 2.0 ** -4, blk_max / 8))

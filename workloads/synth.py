@@ -55,7 +55,7 @@ def _cfg(**kw):
         route_scale=1.0, hidden_act="silu", act_alpha=1.702, act_limit=7.0,
         act_beta=1.0, x_scale=1.0, w_std=0.02, router_bf16_values=True,
         skew=None, rms_norm_eps=1e-5, norm_add_one=0, norm_w_std=0.1,
-        weight_format="dtype", n_group=1, topk_group=1,
+        weight_format="dtype", n_group=1, topk_group=1, router_format="f32",
     )
     base.update(kw)
     if base.get("shared_intermediate_size", 0) == 0:
@@ -129,7 +129,8 @@ CONFIGS: dict[str, dict] = {
         shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
         route_scale=2.826, router_bf16_values=False, weight_format="mxfp8"),
     # 4-bit expert weights (the Trinity checkpoints are 4-bit, router at 8
-    # bits; read as MXFP4), and the M3 decode layer with the same format
+    # bits; read as MXFP4 and MXFP8), and the M3 decode layer with the same
+    # expert format
     "trinity_nano_decode_T32_mxfp4": _cfg(
         T=32, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
         moe_intermediate_size=256, num_shared_experts=1,
@@ -140,6 +141,18 @@ CONFIGS: dict[str, dict] = {
         moe_intermediate_size=256, num_shared_experts=1,
         shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
         route_scale=2.826, router_bf16_values=False, weight_format="mxfp4"),
+    "trinity_nano_decode_T32_q4r8": _cfg(
+        T=32, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
+        moe_intermediate_size=256, num_shared_experts=1,
+        shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
+        route_scale=2.826, router_bf16_values=False, weight_format="mxfp4",
+        router_format="mxfp8"),
+    "trinity_nano_prefill_T8192_q4r8": _cfg(
+        T=8192, hidden_size=1024, num_experts=128, num_experts_per_tok=8,
+        moe_intermediate_size=256, num_shared_experts=1,
+        shared_intermediate_size=256, dtype="bf16", bias_limit=0.05,
+        route_scale=2.826, router_bf16_values=False, weight_format="mxfp4",
+        router_format="mxfp8"),
     "minimax_m3_decode_T64_mxfp4": _cfg(
         T=64, hidden_size=6144, num_experts=128, num_experts_per_tok=4,
         moe_intermediate_size=3072, num_shared_experts=1,
@@ -162,7 +175,8 @@ def layer_keys(cfg: dict) -> dict:
             "num_shared_experts", "moe_intermediate_size",
             "shared_intermediate_size", "shared_packed", "score_func",
             "route_norm", "route_scale", "hidden_act", "act_alpha",
-            "act_limit", "act_beta", "dtype", "weight_format", "n_group", "topk_group")
+            "act_limit", "act_beta", "dtype", "weight_format", "n_group", "topk_group",
+            "router_format")
     return {k: cfg[k] for k in keys}
 
 
@@ -238,6 +252,8 @@ class MoeInputs:
     ws_up: np.ndarray | None = None
     ws_down: np.ndarray | None = None  # [S, H, I_s]
     meta: dict = field(default_factory=dict)
+    # MXFP8 router (router_format "mxfp8"): w_router holds E4M3 codes [E, H]
+    # and mx["router"] their scales [H/32, E].
     # MX expert weights: the w_* / ws_* arrays hold E4M3 codes (MXFP8, uint8
     # [., N, K]) or packed E2M1 codes (MXFP4, uint8 [., N, K/2], input 2j in
     # the low nibble of byte j) and mx holds their E8M0 scales, block-major:
@@ -304,6 +320,14 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
     bias = ((u * np.float32(2.0) - np.float32(1.0)) * lim).astype(np.float32)
 
     inp = MoeInputs(cfg=dict(cfg, T=T), x=x, w_router=wr, expert_bias=bias)
+    rf = cfg.get("router_format", "f32")
+    if rf not in ("f32", "mxfp8"):
+        raise ValueError(f"unknown router_format {rf!r}")
+    if rf == "mxfp8":
+        # the 8-bit router: the same fp32 draw, quantised (codes [E, H],
+        # scales [H/32, E])
+        inp.w_router, rsc = quantize_mxfp8(wr)
+        inp.mx = {"router": rsc}
 
     jobs = [(_xblock, b) for b in range(nblk)]
 
@@ -324,9 +348,10 @@ def generate(cfg: dict, T: int | None = None, experts: bool = True,
         inp.w_up = np.empty((Etot, I, H // kdiv), edt)
         inp.w_down = np.empty((Etot, H, I // kdiv), edt)
         if mx:
-            inp.mx = {"gate": np.empty((Etot, H // 32, I), np.uint8),
-                      "up": np.empty((Etot, H // 32, I), np.uint8),
-                      "down": np.empty((Etot, I // 32, H), np.uint8)}
+            inp.mx = dict(inp.mx or {},
+                          gate=np.empty((Etot, H // 32, I), np.uint8),
+                          up=np.empty((Etot, H // 32, I), np.uint8),
+                          down=np.empty((Etot, I // 32, H), np.uint8))
         scl = (lambda key: inp.mx[key]) if mx else (lambda key: None)
         for arr, key, tid in ((inp.w_gate, "gate", TID_GATE), (inp.w_up, "up", TID_UP),
                               (inp.w_down, "down", TID_DOWN)):
