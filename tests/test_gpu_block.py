@@ -157,6 +157,12 @@ BLOCK = {
                                         num_experts_per_tok=8, moe_intermediate_size=256,
                                         num_shared_experts=1, shared_intermediate_size=256,
                                         route_scale=2.826, weight_format="mxfp4"),
+    # ... and with the 8-bit router as well (the q4r8 checkpoint widths)
+    "trinity_like_q4r8_decode": custom(T=32, hidden_size=1024, num_experts=64,
+                                       num_experts_per_tok=8, moe_intermediate_size=256,
+                                       num_shared_experts=1, shared_intermediate_size=256,
+                                       route_scale=2.826, weight_format="mxfp4",
+                                       router_bf16_values=False, router_format="mxfp8"),
 }
 
 

@@ -42,6 +42,10 @@ CASES = {
     "mxfp4_decode": custom(T=48, hidden_size=1024, num_experts=16, num_experts_per_tok=4,
                            moe_intermediate_size=256, num_shared_experts=1, shared_packed=1,
                            hidden_act="swigluoai", route_scale=2.0, weight_format="mxfp4"),
+    "q4r8_decode": custom(T=32, hidden_size=1024, num_experts=64, num_experts_per_tok=8,
+                          moe_intermediate_size=256, num_shared_experts=1,
+                          shared_intermediate_size=256, route_scale=2.826,
+                          weight_format="mxfp4", router_format="mxfp8"),
 }
 
 

@@ -46,6 +46,10 @@ CASES = {
                                 moe_intermediate_size=128, num_shared_experts=2,
                                 shared_intermediate_size=64, x_scale=16.0,
                                 router_format="mxfp8"),
+    "softmax_grouped": custom(T=90, hidden_size=256, num_experts=64, num_experts_per_tok=6,
+                              moe_intermediate_size=128, num_shared_experts=1, n_group=8,
+                              topk_group=3, score_func="softmax", route_scale=2.5,
+                              router_format="mxfp8"),
     "q4r8_decode": custom(T=32, hidden_size=1024, num_experts=64, num_experts_per_tok=8,
                           moe_intermediate_size=256, num_shared_experts=1,
                           shared_intermediate_size=256, route_scale=2.826,
