@@ -743,3 +743,75 @@ def test_route_all_groups_kept_is_plain_topk():
     b = O.route(L, bias, 6, "softmax", True, 2.0, n_group=8, topk_group=8)
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
 
+
+
+# --------------------------------------------------------------------------
+# storage decoding and the routing report's boundary gap
+
+def _hand_value(s):
+    """A hand-written exact value: "1", "-0", "inf", "2^-133", "127*2^-133"."""
+    if s in ("inf", "-inf"):
+        return float(s)
+    sign = -1.0 if s.startswith("-") else 1.0
+    s = s.lstrip("-")
+    mult = 1.0
+    if "*" in s:
+        m, s = s.split("*")
+        mult = float(int(m))
+    if s.startswith("2^"):
+        return sign * mult * math.ldexp(1.0, int(s[2:]))
+    return sign * mult * float(s)
+
+
+def test_as_f64_bf16_bits_hand_values():
+    """bf16 bit patterns through the oracle's storage decoder, against values
+    worked by hand from the format (the path every bf16 workload value takes
+    into the oracle)."""
+    g = _gold("bf16_hand_example.json")
+    bits = np.array([int(b, 16) for b, _ in g["values"]], dtype=np.uint16)
+    want = np.array([_hand_value(v) for _, v in g["values"]], dtype=np.float64)
+    got = O.as_f64(bits)
+    assert got.dtype == np.float64
+    assert np.array_equal(got, want)
+    # the sign of zero is kept (0x8000 is -0)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    nan = O.as_f64(np.array([int(b, 16) for b in g["nan"]], dtype=np.uint16))
+    assert np.all(np.isnan(nan))
+    # shape is kept; a 2-D array decodes element by element
+    two = O.as_f64(bits[:4].reshape(2, 2))
+    assert two.shape == (2, 2) and np.array_equal(two.reshape(-1), want[:4])
+
+
+def test_as_f64_bf16_catches_a_shift_before_widening():
+    """A plausible slip, shifting the 16-bit array before widening it, loses
+    every bit: the hand values reject it (planted on the CPU, in a copy)."""
+    g = _gold("bf16_hand_example.json")
+    bits = np.array([int(b, 16) for b, _ in g["values"]], dtype=np.uint16)
+    want = np.array([_hand_value(v) for _, v in g["values"]], dtype=np.float64)
+
+    def shifted_first(a):
+        return (a << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+    def low_half(a):  # the bits placed in the low half of the binary32
+        return a.astype(np.uint32).view(np.float32).astype(np.float64)
+
+    for bad in (shifted_first, low_half):
+        with np.errstate(all="ignore"):
+            assert not np.array_equal(bad(bits), want)
+
+
+def test_as_f64_other_dtypes():
+    """fp32 values widen exactly; MX codes without scales are refused."""
+    v = np.array([1.0, -3.5, 2.0 ** -140, 3.4e38], dtype=np.float32)
+    assert np.array_equal(O.as_f64(v), v.astype(np.float64))
+    with pytest.raises(ValueError):
+        O.as_f64(np.zeros(4, np.uint8))
+
+
+def test_boundary_gap_hand_examples():
+    """The smallest k-th minus (k+1)-th key, worked by hand on dyadic keys
+    (exact tie -> 0, no boundary -> inf)."""
+    for c in _gold("boundary_gap_hand_example.json")["cases"]:
+        keys = np.array([[float(v) for v in row] for row in c["keys"]], dtype=np.float64)
+        want = float(c["gap"])
+        assert O.boundary_gap(keys, c["k"]) == want, c["why"]
