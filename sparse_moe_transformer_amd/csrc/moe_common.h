@@ -53,22 +53,6 @@ __device__ __forceinline__ float act_apply(float g, float u, const ActParams& a)
 }
 
 // ---------------------------------------------------------------------------
-// XCD-aware block remap. The hardware hands consecutive workgroup ids to the
-// 8 XCDs round-robin; remapping makes a run of consecutive *logical* tiles
-// land on one XCD, so tiles that share weights share that XCD's L2.
-
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
-  const uint32_t nx = 8;
-  uint32_t per = nblocks / nx;         // full rounds
-  uint32_t rem = nblocks % nx;
-  uint32_t xcd = bid % nx;
-  uint32_t slot = bid / nx;
-  // XCDs [0, rem) own per+1 logical blocks, the rest own per.
-  uint32_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  return base + slot;
-}
-
-// ---------------------------------------------------------------------------
 // Eight consecutive elements of a row as fp32 (16-byte loads and stores of
 // bf16, two of fp32); bf16 stores round to nearest even.
 

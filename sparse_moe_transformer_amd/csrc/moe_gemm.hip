@@ -753,7 +753,6 @@ __global__ void __launch_bounds__(NTHR) moe_down_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 
-size_t gemm_lds_bytes(int) { return 0; }
 int gemm_bm() { return BM; }
 
 static int g_num_cus = 0;

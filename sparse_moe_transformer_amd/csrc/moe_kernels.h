@@ -40,7 +40,6 @@ struct GemmArgs {
   const uint8_t* sws1;
 };
 
-size_t gemm_lds_bytes(int E);
 int gemm_bm();
 hipError_t launch_gate_up(const GemmArgs& g, int dtype, hipStream_t st);
 hipError_t launch_down_shared(const GemmArgs& g, int dtype, hipStream_t st);
