@@ -133,10 +133,13 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray, elem: str = "e4m3") -> 
     inputs): w[n, k] = element(n, k) * 2^(s[k/32, n] - 127).
     elem "e4m3" (MXFP8): codes [N, K], one byte per input;
     elem "e2m1" (MXFP4): codes [N, K/2], two inputs per byte (unpack_fp4)."""
+    # each element value is a function of its code alone: evaluated once per
+    # possible code, then looked up (the same numbers, without re-deriving
+    # them for every one of the N*K inputs)
     if elem == "e2m1":
-        vals = e2m1_value(unpack_fp4(codes))
+        vals = e2m1_value(np.arange(16, dtype=np.uint8))[unpack_fp4(codes)]
     elif elem == "e4m3":
-        vals = e4m3_value(codes)
+        vals = e4m3_value(np.arange(256, dtype=np.uint8))[np.asarray(codes, dtype=np.uint8)]
     else:
         raise ValueError(f"unknown MX element format {elem!r}")
     K = vals.shape[1]
