@@ -5,11 +5,21 @@
 A step is one pass of the whole layer (router GEMM, routing, grouping,
 gate/up + activation, down + combine, output cast) over one batch of seeded
 synthetic inputs that are resident in HBM before timing starts, through the
-layer's single entry point moe_layer_forward, called eagerly on one stream
-(--graph on: captured once in a HIP graph and replayed), with the K timed
-steps bracketed by device synchronisation. The per-stage breakdown comes
-from a separate eager pass over the stage entry points with HIP events
-around each call.
+layer's single entry point moe_layer_forward on one stream.
+
+Timing protocol (every timed number): W untimed warm-up steps, then K timed
+steps; before each timed step a 1 GiB buffer (more than the 256 MB MALL) is
+written, outside the timed events, so expert weights come from HBM as they
+do in a many-layer model; HIP events on the layer's stream bracket the layer
+call alone, and the step time is the median of the K (min and max beside it).
+The K timed steps are bracketed by device synchronisation. The per-stage
+breakdown comes from a second pass over the stage entry points with the same
+flushes and HIP events around each call.
+
+By default the headline is the MiniMax-M3-shaped layer at T = 8192 (the
+prefill target, MFMA-bound), and the same JSON line carries the two decode
+layers (MiniMax-M3-shaped at T = 64, Trinity-like at T = 32; HBM-bound),
+each with its own roofline object; --workload NAME benches one workload.
 
 Prints ONE JSON line: tokens/s of the layer, its TFLOP/s (fraction of bf16
 MFMA peak) and GB/s (fraction of HBM peak), the roofline of the dominant
@@ -35,7 +45,11 @@ METRIC = ("MoE-layer tokens/s + % bf16 MFMA peak (prefill) / % HBM GB/s (decode)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-DEFAULT_WORKLOAD = "afmoe_default_T4096"
+DEFAULT_WORKLOAD = "minimax_m3_prefill_T8192"
+# decode layers carried in the default line; the M3 decode batch is the first
+# 64 tokens of the M3 prefill batch (same weights)
+DECODE_WORKLOADS = ("minimax_m3_decode_T64", "trinity_nano_decode_T32")
+FLUSH_BYTES = 1 << 30
 
 
 def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
@@ -328,21 +342,189 @@ def block_measurements(moe, synth, cfg, keys, T, ordered, args, stream, t, layer
                         "gbs": gbs(b_comb, ms_comb), "frac_hbm_peak": gbs(b_comb, ms_comb) / PEAK_HBM_GBS}}
 
 
+def upload(moe, inp, T=None):
+    """The workload's tensors on the GPU (x limited to its first T rows)."""
+    d = moe.to_device
+    x = inp.x if T is None else inp.x[:T]
+    return dict(x=d(x), wr=d(inp.w_router), b=d(inp.expert_bias), wg=d(inp.w_gate),
+                wu=d(inp.w_up), wd=d(inp.w_down), sg=d(inp.ws_gate), su=d(inp.ws_up),
+                sd=d(inp.ws_down),
+                mx={key: d(v) for key, v in inp.mx.items()} if inp.mx is not None else None)
+
+
+def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
+    """Time one workload by the protocol: stage-call pass and layer pass, each
+    with a 1 GiB flush before every timed step and HIP events around the
+    layer (or each stage); medians over `steps` steps; plus the warm figure of
+    back-to-back calls. Returns timings and the stage tensors."""
+    import torch
+    keys = synth_keys(cfg)
+    E, k, H, I = cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"], \
+        cfg["moe_intermediate_size"]
+    S = cfg["num_shared_experts"]
+    Is = cfg["shared_intermediate_size"] or I
+    dt = moe.torch_dtype(keys)
+    dev = t["x"].device
+    ws = moe.alloc_block_workspace(keys, T)
+    f32, i32 = torch.float32, torch.int32
+    st = dict(
+        logits=torch.empty(T * E, dtype=f32, device=dev),
+        idx=torch.empty(T * k, dtype=i32, device=dev),
+        w=torch.empty(T * k, dtype=f32, device=dev),
+        offs=torch.empty(E + 1, dtype=i32, device=dev),
+        sr=torch.empty(T * k, dtype=i32, device=dev),
+        rp=torch.empty(T * k, dtype=i32, device=dev),
+        h=torch.empty(T * k * I, dtype=dt, device=dev),
+        hs=torch.empty(T * S * Is, dtype=dt, device=dev) if S else None,
+        acc=torch.empty(T * H, dtype=f32, device=dev),
+        out=torch.empty(T * H, dtype=dt, device=dev),
+        yp=torch.empty(T * k * H, dtype=dt, device=dev) if ordered else None,
+        ws=ws)
+    x, mx = t["x"], t["mx"]
+    stages = ["router", "route", "permute", "gate_up", "down", "combine"]
+
+    def step(events=None):
+        s = torch.cuda.current_stream()
+        rec = (lambda i: events[i].record(s)) if events else (lambda i: None)
+        rec(0)
+        moe.moe_router_logits(keys, T, x, t["wr"], st["logits"], ws, s, mx=mx)
+        rec(1)
+        moe.moe_route(keys, T, st["logits"], t["b"], st["idx"], st["w"], None, s)
+        rec(2)
+        moe.moe_permute(keys, T, st["idx"], st["offs"], st["sr"], st["rp"], ws, s)
+        rec(3)
+        moe.moe_grouped_gate_up_swiglu(keys, T, x, t["wg"], t["wu"], t["sg"], t["su"],
+                                       st["offs"], st["sr"], st["h"], st["hs"], ws, s, mx=mx)
+        rec(4)
+        moe.moe_grouped_down(keys, T, st["h"], t["wd"], st["hs"], t["sd"], st["offs"], st["sr"],
+                             st["w"], st["acc"], st["yp"], ws, s, mx=mx)
+        rec(5)
+        moe.moe_combine(keys, T, st["acc"], st["yp"], st["rp"], st["w"], st["out"], s)
+        rec(6)
+
+    def layer():
+        moe.moe_layer_forward(keys, T, x, t["wr"], t["b"], t["wg"], t["wu"], t["wd"], t["sg"],
+                              t["su"], t["sd"], None, None, None, None, st["out"], int(ordered),
+                              ws, torch.cuda.current_stream(), mx=mx)
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # stage-call pass: flush, then the six stage calls with events between
+    sev = [[ev() for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        step(sev[i])
+    torch.cuda.synchronize()
+    per_stage = {s: [sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(steps)]
+                 for j, s in enumerate(stages)}
+    stage_ms = {s: float(np.median(v)) for s, v in per_stage.items()}
+    gate_up_mean = float(np.mean(per_stage["gate_up"]))
+
+    # the timed steps: flush (outside the events), then the layer call alone;
+    # everything is queued on one stream and synchronised once, so the flush
+    # also hides the host's launch of the layer's kernels
+    for _ in range(warmup):
+        layer()
+    torch.cuda.synchronize()
+    lev = [(ev(), ev()) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        lev[i][0].record(stream)
+        layer()
+        lev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = [a.elapsed_time(b) for a, b in lev]
+
+    # warm: back-to-back calls (weights partly in the MALL), for comparison
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer()
+    torch.cuda.synchronize()
+    ms_warm = (time.perf_counter() - t0) * 1e3 / steps
+    return dict(ms=float(np.median(per_call)), ms_min=float(np.min(per_call)),
+                ms_max=float(np.max(per_call)), wall_s=wall, ms_warm=ms_warm,
+                stage_ms=stage_ms, gate_up_mean_ms=gate_up_mean, st=st, keys=keys,
+                stream=stream)
+
+
+def synth_keys(cfg):
+    from workloads import synth
+    return synth.layer_keys(cfg)
+
+
+def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
+    """The measured figures of one workload: tokens/s, the layer against both
+    rooflines, the dominant kernel's roofline object and the routing report."""
+    alg = algorithmic(cfg, T, idx_h)
+    ms = m["ms"]
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+    peak_mm = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_MFMA_TFLOPS
+    k, E = cfg["num_experts_per_tok"], cfg["num_experts"]
+    # prefill-sized batches are priced against the MFMA peak, decode-sized
+    # ones (at most 32 rows per expert on average) against HBM
+    decode = T * k <= 32 * E
+    gu_ms = m["gate_up_mean_ms"]
+    kname = gate_up_kernel(cfg, T)
+    gu_tf = alg["gate_up_flops"] / (gu_ms * 1e-3) / 1e12
+    gu_gb = alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9
+    if decode:
+        roof = {"bound": "hbm", "achieved": gu_gb, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_tf, "peak": peak_mm, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profile(kname, name, gemm_source_sha())
+    roof["kernel"] = kname
+    roof["ms_per_launch"] = gu_ms
+    roof["launches_timed"] = steps
+    roof["frac_other_roof"] = (gu_gb / PEAK_HBM_GBS) if not decode else (gu_tf / peak_mm)
+    layer = {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
+             "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"], "bytes": alg["bytes"],
+             "arith_intensity": alg["flops"] / alg["bytes"],
+             "gate_up_flops": alg["gate_up_flops"], "gate_up_bytes": alg["gate_up_bytes"],
+             "bound": "hbm" if decode else "mfma", "touched_experts": alg["touched"],
+             "stage_ms": m["stage_ms"], "ms_median": ms, "ms_min": m["ms_min"],
+             "ms_max": m["ms_max"], "ms_per_step_warm": m["ms_warm"],
+             "frac_bf16_peak_warm": alg["flops"] / (m["ms_warm"] * 1e-3) / 1e12 / peak_mm,
+             "frac_hbm_peak_warm": alg["bytes"] / (m["ms_warm"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+             "routing": routing_report(cfg, idx_h, logits_h, bias)}
+    return layer, roof
+
+
+def run_workload(moe, name, cfg, t, T, args, flush, steps):
+    import torch
+    print(f"[bench] timing {name} (T={T}, {steps} steps)", file=sys.stderr, flush=True)
+    m = measure_layer(moe, cfg, t, T, steps, args.warmup, args.combine == "ordered", flush)
+    st = m["st"]
+    E, k = cfg["num_experts"], cfg["num_experts_per_tok"]
+    idx_h = st["idx"].view(T, k).cpu().numpy()
+    logits_h = st["logits"].view(T, E).cpu().numpy()
+    torch.cuda.synchronize()
+    return m, idx_h, logits_h
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps of the headline workload (decode layers: 5x as many)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None,
+                    help="bench one workload only (default: the M3-shaped T=8192 layer with "
+                         "the two decode layers nested)")
     ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="tokens for the CPU oracle baseline (0 = skip)")
+                    help="tokens for the CPU oracle baseline (0 = skip; default 1024, or T "
+                         "if smaller)")
     ap.add_argument("--combine", choices=["atomic", "ordered"], default="ordered",
                     help="down-projection combine: fp32 atomics into the output rows, or "
                          "per-row expert outputs summed in a fixed order by moe_combine")
-    ap.add_argument("--graph", choices=["on", "off"], default="off",
-                    help="time replays of the layer call captured once in a HIP graph (on) or "
-                         "eager calls (off, the default: measured faster on this stack); the "
-                         "per-stage breakdown always comes from an eager pass")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the measurements of the MoE block around the layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -381,179 +563,73 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     moe.lib()
-    cfg = synth.config(args.workload)
+    name = args.workload or DEFAULT_WORKLOAD
+    with_decode = args.workload is None
+    cfg = synth.config(name)
     keys = synth.layer_keys(cfg)
     T = cfg["T"]
     E, k, H, I = cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"], \
         cfg["moe_intermediate_size"]
     S = cfg["num_shared_experts"]
     Is = cfg["shared_intermediate_size"] or I
-    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     inp = synth.generate(cfg)
-    d = moe.to_device
-    x, wr, b = d(inp.x), d(inp.w_router), d(inp.expert_bias)
-    wg, wu, wd = d(inp.w_gate), d(inp.w_up), d(inp.w_down)
-    sg, su, sd = d(inp.ws_gate), d(inp.ws_up), d(inp.ws_down)
-    mx = {key: d(v) for key, v in inp.mx.items()} if inp.mx is not None else None
-    dt = moe.torch_dtype(keys)
-    dev = x.device
-    # the block's workspace holds the layer's, plus the normalised rows
-    ws = moe.alloc_block_workspace(keys, T)
-    f32, i32 = torch.float32, torch.int32
-    logits = torch.empty(T * E, dtype=f32, device=dev)
-    idx = torch.empty(T * k, dtype=i32, device=dev)
-    w = torch.empty(T * k, dtype=f32, device=dev)
-    offs = torch.empty(E + 1, dtype=i32, device=dev)
-    sr = torch.empty(T * k, dtype=i32, device=dev)
-    rp = torch.empty(T * k, dtype=i32, device=dev)
-    h = torch.empty(T * k * I, dtype=dt, device=dev)
-    hs = torch.empty(T * S * Is, dtype=dt, device=dev) if S else None
-    acc = torch.empty(T * H, dtype=f32, device=dev)
-    out = torch.empty(T * H, dtype=dt, device=dev)
-    ordered = args.combine == "ordered"
-    yp = torch.empty(T * k * H, dtype=dt, device=dev) if ordered else None
-    stream = torch.cuda.current_stream()
+    t = upload(moe, inp)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=t["x"].device)
+    decode_steps = 5 * args.steps
 
-    stages = ["router", "route", "permute", "gate_up", "down", "combine"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
+    steps = decode_steps if T * k <= 32 * E else args.steps
+    m, idx_h, logits_h = run_workload(moe, name, cfg, t, T, args, flush, steps)
+    layer, roof = layer_report(name, cfg, T, m, idx_h, logits_h, inp.expert_bias, steps)
+    ms = m["ms"]
 
-    def step(events=None):
-        # the stream current at call time: the capture stream inside graph capture
-        st = torch.cuda.current_stream()
-        rec = (lambda i: events[i].record(st)) if events else (lambda i: None)
-        rec(0)
-        moe.moe_router_logits(keys, T, x, wr, logits, ws, st, mx=mx)
-        rec(1)
-        moe.moe_route(keys, T, logits, b, idx, w, None, st)
-        rec(2)
-        moe.moe_permute(keys, T, idx, offs, sr, rp, ws, st)
-        rec(3)
-        moe.moe_grouped_gate_up_swiglu(keys, T, x, wg, wu, sg, su, offs, sr, h, hs, ws, st, mx=mx)
-        rec(4)
-        moe.moe_grouped_down(keys, T, h, wd, hs, sd, offs, sr, w, acc, yp, ws, st, mx=mx)
-        rec(5)
-        moe.moe_combine(keys, T, acc, yp, rp, w, out, st)
-        rec(6)
+    blk = None
+    if not args.no_block:
+        st = m["st"]
+        blk = block_measurements(moe, synth, cfg, keys, T, args.combine == "ordered", args,
+                                 m["stream"],
+                                 dict(x=t["x"], wr=t["wr"], b=t["b"], wg=t["wg"], wu=t["wu"],
+                                      wd=t["wd"], sg=t["sg"], su=t["su"], sd=t["sd"],
+                                      acc=st["acc"], yp=st["yp"], rp=st["rp"], w=st["w"],
+                                      out=st["out"], ws=st["ws"], mx=t["mx"]), m["ms_warm"])
+    del m
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # eager pass over the stage entry points: per-stage HIP events
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    ms_stages = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage_ms = {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-                for j, s in enumerate(stages)}
-
-    # the timed step: the whole layer through its single entry point
-    # (intermediates in the library workspace)
-    def layer():
-        moe.moe_layer_forward(keys, T, x, wr, b, wg, wu, wd, sg, su, sd, None, None, None, None,
-                              out, int(ordered), ws, torch.cuda.current_stream(), mx=mx)
-
-    for _ in range(args.warmup):
-        layer()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        layer()
-    torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-    if args.graph == "on":
-        # one layer call captured once; every replay runs all of its kernels
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            layer()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    else:
-        ms = ms_eager
-
-    # HBM-cold steps: before each, write a 1 GiB buffer (more than the 256 MB
-    # MALL), then time only the layer call with events on the same stream,
-    # so expert weights come from HBM (what a multi-layer model sees: every
-    # layer's weights differ)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    n_cold = max(3, min(args.steps, 10))
-    cold = []
-    for _ in range(n_cold):
-        flush.fill_(1)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        layer()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(c0.elapsed_time(c1))
+    decode = None
+    if with_decode:
+        decode = {}
+        for dname in DECODE_WORKLOADS:
+            dcfg = synth.config(dname)
+            dT = dcfg["T"]
+            same = {kk: v for kk, v in dcfg.items() if kk not in ("T", "name")} == \
+                {kk: v for kk, v in cfg.items() if kk not in ("T", "name")}
+            if same and dT <= T:
+                # the first dT tokens of the same batch, same weights
+                dinp, dt_ = inp, dict(t, x=t["x"][:dT])
+            else:
+                print(f"[bench] generating {dname}", file=sys.stderr, flush=True)
+                dinp = synth.generate(dcfg)
+                dt_ = upload(moe, dinp)
+            dm, didx, dlog = run_workload(moe, dname, dcfg, dt_, dT, args, flush, decode_steps)
+            dl, droof = layer_report(dname, dcfg, dT, dm, didx, dlog, dinp.expert_bias,
+                                     decode_steps)
+            decode[dname] = {"tokens_per_s": dT / (dm["ms"] * 1e-3), "ms_per_step": dm["ms"],
+                             "steps": decode_steps, "layer": dl, "roofline": droof}
+            del dm
     del flush
-    ms_cold = float(np.median(cold))
-
-    # the spread of single warm calls (each timed alone with events)
-    per_call = []
-    for _ in range(args.steps):
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        p0.record(stream)
-        layer()
-        p1.record(stream)
-        torch.cuda.synchronize()
-        per_call.append(p0.elapsed_time(p1))
-
-    idx_h = idx.view(T, k).cpu().numpy()
-    alg = algorithmic(cfg, T, idx_h)
-    routing = routing_report(cfg, idx_h, logits.view(T, E).cpu().numpy(), inp.expert_bias)
-    tflops = alg["flops"] / (ms * 1e-3) / 1e12
-    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
-    peak_mm = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_MFMA_TFLOPS
-    ai = alg["flops"] / alg["bytes"]
-    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
-
-    # roofline of the dominant kernel: the grouped gate/up GEMM + activation,
-    # its average duration over the K timed steps of the stage-call pass (HIP
-    # events on the bench stream around each gate/up launch, inside whole
-    # layer steps). Not back-to-back launches of the kernel alone: run without
-    # the layer's other kernels in between, the dense MFMA load lowers the
-    # clock within a few launches (gate/up on the AFMoE workload: 410 us in
-    # the layer, up to 600 us back to back), a state the layer never reaches.
-    gu_ms = stage_ms["gate_up"]
-    n_rl = args.steps
-    sha = gemm_source_sha()
-    gu_ai = alg["gate_up_flops"] / alg["gate_up_bytes"]
-    if gu_ai >= ridge:
-        roof = {"bound": "mfma", "achieved": alg["gate_up_flops"] / (gu_ms * 1e-3) / 1e12,
-                "peak": peak_mm, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    kname = gate_up_kernel(cfg, T)
-    roof["traffic"] = traffic_from_profile(kname, args.workload, sha)
-    roof["kernel"] = kname
-    roof["ms_per_launch"] = gu_ms
-    roof["launches_timed"] = n_rl
-
-    blk = block_measurements(moe, synth, cfg, keys, T, ordered, args, stream,
-                             dict(x=x, wr=wr, b=b, wg=wg, wu=wu, wd=wd, sg=sg, su=su, sd=sd,
-                                  acc=acc, yp=yp, rp=rp, w=w, out=out, ws=ws, mx=mx), ms_eager)
 
     sample = args.cpu_sample
     if sample is None:
-        sample = T
-    cpu = cpu_baseline(args.workload, cfg, inp, sample) if sample > 0 else None
+        sample = min(T, 1024)
+    if sample > 0:
+        print(f"[bench] float64 oracle on {sample} tokens of {name}", file=sys.stderr, flush=True)
+    cpu = cpu_baseline(name, cfg, inp, sample) if sample > 0 else None
 
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -561,29 +637,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded; shapes of the workload, random weights)",
-        "config": {"workload": args.workload, "tokens": T, "hidden_size": H, "num_experts": E,
+        "config": {"workload": name, "tokens": T, "hidden_size": H, "num_experts": E,
                    "num_experts_per_tok": k, "moe_intermediate_size": I,
                    "num_shared_experts": S, "shared_intermediate_size": Is,
                    "shared_packed": cfg["shared_packed"], "hidden_act": cfg["hidden_act"],
                    "expert_weights": (cfg["weight_format"]
                                       if cfg.get("weight_format", "dtype") != "dtype"
                                       else cfg["dtype"]),
-                   "combine": args.combine, "graph": args.graph, "entry": "moe_layer_forward"},
-        "layer": {"tflops": tflops, "frac_bf16_peak": tflops / peak_mm, "gbs": gbs,
-                  "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"],
-                  "bytes": alg["bytes"], "arith_intensity": ai,
-                  "gate_up_flops": alg["gate_up_flops"], "gate_up_bytes": alg["gate_up_bytes"],
-                  "bound": "mfma" if ai >= ridge else "hbm",
-                  "touched_experts": alg["touched"], "stage_ms": stage_ms,
-                  "ms_per_step_eager": ms_eager, "ms_per_step_stage_calls": ms_stages,
-                  "ms_per_step_hbm_cold": ms_cold,
-                  "gbs_hbm_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9,
-                  "frac_hbm_peak_cold": alg["bytes"] / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                  "single_call_ms": {"median": float(np.median(per_call)),
-                                     "min": float(np.min(per_call)),
-                                     "max": float(np.max(per_call))},
-                  "routing": routing},
+                   "combine": args.combine, "entry": "moe_layer_forward",
+                   "timing": "median of K steps, 1 GiB flush before each (outside the events)"},
+        "layer": layer,
         "roofline": roof,
+        "decode": decode,
         "block": blk,
         "cpu_baseline": cpu,
     }

@@ -105,3 +105,31 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
+    """The roofline object of a prefill-sized batch is the gate/up kernel
+    against the bf16 MFMA peak; a decode-sized batch (at most 32 rows per
+    expert on average) against HBM; achieved = algorithmic work / the
+    kernel's mean time."""
+    from workloads import synth
+    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, gate_up_mean_ms=1.0,
+             stage_ms={"gate_up": 1.0})
+    for name, bound in (("minimax_m3_prefill_T8192", "mfma"), ("minimax_m3_decode_T64", "hbm"),
+                        ("trinity_nano_decode_T32", "hbm")):
+        cfg = synth.config(name)
+        T, E, k = cfg["T"], cfg["num_experts"], cfg["num_experts_per_tok"]
+        idx = (np.arange(T * k).reshape(T, k) % E).astype(np.int64)
+        L = np.zeros((T, E), np.float32)
+        layer, roof = bench.layer_report(name, cfg, T, m, idx, L, np.zeros(E, np.float32), 5)
+        alg = bench.algorithmic(cfg, T, idx)
+        assert roof["bound"] == bound and layer["bound"] == bound
+        if bound == "mfma":
+            assert roof["achieved"] == pytest.approx(alg["gate_up_flops"] / 1e-3 / 1e12)
+            assert roof["peak"] == bench.PEAK_BF16_TFLOPS and roof["unit"] == "TFLOP/s"
+        else:
+            assert roof["achieved"] == pytest.approx(alg["gate_up_bytes"] / 1e-3 / 1e9)
+            assert roof["peak"] == bench.PEAK_HBM_GBS and roof["unit"] == "GB/s"
+        assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"])
+        assert layer["frac_hbm_peak"] == pytest.approx(alg["bytes"] / 2e-3 / 1e9 / 8000.0)
+        assert layer["frac_bf16_peak"] == pytest.approx(alg["flops"] / 2e-3 / 1e12 / 2516.6)
