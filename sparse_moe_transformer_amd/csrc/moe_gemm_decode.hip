@@ -121,9 +121,8 @@ __device__ __forceinline__ int b_row_fp8(int j) {
 // that the compiler does not track them: its tracking merges pending LDS
 // writes conservatively at every join and then waits for all loads before the
 // next LDS read. All waits for these loads are the explicit vmcnt waits and
-// barriers of the step loop. The LDS address goes in as an m0 operand
-// ("{m0}" constraint), so the compiler itself sets m0 for each statement and
-// knows the register is read there.
+// barriers of the step loop. Every direct load of this kernel goes through
+// these two functions, so the compiler itself never relies on m0 here.
 // a wave-uniform pointer, moved to scalar registers
 __device__ __forceinline__ const char* sptr(const char* p) {
   const uint64_t u = (uint64_t)(uintptr_t)p;
@@ -134,17 +133,17 @@ __device__ __forceinline__ const char* sptr(const char* p) {
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, const void* lds) {
   const char* sbase = sptr(base);
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("global_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "{m0}"(l)
+               : "v"(voff), "s"(sbase), "s"(l)
                : "memory");
 }
 __device__ __forceinline__ void dma4(const char* base, uint32_t voff, const void* lds) {
   const char* sbase = sptr(base);
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("global_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(voff), "s"(sbase), "{m0}"(l)
+               : "v"(voff), "s"(sbase), "s"(l)
                : "memory");
 }
 
