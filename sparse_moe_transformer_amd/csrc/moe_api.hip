@@ -200,6 +200,16 @@ bool use_decode(const Dims& d) {
   return d.T * d.k <= (int64_t)32 * d.E;
 }
 
+// The 256-row tiles for prefill-sized bf16 batches: selected by
+// MOE_GEMM_TILE=256 where they fit (measured slower than the 128-row tiles on
+// the workloads here, so not the default).
+bool use_wide(const Dims& d) {
+  if (d.dtype != MOE_BF16 || d.wfmt != WF_DTYPE || use_decode(d)) return false;
+  if (!gemm_wide_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
+  const char* e = std::getenv("MOE_GEMM_TILE");
+  return e && std::strcmp(e, "256") == 0;
+}
+
 // --- stages (arguments already checked) ---
 
 moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
@@ -216,7 +226,8 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
     g.sws1 = d.packed ? scale_slot(mx->up, d, per) : mx->shared_up;
   }
   const bool dec = use_decode(d);
-  const int BM = dec ? gemm_decode_bm() : gemm_bm();
+  const bool wide = use_wide(d);
+  const int BM = dec ? gemm_decode_bm() : wide ? gemm_wide_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
   g.a = x;
   g.w0 = w_gate;
@@ -239,6 +250,7 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
   g.gm_routed = 8;
   g.gm_shared = 8;
   if (dec) return hip_ok(launch_gate_up_decode(g, st));
+  if (wide) return hip_ok(launch_gate_up_wide(g, st));
   return hip_ok(launch_gate_up(g, d.dtype, st));
 }
 
@@ -253,7 +265,8 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
     g.sws0 = d.packed ? scale_slot(mx->down, d, (size_t)(d.I / 32) * d.H) : mx->shared_down;
   }
   const bool dec = use_decode(d);
-  const int BM = dec ? gemm_decode_bm() : gemm_bm();
+  const bool wide = use_wide(d);
+  const int BM = dec ? gemm_decode_bm() : wide ? gemm_wide_bm() : gemm_bm();
   const int64_t rows = d.T * d.k;
   g.offsets = offsets;
   g.sorted_rows = sorted_rows;
@@ -275,10 +288,20 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
       g.a_shared = h_shared;
       g.w0 = w_down;
       if (dec) return hip_ok(launch_down_both_decode(g, st));
-      return hip_ok(launch_down_both(g, d.dtype, st));
+      if (!wide) return hip_ok(launch_down_both(g, d.dtype, st));
+      // 256-row tiles: shared rows, then routed rows, in two launches (one
+      // output type per kernel keeps its accumulators in registers)
+      g.a = h_shared;
+      MOE_TRY(hip_ok(launch_down_shared_wide(g, st)));
+      g.mt_shared = 0;
+      g.nt_shared = 0;
+      g.a = h;
+      return hip_ok(launch_down_routed_wide(g, false, st));
     }
     g.a = h_shared;
-    MOE_TRY(hip_ok(dec ? launch_down_shared_decode(g, st) : launch_down_shared(g, d.dtype, st)));
+    MOE_TRY(hip_ok(dec    ? launch_down_shared_decode(g, st)
+                   : wide ? launch_down_shared_wide(g, st)
+                          : launch_down_shared(g, d.dtype, st)));
   } else {
     MOE_TRY(hip_ok(launch_fill_zero(acc, (size_t)d.T * d.H * 4, st)));
   }
@@ -287,6 +310,7 @@ moe_status do_down(const moe_config* c, const Dims& d, const void* h, const void
   g.a = h;
   g.w0 = w_down;
   if (dec) return hip_ok(launch_down_routed_decode(g, y_perm == nullptr, st));
+  if (wide) return hip_ok(launch_down_routed_wide(g, y_perm == nullptr, st));
   return hip_ok(launch_down_routed(g, d.dtype, y_perm == nullptr, st));
 }
 

@@ -1,0 +1,600 @@
+// Grouped expert GEMMs for prefill-sized bf16 batches on 256-row tiles
+// (gfx950).
+//
+// Same operands, outputs and persistent tile order as the 128-row kernel in
+// moe_gemm.hip: stacked [out, in] expert weights (mlxcel #845 "Checkpoint
+// weight layout": pre-stacked experts.{gate,up,down}_proj), activation rows
+// gathered through sorted_rows for gate/up, the activation applied to the
+// gate and up accumulators in registers (HF "AFMoE" doc, hidden_act silu;
+// mlxcel #763 Activation bullet, clamp-SwiGLU), the down projection writing
+// shared rows to acc and routed rows to y_perm (or w-scaled into acc).
+//
+// Why a second tile: with 128 activation rows x 256 weight rows per
+// workgroup, one K-step of 64 inputs moves 48 KiB into LDS and 96 KiB of
+// MFMA fragments out of it for 1024 MFMA cycles, more than the LDS and the
+// load path deliver in that time. Here a workgroup owns 256 activation rows
+// x 256 weight rows and each wave a 128 x 128 block (4 x 4 MFMAs of
+// 32x32x16, 256 accumulators): per K-step 64 KiB in and 128 KiB of fragments
+// out for 2048 MFMA cycles.
+//
+// Half tiles: an expert's last m-slot with at most 128 rows keeps its 256
+// weight rows but spreads them over the four waves (each 128 rows x 64 weight
+// rows, 4 x 2 MFMAs), so the remainder costs about half a tile rather than a
+// whole one. Its activation rows 128..255 are still loaded (clamped to a
+// valid row) so every tile issues the same loads per step.
+//
+// Pipeline: two LDS stages of 64 KiB (A 256 x 128 B, B 256 x 128 B), filled
+// by direct global->LDS loads. At the start of step s every wave waits for
+// its loads of stage s, a barrier makes every wave's loads visible and frees
+// the other stage (read in step s-1), and the loads of step s+1 (or of the
+// next tile's first step) are issued into it between the MFMAs of step s's
+// first two sub-steps. A tile's steps come in pairs (stage 0, then stage 1):
+// an odd K-step count gets one leading step of zeros (loaded from a zero
+// line, it adds exactly zero), so every tile starts on stage 0 and the two
+// stage arrays stay distinct __shared__ objects, which lets the compiler see
+// that the loads into one stage do not alias the fragment reads of the
+// other. The last step of a tile takes its load addresses from the next
+// tile by a uniform select, so the step loop has no tail. LDS rows are 8
+// chunks of 16 B, chunk c of row r at c ^ ((r >> 1) & 7), conflict-free for
+// the 32x32 fragment reads.
+#include "moe_common.h"
+#include "moe_gemm_common.h"
+#include "moe_kernels.h"
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int WBM = 256;       // activation rows of a full tile
+constexpr int WBR = 256;       // weight rows of a tile
+constexpr int HBM_ROWS = 128;  // rows of a half tile (at most)
+constexpr int NCH = 8;         // 16-byte chunks per row per K-step
+constexpr int KSB = NCH * 16;  // bytes per row per K-step (64 bf16)
+constexpr int NTHR = 256;
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_WG_TILES = 128;
+
+#define WIDE_LDS_STAGES                              \
+  __shared__ __align__(16) u32x4_t lds_a0[WBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_a1[WBM * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b0[WBR * NCH]; \
+  __shared__ __align__(16) u32x4_t lds_b1[WBR * NCH];
+
+// Load instruction j (0..7) of wave w fills rows 64w + 8j .. +7 of the
+// activation and of the weight part of a stage; the lane's row is that base
+// + lane / 8 and it fetches the logical chunk stored at physical chunk
+// lane % 8.
+__device__ __forceinline__ int ld_row(int j) { return (threadIdx.x >> 6) * 64 + 8 * j + ((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int ld_chunk(int row) { return (threadIdx.x & 7) ^ swz(row); }
+
+struct WTile {
+  const char* a;      // activation base (x, h or h_shared)
+  const char* b;      // this wave's weight base (gate or up rows for gate/up)
+  uint32_t aoff[8];   // this lane's activation rows + chunk, bytes from a
+  uint32_t boff[8];   // this lane's weight rows + chunk, bytes from b
+  int nk;             // K-steps of real data
+  int nk2;            // steps run: nk rounded up to even (a leading zero step)
+  uint32_t kseg;      // bytes of K per weight segment (the shared down's S experts)
+  uint32_t bstride;   // bytes between weight segments
+  int shared, e, row0, nrows, n0, N, half;
+};
+
+// Byte offsets (activation, weight) of K-step s of tile t (s >= nk2 - nk).
+__device__ __forceinline__ void step_offsets(const WTile& t, int s, uint32_t* ka, uint32_t* kw) {
+  const uint32_t kb = (uint32_t)(s - (t.nk2 - t.nk)) * KSB;
+  const uint32_t seg = kb / t.kseg;
+  *ka = kb;
+  *kw = seg * t.bstride + (kb - seg * t.kseg);
+}
+
+// The 16 loads of one stage: activation rows from a + ao[j] + ka, weight
+// rows from b + bo[j] + kw.
+__device__ __forceinline__ void issue_at(const char* a, const uint32_t (&ao)[8], uint32_t ka,
+                                         const char* b, const uint32_t (&bo)[8], uint32_t kw,
+                                         u32x4_t* la, u32x4_t* lb) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds(a + (ao[j] + ka), la + (w * 8 + j) * 64, 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_global_load_lds(b + (bo[j] + kw), lb + (w * 8 + j) * 64, 16, 0, 0);
+}
+
+// Step s of tile t (a real step: s >= nk2 - nk).
+__device__ __forceinline__ void issue_step(const WTile& t, int s, u32x4_t* la, u32x4_t* lb) {
+  uint32_t ka, kw;
+  step_offsets(t, s, &ka, &kw);
+  issue_at(t.a, t.aoff, ka, t.b, t.boff, kw, la, lb);
+}
+
+// The first step of tile n, or zeros when there is no next tile or its
+// first step is the leading zero step (lane chunks of the zero line).
+__device__ __forceinline__ void issue_first(const WTile& n, bool has_next, u32x4_t* la, u32x4_t* lb) {
+  const bool zero = !has_next || n.nk2 != n.nk;
+  const char* z = reinterpret_cast<const char*>(g_zero_line);
+  const uint32_t zo = (uint32_t)(threadIdx.x & 7) * 16u;
+  uint32_t ao[8], bo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ao[j] = zero ? zo : n.aoff[j];
+    bo[j] = zero ? zo : n.boff[j];
+  }
+  issue_at(zero ? z : n.a, ao, 0, zero ? z : n.b, bo, 0, la, lb);
+}
+
+// Weight row (within the tile's 256) of MFMA block nb of a wave.
+// Full tile, wave column wn (0..1), nb 0..3:
+//   gate/up: gate rows wn*64 + {0,32}, then the up rows of the same columns
+//   down:    rows wn*128 + 32*nb
+// Half tile, wave w (0..3), nb 0..1:
+//   gate/up: gate rows w*32, up row 128 + w*32
+//   down:    rows w*64 + 32*nb
+template <int KIND, bool HALF>
+__device__ __forceinline__ int wrow(int wv, int nb) {
+  if (HALF) {
+    if (KIND == GATE_UP) return nb == 0 ? wv * 32 : 128 + wv * 32;
+    return wv * 64 + nb * 32;
+  }
+  if (KIND == GATE_UP) return nb < 2 ? wv * 64 + nb * 32 : 128 + wv * 64 + (nb - 2) * 32;
+  return wv * 128 + nb * 32;
+}
+
+typedef floatx16_t Acc[4][4];
+
+// One K-step from one stage: 4 sub-steps of K = 16. Lane l reads row l % 32
+// of a block and chunk 2s + l / 32 of sub-step s. The stage loads issued
+// just before (into the other stage) are placed between the MFMAs of the
+// first two sub-steps.
+template <int KIND, bool HALF>
+__device__ __forceinline__ void compute_wide(const u32x4_t* la, const u32x4_t* lb, Acc& acc) {
+  constexpr int NB = HALF ? 2 : 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mrow0 = HALF ? 0 : (wave >> 1) * 128;  // first activation row of the wave
+  const int wv = HALF ? wave : (wave & 1);
+  const int q = lane >> 5, r = lane & 31;
+  bf16x8_t fa[2][4], fb[2][NB];
+  auto read = [&](int s, int slot) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int row = mrow0 + mb * 32 + r;
+      fa[slot][mb] = __builtin_bit_cast(bf16x8_t, la[row * NCH + ((2 * s + q) ^ swz(row))]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wrow<KIND, HALF>(wv, nb) + r;
+      fb[slot][nb] = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
+    }
+  };
+  read(0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < 3) read(s + 1, (s + 1) & 1);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][mb], fb[s & 1][nb],
+                                                              acc[mb][nb], 0, 0, 0);
+  }
+  // schedule: the reads of sub-step 0 first; then per sub-step its MFMAs
+  // with the next sub-step's fragment reads between them, and the 16 stage
+  // loads between the MFMAs of sub-steps 0 and 1
+  constexpr int NM = 4 * NB;             // MFMAs per sub-step
+  constexpr int NR = 4 + NB;             // fragment reads per sub-step
+  constexpr int LPS = 8;                 // stage loads per sub-step (sub-steps 0, 1)
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s < 3 && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (s < 2 && (i * LPS) / NM != ((i + 1) * LPS) / NM)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ int tile_count(const GemmArgs& g, const int* cum) {
+  if (KIND == GATE_UP || KIND == DOWN_BOTH) return g.mt_shared * g.nt_shared + cum[g.E] * g.nt_routed;
+  if (KIND == DOWN_SHARED) return g.mt_shared * g.nt_shared;
+  return cum[g.E] * g.nt_routed;
+}
+
+// row0 (x), nrows | shared << 16 (y), expert (z), n-tile (w) of tile idx
+template <int KIND>
+__device__ __forceinline__ int4 place_of(const GemmArgs& g, const int* offs, const int* cum,
+                                         int idx) {
+  const int nshared = KIND == DOWN_ROUTED ? 0 : g.mt_shared * g.nt_shared;
+  int mt, nt, row0, nrows, e = 0, shared;
+  if (idx < nshared) {
+    shared = 1;
+    grouped_order(idx, g.mt_shared, g.nt_shared, g.gm_shared, &mt, &nt);
+    row0 = mt * WBM;
+    nrows = min(WBM, g.T - row0);
+  } else {
+    // routed tiles are expert-major (expert e owns tiles [cum[e] * nt,
+    // cum[e+1] * nt)), groups of gm m-slots inside an expert, m fastest
+    shared = 0;
+    const int t = idx - nshared;
+    e = owner(cum, g.E, t / g.nt_routed);
+    const int ms = cum[e + 1] - cum[e];
+    int m;
+    grouped_order(t - cum[e] * g.nt_routed, ms, g.nt_routed, g.gm_routed, &m, &nt);
+    row0 = offs[e] + m * WBM;
+    nrows = min(WBM, offs[e + 1] - row0);
+  }
+  return make_int4(row0, nrows | (shared << 16), e, nt);
+}
+
+// Tokens of this lane's 8 activation rows of gate/up tile p (global loads;
+// shared tiles take rows row0 + R directly).
+template <int KIND>
+__device__ __forceinline__ void load_tokens(const GemmArgs& g, int4 p, int (&tok)[8]) {
+  if (KIND != GATE_UP) return;
+  const int row0 = p.x, nrows = p.y & 0xFFFF, shared = p.y >> 16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int R = min(ld_row(j), nrows - 1);
+    tok[j] = shared ? row0 + R : g.sorted_rows[row0 + R];
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[8], WTile& t) {
+  const int H = g.H;
+  t.row0 = p.x;
+  t.nrows = p.y & 0xFFFF;
+  t.shared = p.y >> 16;
+  t.e = p.z;
+  t.half = t.nrows <= HBM_ROWS;
+  const int nt = p.w;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (KIND == GATE_UP) {
+    t.a = static_cast<const char*>(g.a);
+    t.n0 = nt * 128;
+    t.N = t.shared ? g.S * g.Is : g.I;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int token = t.shared ? tok[j] : div_k(tok[j], g.k, g.kmagic);
+      t.aoff[j] = (uint32_t)token * (uint32_t)(H * 2) + (uint32_t)ld_chunk(ld_row(j)) * 16u;
+    }
+    // waves 0, 1 load the gate rows (0..127 of the tile), waves 2, 3 the up rows
+    const char* wgt = static_cast<const char*>(t.shared ? (w < 2 ? g.ws0 : g.ws1)
+                                                        : (w < 2 ? g.w0 : g.w1));
+    t.b = wgt + (t.shared ? (size_t)0 : (size_t)t.e * g.I * H * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = ld_row(j);
+      const int n = min(t.n0 + (row & 127), t.N - 1);
+      t.boff[j] = (uint32_t)n * (uint32_t)(H * 2) + (uint32_t)ld_chunk(row) * 16u;
+    }
+    t.nk = H / 64;
+    t.nk2 = (t.nk + 1) & ~1;
+    t.kseg = (uint32_t)H * 2;
+    t.bstride = 0;
+  } else {
+    // down: shared tiles read h_shared [T, S*Is] against the S shared down
+    // matrices [H, Is] (K segment s at ws_down + s*H*Is); routed tiles read
+    // h [T*k, I] (expert-sorted rows) against expert e's down matrix [H, I]
+    const bool sh = KIND == DOWN_SHARED || (KIND == DOWN_BOTH && t.shared);
+    const int Ks = sh ? g.S * g.Is : g.I;  // activation row length
+    const int ldb = sh ? g.Is : g.I;       // weight row length of a K segment
+    t.a = static_cast<const char*>(KIND == DOWN_BOTH && sh ? g.a_shared : g.a);
+    t.n0 = nt * WBR;
+    t.N = H;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = ld_row(j);
+      t.aoff[j] = (uint32_t)(t.row0 + min(row, t.nrows - 1)) * (uint32_t)(Ks * 2) +
+                  (uint32_t)ld_chunk(row) * 16u;
+    }
+    t.b = sh ? static_cast<const char*>(g.ws0)
+             : static_cast<const char*>(g.w0) + (size_t)t.e * H * g.I * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = ld_row(j);
+      t.boff[j] = (uint32_t)min(t.n0 + row, H - 1) * (uint32_t)(ldb * 2) +
+                  (uint32_t)ld_chunk(row) * 16u;
+    }
+    t.nk = Ks / 64;
+    t.nk2 = (t.nk + 1) & ~1;
+    t.kseg = (uint32_t)ldb * 2;
+    t.bstride = sh ? (uint32_t)H * (uint32_t)ldb * 2u : 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues. Accumulator element v of block (mb, nb) of lane (q, r) is row
+// acc_row(mb, v, q) of the wave's rows, column r of the block.
+
+// The wave's index, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Stores of one wave's accumulators. CHECK: bounds-check rows against nrows
+// and columns against N (partial tiles); full tiles take the branch-free
+// instance. Row pointers are wave-uniform (scalar registers); each lane adds
+// its own 32-bit offset (rows 4q.., column r).
+template <int KIND, bool HALF, bool ATOMIC, bool CHECK>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const WTile& cur, const Acc& acc,
+                                           const int* ep_tok, const float* ep_w) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int q = lane >> 5, r = lane & 31;
+  const int mrow0 = HALF ? 0 : (wave >> 1) * 128;
+  const int wv = HALF ? wave : (wave & 1);
+  // row (within the wave's rows) of element v of block mb, without the lane's 4q
+  auto rrow = [](int mb, int v) { return mb * 32 + (v >> 2) * 8 + (v & 3); };
+  if (KIND == GATE_UP) {
+    bf16_t* dst = static_cast<bf16_t*>(cur.shared ? g.out_shared : g.out);
+    const int ld = cur.shared ? g.S * g.Is : g.I;
+    // this wave's output columns: full tiles 64 (two blocks), half tiles 32
+    const int col0 = cur.n0 + (HALF ? wv * 32 : wv * 64);
+    constexpr int NC = HALF ? 1 : 2;
+    bf16_t* base = dst + (size_t)(cur.row0 + mrow0) * ld + col0;
+    const uint32_t lo = (uint32_t)(q * 4 * ld + r);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if (CHECK && mrow0 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;  // uniform
+        if (CHECK && mrow0 + rrow(mb, v) + 4 * q >= cur.nrows) continue;
+        bf16_t* p = base + (size_t)rrow(mb, v) * ld;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (CHECK && col0 + c * 32 + r >= cur.N) continue;
+          store_out<bf16_t>(p + lo + c * 32, act_apply(acc[mb][c][v], acc[mb][c + NC][v], g.act));
+        }
+      }
+  } else {
+    constexpr int NB = HALF ? 2 : 4;
+    const int col0 = cur.n0 + (HALF ? wv * 64 : wv * 128);
+    const bool sh = KIND == DOWN_SHARED || (KIND == DOWN_BOTH && cur.shared);
+    const uint32_t lo = (uint32_t)(q * 4 * g.H + r);
+    if (sh) {
+      // shared rows: fp32 into acc (stored, the routed rows add later)
+      float* base = static_cast<float*>(g.out) + (size_t)(cur.row0 + mrow0) * g.H + col0;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (CHECK && mrow0 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
+          if (CHECK && mrow0 + rrow(mb, v) + 4 * q >= cur.nrows) continue;
+          float* p = base + (size_t)rrow(mb, v) * g.H;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (!CHECK || col0 + nb * 32 + r < cur.N) p[lo + nb * 32] = acc[mb][nb][v];
+        }
+    } else if (!ATOMIC) {
+      // routed rows, fixed-order combine: unweighted bf16 rows into y_perm
+      // (expert-sorted row order)
+      bf16_t* base = static_cast<bf16_t*>(g.y_perm) + (size_t)(cur.row0 + mrow0) * g.H + col0;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (CHECK && mrow0 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
+          if (CHECK && mrow0 + rrow(mb, v) + 4 * q >= cur.nrows) continue;
+          bf16_t* p = base + (size_t)rrow(mb, v) * g.H;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (!CHECK || col0 + nb * 32 + r < cur.N) store_out<bf16_t>(p + lo + nb * 32, acc[mb][nb][v]);
+        }
+    } else {
+      // routed rows, atomic combine: w-scaled fp32 adds into the token's acc row
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = mrow0 + acc_row(mb, v, q);
+          if (CHECK && mrow0 + mb * 32 + (v >> 2) * 8 >= cur.nrows) continue;
+          if (CHECK && m >= cur.nrows) continue;
+          float* orow = static_cast<float*>(g.out) + (size_t)ep_tok[m] * g.H + col0 + r;
+          const float wt = ep_w[m];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (!CHECK || col0 + nb * 32 + r < cur.N) unsafeAtomicAdd(orow + nb * 32, wt * acc[mb][nb][v]);
+        }
+    }
+  }
+}
+
+template <int KIND, bool HALF, bool ATOMIC>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const WTile& cur, const Acc& acc,
+                                         const int* ep_tok, const float* ep_w) {
+  const int ncols = KIND == GATE_UP ? 128 : WBR;
+  if (cur.nrows == WBM && cur.n0 + ncols <= cur.N)
+    store_tile<KIND, HALF, ATOMIC, false>(g, cur, acc, ep_tok, ep_w);
+  else
+    store_tile<KIND, HALF, ATOMIC, true>(g, cur, acc, ep_tok, ep_w);
+}
+
+// ---------------------------------------------------------------------------
+// The steps of one tile, in pairs (stage 0, stage 1); the last step loads the
+// next tile's first step into stage 0.
+
+template <int KIND, bool HALF>
+__device__ __forceinline__ void run_steps(const WTile& cur, const WTile& nxt, bool has_next,
+                                          Acc& acc, u32x4_t* a0, u32x4_t* a1, u32x4_t* b0,
+                                          u32x4_t* b1) {
+  const int nk2 = cur.nk2;
+  const bool next_zero = !has_next || nxt.nk2 != nxt.nk;
+  const char* z = reinterpret_cast<const char*>(g_zero_line);
+  const uint32_t zo = (uint32_t)(threadIdx.x & 7) * 16u;
+  for (int s = 0; s < nk2; s += 2) {
+    // step s: stage 0; loads of step s + 1 (always inside the tile) into stage 1
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue_step(cur, s + 1, a1, b1);
+    compute_wide<KIND, HALF>(a0, b0, acc);
+    // step s + 1: stage 1; loads of step s + 2, or of the next tile's first
+    // step, into stage 0 (addresses chosen by uniform selects)
+    const bool last = s + 2 >= nk2;
+    const bool zero = last && next_zero;
+    uint32_t ka, kw;
+    step_offsets(cur, last ? s + 1 : s + 2, &ka, &kw);
+    ka = last ? 0u : ka;
+    kw = last ? 0u : kw;
+    uint32_t ao[8], bo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ao[j] = zero ? zo : last ? nxt.aoff[j] : cur.aoff[j];
+      bo[j] = zero ? zo : last ? nxt.boff[j] : cur.boff[j];
+    }
+    const char* pa = zero ? z : last ? nxt.a : cur.a;
+    const char* pb = zero ? z : last ? nxt.b : cur.b;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    issue_at(pa, ao, ka, pb, bo, kw, a0, b0);
+    compute_wide<KIND, HALF>(a1, b1, acc);
+  }
+}
+
+template <int KIND, bool ATOMIC>
+__device__ __forceinline__ void wide_body(const GemmArgs& g) {
+  WIDE_LDS_STAGES
+  __shared__ int offs[MAX_EXPERTS + 1];
+  __shared__ int cum[MAX_EXPERTS + 1];
+  __shared__ int ep_tok[WBM];  // routed atomic epilogue: token and weight of each row
+  __shared__ float ep_w[WBM];
+  __shared__ int4 places[MAX_WG_TILES];
+
+  if (KIND != DOWN_SHARED) build_tile_prefix<WBM>(g.offsets, g.E, offs, cum);
+  __syncthreads();
+  const int ntiles = tile_count<KIND>(g, cum);
+  const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0);
+  const int n_my = wt.n_my;
+  if (n_my == 0) return;
+  for (int i = threadIdx.x; i < min(n_my, MAX_WG_TILES); i += NTHR)
+    places[i] = place_of<KIND>(g, offs, cum, wt.global(i));
+  __syncthreads();
+  auto place = [&](int i) -> int4 {
+    i = min(i, n_my - 1);
+    const int4 p = i < MAX_WG_TILES ? places[i] : place_of<KIND>(g, offs, cum, wt.global(i));
+    return make_int4(__builtin_amdgcn_readfirstlane(p.x), __builtin_amdgcn_readfirstlane(p.y),
+                     __builtin_amdgcn_readfirstlane(p.z), __builtin_amdgcn_readfirstlane(p.w));
+  };
+
+  // row ids one tile ahead (their loads complete before the stage loads
+  // issued after them)
+  int tok[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  load_tokens<KIND>(g, place(0), tok);
+  WTile cur, nxt;
+  make_tile<KIND>(g, place(0), tok, cur);
+  load_tokens<KIND>(g, place(1), tok);
+  // routed atomic epilogue: the sorted row id of row threadIdx.x
+  int ep_r = 0;
+  if (KIND == DOWN_ROUTED && ATOMIC) ep_r = g.sorted_rows[cur.row0 + min((int)threadIdx.x, cur.nrows - 1)];
+  issue_first(cur, true, lds_a0, lds_b0);
+  int li = 0;
+  for (;;) {
+    const bool has_next = li + 1 < n_my;
+    Acc acc;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+    int ep_t = 0;
+    float ep_wt = 0.f;
+    if (KIND == DOWN_ROUTED && ATOMIC) {
+      ep_wt = g.topk_w[ep_r];
+      ep_t = div_k(ep_r, g.k, g.kmagic);
+    }
+    make_tile<KIND>(g, place(li + 1), tok, nxt);
+    load_tokens<KIND>(g, place(li + 2), tok);
+    if (KIND == DOWN_ROUTED && ATOMIC)
+      ep_r = g.sorted_rows[nxt.row0 + min((int)threadIdx.x, nxt.nrows - 1)];
+    if (cur.half) run_steps<KIND, true>(cur, nxt, has_next, acc, lds_a0, lds_a1, lds_b0, lds_b1);
+    else run_steps<KIND, false>(cur, nxt, has_next, acc, lds_a0, lds_a1, lds_b0, lds_b1);
+    if (KIND == DOWN_ROUTED && ATOMIC) {
+      ep_tok[threadIdx.x] = ep_t;
+      ep_w[threadIdx.x] = ep_wt;
+      // raw barrier: only these LDS writes must be complete (the next
+      // tile's first stage loads stay in flight)
+      __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    }
+    if (cur.half) epilogue<KIND, true, ATOMIC>(g, cur, acc, ep_tok, ep_w);
+    else epilogue<KIND, false, ATOMIC>(g, cur, acc, ep_tok, ep_w);
+    if (!has_next) break;
+    ++li;
+    cur = nxt;
+  }
+  // the last tile's look-ahead loads (zeros) land before the workgroup ends
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// one name per kind, so that profiles tell them apart
+__global__ void __launch_bounds__(NTHR) moe_gate_up_wide_kernel(GemmArgs g) {
+  wide_body<GATE_UP, false>(g);
+}
+__global__ void __launch_bounds__(NTHR) moe_down_shared_wide_kernel(GemmArgs g) {
+  wide_body<DOWN_SHARED, false>(g);
+}
+template <bool ATOMIC>
+__global__ void __launch_bounds__(NTHR) moe_down_routed_wide_kernel(GemmArgs g) {
+  wide_body<DOWN_ROUTED, ATOMIC>(g);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host side
+
+int gemm_wide_bm() { return WBM; }
+
+// bf16 only; every K length a whole number of 64-input steps; the per-lane
+// 32-bit offsets reach every row of x, h, h_shared, one expert's weights and
+// the shared weights.
+bool gemm_wide_fits(int64_t T, int H, int I, int k, int S, int Is) {
+  if (H % 64 || I % 64 || (S && Is % 64)) return false;
+  const uint64_t lim = 1ull << 31;
+  const uint64_t x = (uint64_t)T * H * 2, h = (uint64_t)T * k * I * 2,
+                 hs = (uint64_t)T * S * Is * 2, w = (uint64_t)H * I * 2,
+                 ws = (uint64_t)S * H * Is * 2;
+  return x < lim && h < lim && hs < lim && w < lim && ws < lim;
+}
+
+static int g_wide_cus = 0;
+static int wide_num_cus() {
+  if (g_wide_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_wide_cus = n;
+    else
+      g_wide_cus = 256;
+  }
+  return g_wide_cus;
+}
+
+static dim3 wide_grid(long tiles) { return dim3((unsigned)(tiles < wide_num_cus() ? tiles : wide_num_cus())); }
+
+hipError_t launch_gate_up_wide(const GemmArgs& g, hipStream_t st) {
+  const long n = (long)g.mt_shared * g.nt_shared + (long)g.mt_routed * g.nt_routed;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_gate_up_wide_kernel, wide_grid(n), dim3(NTHR), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_shared_wide(const GemmArgs& g, hipStream_t st) {
+  const long n = (long)g.mt_shared * g.nt_shared;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_down_shared_wide_kernel, wide_grid(n), dim3(NTHR), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_routed_wide(const GemmArgs& g, bool atomic, hipStream_t st) {
+  const long n = (long)g.mt_routed * g.nt_routed;
+  if (n <= 0) return hipSuccess;
+  if (atomic)
+    hipLaunchKernelGGL(moe_down_routed_wide_kernel<true>, wide_grid(n), dim3(NTHR), 0, st, g);
+  else
+    hipLaunchKernelGGL(moe_down_routed_wide_kernel<false>, wide_grid(n), dim3(NTHR), 0, st, g);
+  return hipGetLastError();
+}

@@ -56,6 +56,14 @@ hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st);
 
+// 256-row tile kernels for prefill-sized bf16 batches (every K length a
+// multiple of 64; per-lane 32-bit offsets: gemm_wide_fits).
+int gemm_wide_bm();
+bool gemm_wide_fits(int64_t T, int H, int I, int k, int S, int Is);
+hipError_t launch_gate_up_wide(const GemmArgs& g, hipStream_t st);
+hipError_t launch_down_shared_wide(const GemmArgs& g, hipStream_t st);
+hipError_t launch_down_routed_wide(const GemmArgs& g, bool atomic, hipStream_t st);
+
 // router GEMM scratch: bf16 split planes of the router weight + K-chunk partials
 int router_kchunks(int64_t T, int E, int H, int dtype);
 size_t router_ws_bytes(int64_t T, int E, int H, int dtype);
