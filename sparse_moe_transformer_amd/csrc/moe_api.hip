@@ -200,14 +200,20 @@ bool use_decode(const Dims& d) {
   return d.T * d.k <= (int64_t)32 * d.E;
 }
 
-// The 256-row tiles for prefill-sized bf16 batches: selected by
-// MOE_GEMM_TILE=256 where they fit (measured slower than the 128-row tiles on
-// the workloads here, so not the default).
+// The 256-row tiles for prefill-sized bf16 batches with many rows per expert
+// (at least 384 on average) and long K (H and I at least 1024): there a
+// weight tile is reused by several row tiles from L2 and the wider tile
+// moves less data per FLOP (measured faster on the AFMoE-default and skewed
+// layers; slower where weights stream from HBM with ~256 rows per expert, or
+// K is short). MOE_GEMM_TILE=128 / =256 force one kernel (testing knobs).
 bool use_wide(const Dims& d) {
   if (d.dtype != MOE_BF16 || d.wfmt != WF_DTYPE || use_decode(d)) return false;
   if (!gemm_wide_fits(d.T, d.H, d.I, d.k, d.S, d.Is)) return false;
-  const char* e = std::getenv("MOE_GEMM_TILE");
-  return e && std::strcmp(e, "256") == 0;
+  if (const char* e = std::getenv("MOE_GEMM_TILE")) {
+    if (std::strcmp(e, "128") == 0) return false;
+    if (std::strcmp(e, "256") == 0) return true;
+  }
+  return d.T * d.k >= (int64_t)384 * d.E && d.H >= 1024 && d.I >= 1024;
 }
 
 // --- stages (arguments already checked) ---

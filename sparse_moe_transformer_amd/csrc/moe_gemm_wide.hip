@@ -143,47 +143,52 @@ __device__ __forceinline__ int wrow(int wv, int nb) {
 typedef floatx16_t Acc[4][4];
 
 // One K-step from one stage: 4 sub-steps of K = 16. Lane l reads row l % 32
-// of a block and chunk 2s + l / 32 of sub-step s. The stage loads issued
-// just before (into the other stage) are placed between the MFMAs of the
-// first two sub-steps.
+// of a block and chunk 2s + l / 32 of sub-step s. The step's last sub-step
+// is deferred: its fragments are read into (ca, cb) and its MFMAs run at the
+// start of the next step, after the barrier, while that step's first
+// fragment reads are in flight (the stage they came from may then be
+// reloaded: the fragments are already in registers). The stage loads issued
+// just before (into the other stage) sit between the MFMAs of the first two
+// sub-steps.
 template <int KIND, bool HALF>
-__device__ __forceinline__ void compute_wide(const u32x4_t* la, const u32x4_t* lb, Acc& acc) {
+__device__ __forceinline__ void compute_wide(const u32x4_t* la, const u32x4_t* lb, Acc& acc,
+                                             bf16x8_t (&ca)[4], bf16x8_t (&cb)[4]) {
   constexpr int NB = HALF ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mrow0 = HALF ? 0 : (wave >> 1) * 128;  // first activation row of the wave
+  const int mrow0 = HALF ? 0 : (wave >> 1) * 128;
   const int wv = HALF ? wave : (wave & 1);
   const int q = lane >> 5, r = lane & 31;
-  bf16x8_t fa[2][4], fb[2][NB];
-  auto read = [&](int s, int slot) {
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read = [&](int s, bf16x8_t (&xa)[4], bf16x8_t (&xb)[4]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int row = mrow0 + mb * 32 + r;
-      fa[slot][mb] = __builtin_bit_cast(bf16x8_t, la[row * NCH + ((2 * s + q) ^ swz(row))]);
+      xa[mb] = __builtin_bit_cast(bf16x8_t, la[row * NCH + ((2 * s + q) ^ swz(row))]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int row = wrow<KIND, HALF>(wv, nb) + r;
-      fb[slot][nb] = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
+      xb[nb] = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
     }
   };
-  read(0, 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) read(s + 1, (s + 1) & 1);
+  auto mma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[4]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][mb], fb[s & 1][nb],
-                                                              acc[mb][nb], 0, 0, 0);
-  }
-  // schedule: the reads of sub-step 0 first; then per sub-step its MFMAs
-  // with the next sub-step's fragment reads between them, and the 16 stage
-  // loads between the MFMAs of sub-steps 0 and 1
-  constexpr int NM = 4 * NB;             // MFMAs per sub-step
-  constexpr int NR = 4 + NB;             // fragment reads per sub-step
-  constexpr int LPS = 8;                 // stage loads per sub-step (sub-steps 0, 1)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[mb], xb[nb], acc[mb][nb], 0, 0, 0);
+  };
+  read(0, fa[0], fb[0]);
+  mma(ca, cb);                      // the previous step's last sub-step
+  read(1, fa[1], fb[1]);
+  mma(fa[0], fb[0]);
+  read(2, fa[0], fb[0]);
+  mma(fa[1], fb[1]);
+  read(3, ca, cb);                  // this step's last sub-step: next time
+  mma(fa[0], fb[0]);
+  constexpr int NM = 4 * NB;
+  constexpr int NR = 4 + NB;
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -191,7 +196,7 @@ __device__ __forceinline__ void compute_wide(const u32x4_t* la, const u32x4_t* l
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (s < 3 && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (s < 2 && (i * LPS) / NM != ((i + 1) * LPS) / NM)
+      if (s < 2 && (i * 8) / NM != ((i + 1) * 8) / NM)
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
@@ -423,12 +428,18 @@ __device__ __forceinline__ void run_steps(const WTile& cur, const WTile& nxt, bo
   const bool next_zero = !has_next || nxt.nk2 != nxt.nk;
   const char* z = reinterpret_cast<const char*>(g_zero_line);
   const uint32_t zo = (uint32_t)(threadIdx.x & 7) * 16u;
+  // the deferred sub-step carried into the first step: zeros (adds exactly 0)
+  bf16x8_t ca[4], cb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) { ca[u] = bf16x8_t{}; cb[u] = bf16x8_t{}; }
   for (int s = 0; s < nk2; s += 2) {
     // step s: stage 0; loads of step s + 1 (always inside the tile) into stage 1
-    wait_vmcnt<0>();
+    // every load and LDS read of this wave done (the deferred fragments are
+    // in registers before the other stage is reloaded), then the barrier
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     issue_step(cur, s + 1, a1, b1);
-    compute_wide<KIND, HALF>(a0, b0, acc);
+    compute_wide<KIND, HALF>(a0, b0, acc, ca, cb);
     // step s + 1: stage 1; loads of step s + 2, or of the next tile's first
     // step, into stage 0 (addresses chosen by uniform selects)
     const bool last = s + 2 >= nk2;
@@ -445,11 +456,18 @@ __device__ __forceinline__ void run_steps(const WTile& cur, const WTile& nxt, bo
     }
     const char* pa = zero ? z : last ? nxt.a : cur.a;
     const char* pb = zero ? z : last ? nxt.b : cur.b;
-    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     issue_at(pa, ao, ka, pb, bo, kw, a0, b0);
-    compute_wide<KIND, HALF>(a1, b1, acc);
+    compute_wide<KIND, HALF>(a1, b1, acc, ca, cb);
   }
+  // the tile's last deferred sub-step
+  constexpr int NB = HALF ? 2 : 4;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[mb], cb[nb], acc[mb][nb], 0, 0, 0);
 }
 
 template <int KIND, bool ATOMIC>
