@@ -9,12 +9,15 @@ layer's single entry point moe_layer_forward on one stream.
 
 Timing protocol (every timed number): W untimed warm-up steps, then K timed
 steps; before each timed step a 1 GiB buffer (more than the 256 MB MALL) is
-written, outside the timed events, so expert weights come from HBM as they
-do in a many-layer model; HIP events on the layer's stream bracket the layer
-call alone, and the step time is the median of the K (min and max beside it).
-The K timed steps are bracketed by device synchronisation. The per-stage
-breakdown comes from a second pass over the stage entry points with the same
-flushes and HIP events around each call.
+written and then read back, outside the timed events, so expert weights come
+from HBM as they do in a many-layer model (the read-back leaves the caches
+holding clean lines, as the previous layers' weight reads would: after the
+write alone, the layer's reads would also pay for writing the flush's dirty
+lines back, reported beside it as the write-only figure); HIP events on the
+layer's stream bracket the layer call alone, and the step time is the median
+of the K (min and max beside it). The K timed steps are bracketed by device
+synchronisation. The per-stage breakdown comes from a second pass over the
+stage entry points with the same flushes and HIP events around each call.
 
 By default the headline is the MiniMax-M3-shaped layer at T = 8192 (the
 prefill target, MFMA-bound), and the same JSON line carries the two decode
@@ -72,19 +75,25 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
                 gate_up_bytes=gate_up_bytes)
 
 
-GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_decode.hip", "moe_gemm_common.h", "moe_common.h",
-                "moe_kernels.h")
+GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_decode.hip", "moe_gemm_common.h",
+                "moe_common.h", "moe_kernels.h")
 
 
 def gate_up_kernel(cfg: dict, T: int) -> str:
     """Name of the grouped gate/up kernel the library runs for this workload
-    (the 32-row tile kernel for decode-sized batches, else the 128-row one)."""
+    (the 32-row tile kernel for decode-sized batches; the 256-row one for
+    bf16 batches with at least 384 rows per expert and H, I >= 1024; else the
+    128-row one)."""
     H, I, k, E = cfg["hidden_size"], cfg["moe_intermediate_size"], cfg["num_experts_per_tok"], \
         cfg["num_experts"]
     S, Is = cfg["num_shared_experts"], cfg["shared_intermediate_size"] or I
     fits = H % 256 == 0 and I % 256 == 0 and (S * Is) % 256 == 0
     dec = cfg["dtype"] == "bf16" and fits and T * k <= 32 * E
-    return "moe_gate_up_decode_kernel" if dec else "moe_gate_up_kernel"
+    if dec:
+        return "moe_gate_up_decode_kernel"
+    wide = (cfg["dtype"] == "bf16" and cfg.get("weight_format", "dtype") == "dtype"
+            and T * k >= 384 * E and H >= 1024 and I >= 1024)
+    return "moe_gate_up_wide_kernel" if wide else "moe_gate_up_kernel"
 
 
 def gemm_source_sha() -> str:
@@ -352,6 +361,14 @@ def upload(moe, inp, T=None):
                 mx={key: d(v) for key, v in inp.mx.items()} if inp.mx is not None else None)
 
 
+def flush_caches(flush, i, read_back=True):
+    """Write the 1 GiB flush buffer, then (read_back) read it all: weights of
+    the next call come from HBM and the caches hold clean lines."""
+    flush.fill_(i & 0xFF)
+    if read_back:
+        flush.view(-1, 1 << 20).amax(dim=1)
+
+
 def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     """Time one workload by the protocol: stage-call pass and layer pass, each
     with a 1 GiB flush before every timed step and HIP events around the
@@ -415,7 +432,7 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     # stage-call pass: flush, then the six stage calls with events between
     sev = [[ev() for _ in range(len(stages) + 1)] for _ in range(steps)]
     for i in range(steps):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush, i)
         step(sev[i])
     torch.cuda.synchronize()
     per_stage = {s: [sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(steps)]
@@ -432,13 +449,23 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     lev = [(ev(), ev()) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush, i)
         lev[i][0].record(stream)
         layer()
         lev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call = [a.elapsed_time(b) for a, b in lev]
+
+    # the same with the write-only flush (dirty lines left in the caches)
+    wev = [(ev(), ev()) for _ in range(steps)]
+    for i in range(steps):
+        flush_caches(flush, i, read_back=False)
+        wev[i][0].record(stream)
+        layer()
+        wev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_write_flush = float(np.median([a.elapsed_time(b) for a, b in wev]))
 
     # warm: back-to-back calls (weights partly in the MALL), for comparison
     t0 = time.perf_counter()
@@ -448,6 +475,7 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     ms_warm = (time.perf_counter() - t0) * 1e3 / steps
     return dict(ms=float(np.median(per_call)), ms_min=float(np.min(per_call)),
                 ms_max=float(np.max(per_call)), wall_s=wall, ms_warm=ms_warm,
+                ms_write_flush=ms_write_flush,
                 stage_ms=stage_ms, gate_up_mean_ms=gate_up_mean, st=st, keys=keys,
                 stream=stream)
 
@@ -490,6 +518,8 @@ def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
              "bound": "hbm" if decode else "mfma", "touched_experts": alg["touched"],
              "stage_ms": m["stage_ms"], "ms_median": ms, "ms_min": m["ms_min"],
              "ms_max": m["ms_max"], "ms_per_step_warm": m["ms_warm"],
+             "ms_per_step_write_flush": m["ms_write_flush"],
+             "frac_hbm_peak_write_flush": alg["bytes"] / (m["ms_write_flush"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
              "frac_bf16_peak_warm": alg["flops"] / (m["ms_warm"] * 1e-3) / 1e12 / peak_mm,
              "frac_hbm_peak_warm": alg["bytes"] / (m["ms_warm"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
              "routing": routing_report(cfg, idx_h, logits_h, bias)}
@@ -645,7 +675,8 @@ def main():
                                       if cfg.get("weight_format", "dtype") != "dtype"
                                       else cfg["dtype"]),
                    "combine": args.combine, "entry": "moe_layer_forward",
-                   "timing": "median of K steps, 1 GiB flush before each (outside the events)"},
+                   "timing": "median of K steps, each after a 1 GiB write + read-back flush "
+                             "(outside the events)"},
         "layer": layer,
         "roofline": roof,
         "decode": decode,

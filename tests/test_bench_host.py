@@ -113,8 +113,8 @@ def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
     expert on average) against HBM; achieved = algorithmic work / the
     kernel's mean time."""
     from workloads import synth
-    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, gate_up_mean_ms=1.0,
-             stage_ms={"gate_up": 1.0})
+    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, ms_write_flush=2.5,
+             gate_up_mean_ms=1.0, stage_ms={"gate_up": 1.0})
     for name, bound in (("minimax_m3_prefill_T8192", "mfma"), ("minimax_m3_decode_T64", "hbm"),
                         ("trinity_nano_decode_T32", "hbm")):
         cfg = synth.config(name)
@@ -133,3 +133,22 @@ def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
         assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"])
         assert layer["frac_hbm_peak"] == pytest.approx(alg["bytes"] / 2e-3 / 1e9 / 8000.0)
         assert layer["frac_bf16_peak"] == pytest.approx(alg["flops"] / 2e-3 / 1e12 / 2516.6)
+
+
+def test_gate_up_kernel_names_follow_the_library_selection():
+    """The roofline kernel's name: 32-row tiles for decode-sized batches,
+    256-row tiles for bf16 batches with >= 384 rows per expert and H, I >=
+    1024, else the 128-row tiles (the selection in the library's API)."""
+    from workloads import synth
+    want = {"minimax_m3_prefill_T8192": "moe_gate_up_kernel",
+            "minimax_m3_decode_T64": "moe_gate_up_decode_kernel",
+            "trinity_nano_decode_T32": "moe_gate_up_decode_kernel",
+            "trinity_nano_prefill_T8192": "moe_gate_up_kernel",
+            "afmoe_default_T4096": "moe_gate_up_wide_kernel",
+            "skewed_afmoe_T8192": "moe_gate_up_wide_kernel",
+            "minimax_m3_prefill_T8192_mxfp8": "moe_gate_up_kernel"}
+    for name, kern in want.items():
+        cfg = synth.config(name)
+        assert bench.gate_up_kernel(cfg, cfg["T"]) == kern, name
+    assert bench._short("(anonymous namespace)::moe_gate_up_wide_kernel(GemmArgs)") == \
+        "moe_gate_up_wide_kernel"
