@@ -473,9 +473,29 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
         layer()
     torch.cuda.synchronize()
     ms_warm = (time.perf_counter() - t0) * 1e3 / steps
+
+    # decode-sized batches: the layer call captured once in a HIP graph and
+    # replayed, each replay after the same flush (events around the replay)
+    ms_graph = None
+    if T * cfg["num_experts_per_tok"] <= 32 * cfg["num_experts"]:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [(ev(), ev()) for _ in range(steps)]
+        for i in range(steps):
+            flush_caches(flush, i)
+            gev[i][0].record(stream)
+            graph.replay()
+            gev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_graph = float(np.median([a.elapsed_time(b) for a, b in gev]))
+        del graph
     return dict(ms=float(np.median(per_call)), ms_min=float(np.min(per_call)),
                 ms_max=float(np.max(per_call)), wall_s=wall, ms_warm=ms_warm,
-                ms_write_flush=ms_write_flush,
+                ms_write_flush=ms_write_flush, ms_graph=ms_graph,
                 stage_ms=stage_ms, gate_up_mean_ms=gate_up_mean, st=st, keys=keys,
                 stream=stream)
 
@@ -519,6 +539,7 @@ def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
              "stage_ms": m["stage_ms"], "ms_median": ms, "ms_min": m["ms_min"],
              "ms_max": m["ms_max"], "ms_per_step_warm": m["ms_warm"],
              "ms_per_step_write_flush": m["ms_write_flush"],
+             "ms_per_step_graph": m["ms_graph"],
              "frac_hbm_peak_write_flush": alg["bytes"] / (m["ms_write_flush"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
              "frac_bf16_peak_warm": alg["flops"] / (m["ms_warm"] * 1e-3) / 1e12 / peak_mm,
              "frac_hbm_peak_warm": alg["bytes"] / (m["ms_warm"] * 1e-3) / 1e9 / PEAK_HBM_GBS,

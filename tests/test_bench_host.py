@@ -113,7 +113,7 @@ def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
     expert on average) against HBM; achieved = algorithmic work / the
     kernel's mean time."""
     from workloads import synth
-    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, ms_write_flush=2.5,
+    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, ms_write_flush=2.5, ms_graph=None,
              gate_up_mean_ms=1.0, stage_ms={"gate_up": 1.0})
     for name, bound in (("minimax_m3_prefill_T8192", "mfma"), ("minimax_m3_decode_T64", "hbm"),
                         ("trinity_nano_decode_T32", "hbm")):
