@@ -218,10 +218,25 @@ bool use_wide(const Dims& d) {
 
 // --- stages (arguments already checked) ---
 
+// Decode batches of at most 256 routed rows: the gate/up kernel groups the
+// rows itself (no separate grouping launch).
+bool group_in_gate_up(const Dims& d) { return use_decode(d) && d.T * d.k <= 256; }
+
+// group: (group_in_gate_up) the routed experts and the grouping's outputs,
+// which the gate/up kernel then computes and stores; else offsets and
+// sorted_rows are inputs.
+struct Grouping {
+  const int32_t* topk_idx;
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* row_pos;
+};
+
 moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
                       const void* w_up, const void* ws_gate, const void* ws_up,
                       const moe_mx_scales* mx, const int32_t* offsets,
-                      const int32_t* sorted_rows, void* h, void* h_shared, hipStream_t st) {
+                      const int32_t* sorted_rows, void* h, void* h_shared, hipStream_t st,
+                      const Grouping* group = nullptr) {
   GemmArgs g = base_args(c, d);
   if (d.wfmt != WF_DTYPE) {
     g.wfmt = d.wfmt;
@@ -255,6 +270,12 @@ moe_status do_gate_up(const moe_config* c, const Dims& d, const void* x, const v
   g.nt_shared = d.S ? (d.S * d.Is + 127) / 128 : 0;
   g.gm_routed = 8;
   g.gm_shared = 8;
+  if (group) {
+    g.topk_idx = group->topk_idx;
+    g.offsets_out = group->offsets;
+    g.sorted_out = group->sorted_rows;
+    g.row_pos_out = group->row_pos;
+  }
   if (dec) return hip_ok(launch_gate_up_decode(g, st));
   if (wide) return hip_ok(launch_gate_up_wide(g, st));
   return hip_ok(launch_gate_up(g, d.dtype, st));
@@ -372,24 +393,38 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
                      int32_t deterministic, const Ws& w, hipStream_t st, LayerOut* res) {
   const int T = (int)d.T;
   const float* logits = router_logits_in;
+  // small bf16 batches: the router leaves per-K-group planes and the routing
+  // kernel sums them (storing the logits) before it routes
+  const float* planes = nullptr;
+  int np = 0;
+  float* lo = router_logits_out ? router_logits_out : w.logits;
   if (!logits) {
-    float* lo = router_logits_out ? router_logits_out : w.logits;
     const float* wr = nullptr;
     MOE_TRY(router_weights(d, w_router, mx, w, st, &wr));
-    MOE_TRY(hip_ok(launch_router_logits(x, wr, lo, T, d.H, d.E, d.dtype, w.router, st)));
+    np = router_planes(T, d.H, d.dtype);
+    if (np > 0) {
+      planes = static_cast<const float*>(w.router);
+      MOE_TRY(hip_ok(launch_router_planes(x, wr, static_cast<float*>(w.router), T, d.H, d.E, st)));
+    } else {
+      MOE_TRY(hip_ok(launch_router_logits(x, wr, lo, T, d.H, d.E, d.dtype, w.router, st)));
+    }
     logits = lo;
   }
   int32_t* idx = topk_idx_out ? topk_idx_out : w.idx;
   float* tw = topk_w_out ? topk_w_out : w.w;
-  // routing: one wavefront per token over many workgroups; grouping: one
-  // workgroup for decode batches (T*k <= 1024), else three small kernels
+  // routing: one wavefront per token over many workgroups; grouping: inside
+  // the gate/up kernel for decode batches of at most 256 routed rows, one
+  // workgroup up to 1024 rows, else three small kernels
   MOE_TRY(hip_ok(launch_route(logits, expert_bias, T, d.E, d.k, cfg->score_func,
                               cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st,
-                              cfg->n_group, cfg->topk_group)));
-  MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
-                                w.local_rank, w.chunk_hist, st)));
+                              cfg->n_group, cfg->topk_group, planes, np, planes ? lo : nullptr)));
+  const Grouping grp{idx, w.offsets, w.sorted_rows, w.row_pos};
+  const bool fused = group_in_gate_up(d);
+  if (!fused)
+    MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
+                                  w.local_rank, w.chunk_hist, st)));
   MOE_TRY(do_gate_up(cfg, d, x, w_gate, w_up, ws_gate, ws_up, mx, w.offsets, w.sorted_rows, w.h,
-                     w.h_shared, st));
+                     w.h_shared, st, fused ? &grp : nullptr));
   void* yp = deterministic ? w.y_perm : nullptr;
   MOE_TRY(do_down(cfg, d, w.h, w_down, w.h_shared, ws_down, mx, w.offsets, w.sorted_rows, tw,
                   w.acc, yp, st));

@@ -44,6 +44,7 @@
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
+#include "moe_small_sort.h"
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
@@ -571,11 +572,25 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
   __shared__ int cum[MAX_EXPERTS + 1];
   __shared__ int4 places[MAX_WG_TILES];
   __shared__ int rows_buf[3][64];  // gathered row ids of tiles li, li+1, li+2 (slot i % 3)
+  __shared__ int sorted[KIND == GATE_UP ? 256 : 1];  // grouped rows, when this kernel groups
   __shared__ int ep_tok[2][64];    // atomic down epilogue: token and weight of each
   __shared__ float ep_w[2][64];    // row (by tile parity: written while the other
                                    // waves may still read the previous tile's)
 
-  if (KIND != DOWN_SHARED) build_tile_prefix<DBM>(g.offsets, g.E, offs, cum);
+  // gate/up of a small decode batch: group the routed rows here (scratch in
+  // stage 0, before any load into it); workgroup 0 also stores the grouping
+  // for the later stages
+  const bool grouped_here = KIND == GATE_UP && g.topk_idx != nullptr;
+  if (grouped_here) {
+    static_assert(sizeof(lds_st[0]) >= (256 + 3 * MAX_EXPERTS + 4) * sizeof(int),
+                  "a stage holds the grouping scratch");
+    int* scratch = reinterpret_cast<int*>(lds_st[0]);
+    const bool pub = blockIdx.x == 0;
+    block_sort_rows_256(g.topk_idx, g.T, g.k, g.E, scratch, offs, sorted,
+                        pub ? g.offsets_out : nullptr, pub ? g.sorted_out : nullptr,
+                        pub ? g.row_pos_out : nullptr);
+  }
+  if (KIND != DOWN_SHARED) build_tile_prefix<DBM>(grouped_here ? offs : g.offsets, g.E, offs, cum);
   __syncthreads();
   const int ntiles = tile_count<KIND>(g, cum);
   const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0);
@@ -593,7 +608,12 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
 
   constexpr int EPI = KIND == GATE_UP ? EPI_GU : EPI_DN;
   constexpr int LOADS = loads_of<M>();
-  constexpr bool ROWS = KIND == GATE_UP || (KIND == DOWN_ROUTED && ATOMIC);
+  // the row ids of tile i: from the grouping in LDS, or gathered into
+  // rows_buf slot i % 3
+  auto rows_of = [&](int i) -> const int* {
+    return grouped_here ? sorted + place(i).x : rows_buf[i % 3];
+  };
+  const bool ROWS = (KIND == GATE_UP && !grouped_here) || (KIND == DOWN_ROUTED && ATOMIC);
   if (ROWS) {
     gather_rows(g, place(0), rows_buf[0]);
     gather_rows(g, place(1), rows_buf[1]);
@@ -604,7 +624,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     __syncthreads();
   }
   DTile cur, nxt;
-  make_tile<KIND, M>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_buf[0]) : 0, cur);
+  make_tile<KIND, M>(g, place(0), KIND == GATE_UP ? token_of(g, place(0), rows_of(0)) : 0, cur);
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) issue_stage<M>(cur, st, lds_st[st], lds_st[st] + STAGE_A);
 
@@ -614,7 +634,7 @@ __device__ __forceinline__ void decode_body(const GemmArgs& g) {
     // the next tile (its row ids were gathered a tile ago), then the row ids
     // of the one after it
     make_tile<KIND, M>(g, place(li + 1),
-                    KIND == GATE_UP ? token_of(g, place(li + 1), rows_buf[(li + 1) % 3]) : 0, nxt);
+                    KIND == GATE_UP ? token_of(g, place(li + 1), rows_of(li + 1)) : 0, nxt);
     if (KIND == DOWN_ROUTED && ATOMIC && threadIdx.x < 64) {
       // this tile's rows: token and routing weight of each (the weights are
       // gathered straight into LDS as well)

@@ -38,6 +38,15 @@ struct GemmArgs {
   const uint8_t* sw1;
   const uint8_t* sws0;
   const uint8_t* sws1;
+  // Gate/up of a decode batch of at most 256 routed rows on the 32-row
+  // kernels (else NULL): the routed experts [T*k]. Every workgroup groups
+  // the rows itself (the stable counting sort, in LDS) instead of reading
+  // offsets and sorted_rows, and workgroup 0 stores expert_offsets,
+  // sorted_rows and row_pos to the *_out arrays for the later stages.
+  const int32_t* topk_idx;
+  int32_t* offsets_out;
+  int32_t* sorted_out;
+  int32_t* row_pos_out;
 };
 
 int gemm_bm();
@@ -72,11 +81,18 @@ hipError_t launch_router_dequant_mx(const uint8_t* codes, const uint8_t* scales,
                                     int H, hipStream_t st);
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
                                 int H, int E, int dtype, void* ws, hipStream_t st);
+// Small bf16 batches: the router's per-K-group partial planes ([H/64][T][E]
+// fp32, router_planes() of them, 0 when the batch takes another path) for a
+// consumer that sums them in plane order (launch_route with planes).
+int router_planes(int64_t T, int H, int dtype);
+hipError_t launch_router_planes(const void* x, const float* w_router, float* part, int T, int H,
+                                int E, hipStream_t st);
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int score_func, int route_norm, float route_scale, int32_t* idx,
                         float* w, int32_t* counts, hipStream_t st,
-                        int n_group = 1, int topk_group = 1);
+                        int n_group = 1, int topk_group = 1, const float* planes = nullptr,
+                        int np = 0, float* logits_out = nullptr);
 
 // permutation scratch: chunk histograms and per-row ranks
 int permute_chunk_rows();

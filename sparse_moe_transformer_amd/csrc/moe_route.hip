@@ -107,17 +107,45 @@ __device__ __forceinline__ void wave_best(Cand c, uint64_t& wk, int& wi) {
   }
 }
 
+// Where a token's logits come from: the row Lrow, or (planes != nullptr) the
+// sum of np partial planes (plane stride pstride floats, summed in plane
+// order in fp32), which is then also stored to out.
+struct LogitSrc {
+  const float* planes;
+  int np;
+  size_t pstride;
+  float* out;
+};
+
+constexpr int MAX_PLANES = 32;
+
+__device__ __forceinline__ float token_logit(const float* Lrow, const LogitSrc& src, int e) {
+  if (!src.planes) return Lrow[e];
+  // every plane's load issued before the first add (np <= MAX_PLANES)
+  float p[MAX_PLANES];
+#pragma unroll
+  for (int g = 0; g < MAX_PLANES; ++g)
+    p[g] = g < src.np ? src.planes[(size_t)g * src.pstride + e] : 0.f;
+  float v = p[0];
+#pragma unroll
+  for (int g = 1; g < MAX_PLANES; ++g)
+    if (g < src.np) v += p[g];
+  src.out[e] = v;
+  return v;
+}
+
 // Routes token row Lrow (one wavefront): writes its k indices and weights
 // (lanes < k, in selection order) and, if ex_row is given, the indices there.
 // gk: E doubles of LDS for this wave when n_group > 1 (else unused).
 template <int NPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
+__device__ __forceinline__ void route_token(const float* Lrow,
                                             const float* __restrict__ bias, int E, int k,
                                             int score_func, int route_norm, float route_scale,
                                             int32_t* __restrict__ idx_row,
                                             float* __restrict__ w_row, int* ex_row,
                                             int32_t* __restrict__ counts, int n_group = 1,
-                                            int topk_group = 1, double* gk = nullptr) {
+                                            int topk_group = 1, double* gk = nullptr,
+                                            LogitSrc src = LogitSrc{nullptr, 0, 0, nullptr}) {
   const int lane = threadIdx.x & 63;
   double key[NPL], sc[NPL];
   bool live[NPL];
@@ -125,7 +153,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     live[i] = e < E;
-    sc[i] = live[i] ? (double)Lrow[e] : 0.0;
+    sc[i] = live[i] ? (double)token_logit(Lrow, src, e) : 0.0;
   }
   if (score_func == MOE_SCORE_SOFTMAX) {
     double m = -INFINITY;
@@ -238,7 +266,9 @@ __device__ __forceinline__ void route_token(const float* __restrict__ Lrow,
 }
 
 template <int NPL, bool GROUPED>
-__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ logits,
+__global__ void __launch_bounds__(256) route_kernel(const float* logits,
+                                                    const float* __restrict__ planes, int np,
+                                                    float* logits_out,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int score_func, int route_norm,
                                                     float route_scale,
@@ -248,14 +278,17 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
                                                     int topk_group) {
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // the whole wave leaves together
+  const LogitSrc src{planes ? planes + (size_t)t * E : nullptr, np, (size_t)T * E,
+                     planes ? logits_out + (size_t)t * E : nullptr};
   if constexpr (GROUPED) {
     __shared__ double gk[4][64 * NPL];
     route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
                      idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts, n_group,
-                     topk_group, gk[threadIdx.x >> 6]);
+                     topk_group, gk[threadIdx.x >> 6], src);
   } else {
     route_token<NPL>(logits + (size_t)t * E, bias, E, k, score_func, route_norm, route_scale,
-                     idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts);
+                     idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, counts, 1, 1,
+                     nullptr, src);
   }
 }
 
@@ -264,19 +297,20 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int score_func, int route_norm, float route_scale, int32_t* idx,
                         float* w, int32_t* counts, hipStream_t st, int n_group,
-                        int topk_group) {
+                        int topk_group, const float* planes, int np, float* logits_out) {
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block), block(64 * waves_per_block);
   const int npl = (E + 63) / 64;
-#define MOE_ROUTE(N)                                                                         \
-  do {                                                                                       \
-    if (n_group > 1)                                                                         \
-      hipLaunchKernelGGL((route_kernel<N, true>), grid, block, 0, st, logits, bias, T, E, k,  \
-                         score_func, route_norm, route_scale, idx, w, counts, n_group,       \
-                         topk_group);                                                        \
-    else                                                                                     \
-      hipLaunchKernelGGL((route_kernel<N, false>), grid, block, 0, st, logits, bias, T, E, k, \
-                         score_func, route_norm, route_scale, idx, w, counts, 1, 1);         \
+#define MOE_ROUTE(N)                                                                       \
+  do {                                                                                     \
+    if (n_group > 1)                                                                       \
+      hipLaunchKernelGGL((route_kernel<N, true>), grid, block, 0, st, logits, planes, np,  \
+                         logits_out, bias, T, E, k, score_func, route_norm, route_scale,   \
+                         idx, w, counts, n_group, topk_group);                             \
+    else                                                                                   \
+      hipLaunchKernelGGL((route_kernel<N, false>), grid, block, 0, st, logits, planes, np, \
+                         logits_out, bias, T, E, k, score_func, route_norm, route_scale,   \
+                         idx, w, counts, 1, 1);                                            \
   } while (0)
   if (npl <= 1) MOE_ROUTE(1);
   else if (npl <= 2) MOE_ROUTE(2);

@@ -319,14 +319,10 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const uint16_t* __rest
 #undef RT_STEP
 
 // ---------------------------------------------------------------------------
-// Small batches (decode): one launch, no split planes in memory, no reduce
-// kernel. A workgroup of 16 waves computes 32 tokens x 32 experts; wave w
-// takes the w-th sixteenth of the K groups (64 elements each), splits its
-// fp32 weights into hi/mid/lo bf16 in registers (the same exact split as the
-// plane kernel) and runs three MFMAs per sub-step, smallest terms first. The
-// 16 partial tiles are summed in LDS in wave order, so the result does not
-// depend on timing and identical router rows give identical logit columns.
-constexpr int RS_WAVES = 16;
+// Small batches (decode): the fp32 weights are split into hi/mid/lo bf16 in
+// registers (the same exact split as the plane kernel) and three MFMAs run per
+// sub-step, smallest terms first.
+constexpr int RS_WAVES = 16;  // K groups of a small batch: at most 2 * RS_WAVES
 
 __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   hi = f32_to_bf16_bits(v);
@@ -335,56 +331,57 @@ __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uin
   lo = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mid));
 }
 
-__global__ void __launch_bounds__(64 * RS_WAVES) router_small_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
-    int T, int H, int E) {
-  __shared__ float part[RS_WAVES][32 * 32];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Small batches, one plane per K group: workgroup (tile of 32 tokens x 32
+// experts, group g) is one wave that computes the group's 64-element partial
+// and stores it to plane g. The planes are summed
+// in plane order by the consumer (the routing kernel, or
+// router_reduce_kernel), so every logit is the same fixed sequence of fp32
+// operations on its token row and expert row (identical router rows give
+// identical logit columns). Many single-wave workgroups put every group's
+// loads in flight at once.
+__global__ void __launch_bounds__(64) router_group_kernel(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ w,
+                                                         float* __restrict__ part, int T, int H,
+                                                         int E) {
+  const int lane = threadIdx.x & 63;
   const int q = lane >> 5, r = lane & 31;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int ng = H / 64;
-  const int g0 = wave * ng / RS_WAVES, g1 = (wave + 1) * ng / RS_WAVES;
-  const uint16_t* xa = x + (size_t)min(t0 + r, T - 1) * H + 32 * q;
-  const float* wb = w + (size_t)min(e0 + r, E - 1) * H + 32 * q;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32, g = blockIdx.z;
+  const int k = g * 64;
+  const uint16_t* xa = x + (size_t)min(t0 + r, T - 1) * H + 32 * q + k;
+  const float* wb = w + (size_t)min(e0 + r, E - 1) * H + 32 * q + k;
+  u32x4_t a[4];
+  floatx4_t b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(xa + 8 * i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = *reinterpret_cast<const floatx4_t*>(wb + 4 * i);
   floatx16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  for (int g = g0; g < g1; ++g) {
-    const int k = g * 64;
-    u32x4_t a[4];
-    floatx4_t b[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(xa + k + 8 * i);
+  for (int i = 0; i < 4; ++i) {
+    uint16_t h[8], m[8], l[8];
+    const float f[8] = {b[2 * i].x, b[2 * i].y, b[2 * i].z, b[2 * i].w,
+                        b[2 * i + 1].x, b[2 * i + 1].y, b[2 * i + 1].z, b[2 * i + 1].w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = *reinterpret_cast<const floatx4_t*>(wb + k + 4 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // sub-step i: elements 8i..8i+7 of this lane's 32-element run
-      uint16_t h[8], m[8], l[8];
-      const float f[8] = {b[2 * i].x, b[2 * i].y, b[2 * i].z, b[2 * i].w,
-                          b[2 * i + 1].x, b[2 * i + 1].y, b[2 * i + 1].z, b[2 * i + 1].w};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) split3(f[u], h[u], m[u], l[u]);
-      auto pack = [](const uint16_t (&v)[8]) {
-        return u32x4_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                       v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
-      };
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a[i]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(l)), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(m)), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(h)), acc, 0, 0, 0);
-    }
+    for (int u = 0; u < 8; ++u) split3(f[u], h[u], m[u], l[u]);
+    auto pack = [](const uint16_t (&v)[8]) {
+      return u32x4_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                     v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+    };
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a[i]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(l)), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(m)), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, pack(h)), acc, 0, 0, 0);
   }
   // 32x32 MFMA layout: lane l holds rows 8*(v/4) + 4*(l/32) + v%4, column l%32
+  float* out = part + (size_t)g * T * E;
+  const int e = e0 + r;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) part[wave][((v >> 2) * 8 + q * 4 + (v & 3)) * 32 + r] = acc[v];
-  __syncthreads();
-  const int i = threadIdx.x;  // one (token, expert) of the tile per thread
-  float sum = part[0][i];
-#pragma unroll
-  for (int ww = 1; ww < RS_WAVES; ++ww) sum += part[ww][i];
-  const int t = t0 + i / 32, e = e0 + i % 32;
-  if (t < T && e < E) logits[(size_t)t * E + e] = sum;
+  for (int v = 0; v < 16; ++v) {
+    const int t = t0 + (v >> 2) * 8 + q * 4 + (v & 3);
+    if (t < T && e < E) out[(size_t)t * E + e] = acc[v];
+  }
 }
 
 // MXFP8 router weights (E4M3 codes [E, H], E8M0 scales block-major
@@ -435,8 +432,13 @@ int router_kchunks(int64_t T, int E, int H, int dtype) {
   return kc;
 }
 
+int router_planes(int64_t T, int H, int dtype) {
+  return dtype == MOE_BF16 && router_small(T, H) ? H / 64 : 0;
+}
+
 size_t router_ws_bytes(int64_t T, int E, int H, int dtype) {
-  if (dtype != MOE_BF16 || router_small(T, H)) return 0;
+  if (dtype != MOE_BF16) return 0;
+  if (router_small(T, H)) return (size_t)(H / 64) * T * E * 4;
   const int kc = router_kchunks(T, E, H, dtype);
   return (size_t)3 * E * H * 2 + 256 + (kc > 1 ? (size_t)kc * T * E * 4 : 0);
 }
@@ -450,6 +452,14 @@ hipError_t launch_router_dequant_mx(const uint8_t* codes, const uint8_t* scales,
   return hipGetLastError();
 }
 
+hipError_t launch_router_planes(const void* x, const float* w_router, float* part, int T, int H,
+                                int E, hipStream_t st) {
+  dim3 grid((T + 31) / 32, (E + 31) / 32, H / 64);
+  hipLaunchKernelGGL(router_group_kernel, grid, dim3(64), 0, st, static_cast<const uint16_t*>(x),
+                     w_router, part, T, H, E);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
                                 int H, int E, int dtype, void* ws, hipStream_t st) {
   if (dtype != MOE_BF16) {
@@ -459,9 +469,13 @@ hipError_t launch_router_logits(const void* x, const float* w_router, float* log
     return hipGetLastError();
   }
   if (router_small(T, H)) {
-    dim3 grid((T + 31) / 32, (E + 31) / 32);
-    hipLaunchKernelGGL(router_small_kernel, grid, dim3(64 * RS_WAVES), 0, st,
-                       static_cast<const uint16_t*>(x), w_router, logits, T, H, E);
+    // one plane per K group, then their sum in plane order
+    float* part = static_cast<float*>(ws);
+    const hipError_t e = launch_router_planes(x, w_router, part, T, H, E, st);
+    if (e != hipSuccess) return e;
+    const size_t m = (size_t)T * E;
+    hipLaunchKernelGGL(router_reduce_kernel, dim3(grid_blocks(m)), dim3(256), 0, st, part,
+                       H / 64, m, logits);
     return hipGetLastError();
   }
   const int kc = router_kchunks(T, E, H, dtype);

@@ -7,7 +7,10 @@ fp32 atomics).
 
 Every stage is compared with the float64 oracle fed the GPU's own router
 logits: routing and grouping exactly, h, h_shared and the output at the
-layer's bf16 bar (max|err| <= 2e-2 max|ref|)."""
+layer's bf16 bar (max|err| <= 2e-2 max|ref|). Through the single entry
+point, batches of at most 256 routed rows are grouped inside the gate/up
+kernel (token masks up to 64 tokens, counted ranks above); its output is
+held to the same bar."""
 import os
 
 import numpy as np
@@ -51,6 +54,12 @@ DECODE = {
     "m3_like_128_experts": custom(T=48, hidden_size=768, num_experts=128, num_experts_per_tok=4,
                                   moe_intermediate_size=256, num_shared_experts=1,
                                   shared_packed=1, route_scale=2.0),
+    # more than 64 tokens and at most 256 routed rows: the layer groups the
+    # rows inside the gate/up kernel by counting earlier equal rows (64
+    # tokens or fewer take the token-mask ranks; above 256 rows, a grouping
+    # launch runs first)
+    "t120_rows240": custom(T=120, hidden_size=256, num_experts=8, num_experts_per_tok=2,
+                           moe_intermediate_size=256, num_shared_experts=1),
 }
 
 
