@@ -295,3 +295,27 @@ def test_layer_forward_exact_ties_small_batch(E, k):
     assert O.boundary_gap(keys, k) == 0.0
     assert np.array_equal(res["idx"], ridx)
     assert np.allclose(res["w"], rw, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("T,H,E", [(40, 2048, 64), (127, 1472, 33), (5, 64, 8)])
+def test_small_batch_router_planes(T, H, E):
+    """Batches under 128 tokens: the router leaves one partial plane per
+    64-input group (32 planes at H=2048, 23 at H=1472, one at H=64) and the
+    single entry point's routing kernel sums them in plane order, the router
+    entry point's reduce kernel likewise: the two logit arrays agree bit for
+    bit, match the float64 oracle, two identical router rows give identical
+    logit columns, and routing matches the oracle on those logits."""
+    cfg = custom(T=T, hidden_size=H, num_experts=E, num_experts_per_tok=4,
+                 moe_intermediate_size=64, num_shared_experts=1)
+    inp = synth.generate(cfg)
+    inp.w_router[E - 1] = inp.w_router[3]  # a duplicated router row
+    dev = Dev(inp)
+    res = dev.forward(deterministic=1)
+    logits = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(dev.keys, T, dev.x, dev.w_router, logits, dev.ws)
+    torch.cuda.synchronize()
+    L = logits.view(T, E).cpu().numpy()
+    assert np.array_equal(res["logits"], L)
+    assert rel_err(L, O.router_logits(inp.x, inp.w_router)) <= 1e-5
+    assert np.array_equal(L[:, 3], L[:, E - 1])
+    check_routing(cfg, inp, res)
