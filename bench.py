@@ -76,7 +76,7 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
 
 
 GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_decode.hip", "moe_gemm_common.h",
-                "moe_common.h", "moe_kernels.h")
+                "moe_common.h", "moe_kernels.h", "moe_small_sort.h")
 
 
 def gate_up_kernel(cfg: dict, T: int) -> str:

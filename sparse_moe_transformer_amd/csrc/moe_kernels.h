@@ -81,9 +81,11 @@ hipError_t launch_router_dequant_mx(const uint8_t* codes, const uint8_t* scales,
                                     int H, hipStream_t st);
 hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
                                 int H, int E, int dtype, void* ws, hipStream_t st);
-// Small bf16 batches: the router's per-K-group partial planes ([H/64][T][E]
+// Small bf16 batches (T < 128, H <= 64 * ROUTER_MAX_PLANES): the router's
+// per-K-group partial planes ([H/64][T][E]
 // fp32, router_planes() of them, 0 when the batch takes another path) for a
 // consumer that sums them in plane order (launch_route with planes).
+constexpr int ROUTER_MAX_PLANES = 32;
 int router_planes(int64_t T, int H, int dtype);
 hipError_t launch_router_planes(const void* x, const float* w_router, float* part, int T, int H,
                                 int E, hipStream_t st);

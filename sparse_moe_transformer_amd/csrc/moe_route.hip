@@ -117,18 +117,16 @@ struct LogitSrc {
   float* out;
 };
 
-constexpr int MAX_PLANES = 32;
-
 __device__ __forceinline__ float token_logit(const float* Lrow, const LogitSrc& src, int e) {
   if (!src.planes) return Lrow[e];
-  // every plane's load issued before the first add (np <= MAX_PLANES)
-  float p[MAX_PLANES];
+  // every plane's load issued before the first add (np <= ROUTER_MAX_PLANES)
+  float p[ROUTER_MAX_PLANES];
 #pragma unroll
-  for (int g = 0; g < MAX_PLANES; ++g)
+  for (int g = 0; g < ROUTER_MAX_PLANES; ++g)
     p[g] = g < src.np ? src.planes[(size_t)g * src.pstride + e] : 0.f;
   float v = p[0];
 #pragma unroll
-  for (int g = 1; g < MAX_PLANES; ++g)
+  for (int g = 1; g < ROUTER_MAX_PLANES; ++g)
     if (g < src.np) v += p[g];
   src.out[e] = v;
   return v;

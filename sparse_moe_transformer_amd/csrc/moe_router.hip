@@ -322,7 +322,6 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const uint16_t* __rest
 // Small batches (decode): the fp32 weights are split into hi/mid/lo bf16 in
 // registers (the same exact split as the plane kernel) and three MFMAs run per
 // sub-step, smallest terms first.
-constexpr int RS_WAVES = 16;  // K groups of a small batch: at most 2 * RS_WAVES
 
 __device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   hi = f32_to_bf16_bits(v);
@@ -416,7 +415,7 @@ inline int grid_blocks(size_t n) {
 // to fill the chip, each chunk a whole number of 64-element steps (at least
 // three for the tiled kernel) that divides H.
 static bool router_tiled(int64_t T) { return T >= RTT_M; }
-static bool router_small(int64_t T, int H) { return T < RTT_M && H / 64 <= 2 * RS_WAVES; }
+static bool router_small(int64_t T, int H) { return T < RTT_M && H / 64 <= ROUTER_MAX_PLANES; }
 
 int router_kchunks(int64_t T, int E, int H, int dtype) {
   if (dtype != MOE_BF16) return 1;
