@@ -23,8 +23,9 @@
 // MFMAs, one barrier per step. The load stream runs on across tiles: the last
 // two steps of a tile load the first two stages of the next tile, so they are
 // in flight during this tile's epilogue. Each tile's step count is padded to
-// a multiple of three with loads of a zero line (they add exactly zero), so
-// the LDS stage of every step is known at compile time. The three stages are
+// a multiple of three with loads of a zero line, so the LDS stage of every
+// step is known at compile time; the padding steps (at most the tile's last
+// two) skip their MFMAs. The three stages are
 // distinct __shared__ arrays and the barrier is a raw s_barrier, so the
 // compiler does not drain all loads before each LDS read. Nothing that a later
 // step must wait for is loaded after the look-ahead loads of a step (vector
@@ -519,6 +520,16 @@ __device__ void make_tile(const GemmArgs& g, int4 p, const int (&tok)[4], Tile& 
     issue_stage<WM>(TL, J, NA, NB);                           \
     compute_stage<T, KIND, WM>(LA, LB, acc);                  \
   }
+// The same step, its MFMAs skipped when C is false (a padding step of zeros,
+// which would add exactly zero; its loads still run, so every step issues the
+// same loads and the waits stay as they are).
+#define MOE_STEP_IF(TL, J, LA, LB, NA, NB, C)                 \
+  {                                                           \
+    wait_vmcnt<loads_of<WM>()>();                             \
+    __builtin_amdgcn_s_barrier();                             \
+    issue_stage<WM>(TL, J, NA, NB);                           \
+    if (C) compute_stage<T, KIND, WM>(LA, LB, acc);           \
+  }
 
 template <typename T, int KIND, bool ATOMIC, int WM>
 __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
@@ -599,8 +610,10 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
     if (KIND == DOWN_ROUTED && threadIdx.x < BM)
       ep_r = g.sorted_rows[nxt.row0 + min((int)threadIdx.x, nxt.nrows - 1)];
     const int s0 = has_next ? 0 : nxt.nk3;  // nothing to load after the last tile
-    MOE_STEP(nxt, s0, lds_a1, lds_b1, lds_a0, lds_b0)
-    MOE_STEP(nxt, s0 + 1, lds_a2, lds_b2, lds_a1, lds_b1)
+    // the tile's last two steps; padding steps (at most the last two: nk3 -
+    // nk <= 2) skip their MFMAs
+    MOE_STEP_IF(nxt, s0, lds_a1, lds_b1, lds_a0, lds_b0, j + 1 < cur.nk)
+    MOE_STEP_IF(nxt, s0 + 1, lds_a2, lds_b2, lds_a1, lds_b1, j + 2 < cur.nk)
 
     // ---- epilogue of the current tile (next tile's first stages in flight).
     // Full tiles (all rows present, all columns inside N) take a path with no
@@ -731,6 +744,7 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   __builtin_amdgcn_s_barrier();
 }
 #undef MOE_STEP
+#undef MOE_STEP_IF
 
 // one entry per kind, so that profiles name them (WM: the weight format)
 template <typename T, int WM>
