@@ -107,3 +107,36 @@ def test_decode_and_128_row_tiles_agree():
         outs[tile] = a
     assert np.array_equal(outs["128"]["idx"], outs["32"]["idx"])
     assert rel_err(outs["32"]["out"], outs["128"]["out"]) <= TOL["bf16"]
+
+
+def test_batch_sizes_interleaved_on_one_workspace():
+    """One workspace, batch sizes that take every grouping path in turn
+    (inside the gate/up kernel with token masks, the one-workgroup sort, the
+    three-kernel sort) and both GEMM kernels, with no
+    state carried from one call to the next: each output against the oracle,
+    and the first batch size bitwise equal when it comes round again."""
+    cfg = custom(T=300, hidden_size=512, num_experts=16, num_experts_per_tok=4,
+                 moe_intermediate_size=256, num_shared_experts=1)
+    full = synth.generate(cfg)
+    dev = Dev(full)
+    first = None
+    for T in (32, 300, 7, 100, 64, 1, 32):
+        sub = synth.MoeInputs(cfg=dict(cfg, T=T), x=full.x[:T], w_router=full.w_router,
+                              expert_bias=full.expert_bias, w_gate=full.w_gate, w_up=full.w_up,
+                              w_down=full.w_down, ws_gate=full.ws_gate, ws_up=full.ws_up,
+                              ws_down=full.ws_down)
+        d = Dev.__new__(Dev)
+        d.__dict__.update(dev.__dict__)
+        d.inp, d.cfg, d.T = sub, sub.cfg, T
+        d.x = dev.x[: T * cfg["hidden_size"]] if dev.x.dim() == 1 else dev.x[:T]
+        res = d.forward(deterministic=1)
+        check_routing(sub.cfg, sub, res)
+        ref = O.moe_forward(sub, sub.cfg, logits=res["logits"])
+        e = rel_err(res["out"], ref["out"])
+        say(f"[decode] interleaved T={T} rows={T * 4} out {e:.2e}")
+        assert e <= TOL["bf16"]
+        if T == 32:
+            if first is None:
+                first = res["out"]
+            else:
+                assert np.array_equal(first, res["out"])
