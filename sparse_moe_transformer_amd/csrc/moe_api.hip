@@ -100,8 +100,39 @@ struct Ws {
   void* h_shared;
   float* acc;
   void* y_perm;
+  float* parts;  // fused decode FFN partial planes (empty when the shapes never take it)
   size_t total;
 };
+
+// The fused decode FFN (gate/up and down in one kernel, by 128-column slices
+// of the intermediate width into fp32 partial planes that the combine sums):
+// bf16 weights and activations, shapes the kernel takes, at most 32 tokens
+// and 256 routed rows. Testing knobs: MOE_DECODE_FFN=0 turns it off, and so
+// does MOE_GEMM_TILE=128 (the 128-row tile kernels forced).
+bool ffn_shape(const Dims& d) {
+  return d.dtype == MOE_BF16 && d.wfmt == WF_DTYPE && ffn_decode_fits(d.H, d.I, d.E, d.S, d.Is);
+}
+
+bool use_ffn(const Dims& d) {
+  if (!ffn_shape(d) || d.T > 32 || d.T * d.k > 256) return false;
+  if (!ffn_decode_schedulable(d.E, d.I, d.S, d.Is)) return false;
+  if (const char* e = std::getenv("MOE_DECODE_FFN"))
+    if (std::strcmp(e, "0") == 0) return false;
+  if (const char* e = std::getenv("MOE_GEMM_TILE"))
+    if (std::strcmp(e, "128") == 0) return false;
+  return true;
+}
+
+// Partial planes for min(T, 32) tokens whenever the shapes allow the fused
+// path (whatever the batch and the knobs), so a workspace sized for T tokens
+// serves every smaller batch too.
+size_t ffn_parts_bytes(const Dims& d) {
+  if (!ffn_shape(d)) return 0;
+  const size_t T = (size_t)std::min<int64_t>(d.T, 32);
+  const size_t slice = (size_t)ffn_decode_slice();
+  const size_t planes_rows = (size_t)d.I / slice * T * d.k + (size_t)d.S * d.Is / slice * T;
+  return planes_rows * d.H * 4;
+}
 
 Ws carve(const Dims& d, void* base) {
   Ws w{};
@@ -128,6 +159,7 @@ Ws carve(const Dims& d, void* base) {
   w.h_shared = take((size_t)d.T * d.S * d.Is * d.es);
   w.acc = (float*)take((size_t)d.T * d.H * 4);
   w.y_perm = take(rows * d.H * d.es);
+  w.parts = (float*)take(ffn_parts_bytes(d));
   w.total = off;
   return w;
 }
@@ -368,7 +400,39 @@ size_t block_ws_bytes(const Dims& d) {
 struct LayerOut {
   float* topk_w;  // routed weights the combine reads
   void* y_perm;   // unweighted routed rows (fixed-order combine) or NULL
+  PartsSrc parts; // the fused decode FFN's partial planes (parts.p NULL: not taken)
 };
+
+// Expert FFN of a small decode batch in one launch (use_ffn): every slice of
+// every chosen expert and of the shared experts into the partial planes.
+moe_status do_ffn(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
+                  const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                  const void* ws_down, const int32_t* topk_idx, float* parts, hipStream_t st,
+                  PartsSrc* src) {
+  GemmArgs g = base_args(c, d);
+  const int slice = ffn_decode_slice();
+  const int64_t rows = d.T * d.k;
+  g.a = x;
+  g.w0 = w_gate;
+  g.w1 = w_up;
+  g.w2 = w_down;
+  if (d.packed) {
+    g.ws0 = shared_slot(w_gate, d, (size_t)d.I * d.H);
+    g.ws1 = shared_slot(w_up, d, (size_t)d.I * d.H);
+    g.ws2 = shared_slot(w_down, d, (size_t)d.H * d.I);
+  } else {
+    g.ws0 = ws_gate;
+    g.ws1 = ws_up;
+    g.ws2 = ws_down;
+  }
+  // slices per routed expert and of the shared width (T <= 32 rows each)
+  g.nt_routed = d.I / slice;
+  g.nt_shared = d.S ? d.S * d.Is / slice : 0;
+  g.topk_idx = topk_idx;
+  g.parts = parts;
+  *src = PartsSrc{parts, g.nt_routed, g.nt_shared, (int)rows};
+  return hip_ok(launch_ffn_decode(g, st));
+}
 
 // The router weights the router GEMM reads: as given (fp32), or MXFP8 codes
 // dequantised exactly into the workspace first.
@@ -419,6 +483,12 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
                               cfg->route_norm, cfg->route_scale, idx, tw, nullptr, st,
                               cfg->n_group, cfg->topk_group, planes, np, planes ? lo : nullptr)));
   const Grouping grp{idx, w.offsets, w.sorted_rows, w.row_pos};
+  res->topk_w = tw;
+  res->y_perm = nullptr;
+  res->parts = PartsSrc{nullptr, 0, 0, 0};
+  if (use_ffn(d))
+    return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, idx, w.parts, st,
+                  &res->parts);
   const bool fused = group_in_gate_up(d);
   if (!fused)
     MOE_TRY(hip_ok(launch_permute(idx, T * d.k, d.E, w.offsets, w.sorted_rows, w.row_pos,
@@ -564,6 +634,8 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
   MOE_TRY(run_layer(cfg, d, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                     ws_down, mx, router_logits_in, router_logits_out, topk_idx_out, topk_w_out,
                     deterministic, w, st, &lo));
+  if (lo.parts.p)
+    return hip_ok(launch_combine_parts(lo.parts, lo.topk_w, out, (int)T, d.H, d.k, d.dtype, st));
   return hip_ok(launch_combine(w.acc, lo.y_perm, w.row_pos, lo.topk_w, out, (int)T, d.H, d.k,
                                d.dtype, st));
 }
@@ -631,6 +703,10 @@ moe_status moe_block_forward(const moe_config* cfg, const moe_norm_config* norm,
   MOE_TRY(run_layer(cfg, d, xn, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                     ws_down, mx, nullptr, router_logits_out, topk_idx_out, topk_w_out,
                     deterministic, w, st, &lo));
+  if (lo.parts.p)
+    return hip_ok(launch_combine_norm_parts(lo.parts, lo.topk_w, post_norm_w, norm->add_one,
+                                            norm->rms_norm_eps, h, out, (int)T, d.H, d.k,
+                                            d.dtype, st));
   return hip_ok(launch_combine_norm(w.acc, lo.y_perm, w.row_pos, lo.topk_w, post_norm_w,
                                     norm->add_one, norm->rms_norm_eps, h, out, (int)T, d.H, d.k,
                                     d.dtype, st));

@@ -8,6 +8,7 @@
 // flight together; the sum still runs slot by slot in j order.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "moe_parts.h"
 
 namespace {
 
@@ -54,7 +55,40 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
+// The same from the fused decode FFN's partial planes.
+template <typename T>
+__global__ void __launch_bounds__(256) combine_parts_kernel(PartsSrc parts,
+                                                            const float* __restrict__ topk_w,
+                                                            T* __restrict__ out, int T_, int H,
+                                                            int k) {
+  const int per_row = H / CW;
+  const size_t n = (size_t)T_ * per_row;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / per_row;
+    const int c = (int)(i - t * per_row) * CW;
+    float v[CW];
+    parts_value(parts, topk_w, t, c, T_, H, k, v);
+    Vec8<T>::store(out + t * H + c, v);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_parts(const PartsSrc& parts, const float* topk_w, void* out, int T,
+                                int H, int k, int dtype, hipStream_t st) {
+  const size_t n = (size_t)T * (H / CW);
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  dim3 grid((unsigned)blocks), block(256);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_parts_kernel<bf16_t>, grid, block, 0, st, parts, topk_w,
+                       static_cast<bf16_t*>(out), T, H, k);
+  else
+    hipLaunchKernelGGL(combine_parts_kernel<float>, grid, block, 0, st, parts, topk_w,
+                       static_cast<float*>(out), T, H, k);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* acc, const void* y_perm, const int32_t* row_pos,
                           const float* topk_w, void* out, int T, int H, int k, int dtype,

@@ -41,6 +41,9 @@
 // as in the 128-input MXFP8 mode. Each 16-byte weight chunk is one scale
 // block of 32 inputs; sub-step s of lane half q takes dword s % 4 of chunk
 // 2q + s / 4 through the scaled fp4 conversion.
+#include <algorithm>
+#include <cstdlib>
+
 #include "moe_common.h"
 #include "moe_gemm_common.h"
 #include "moe_kernels.h"
@@ -130,6 +133,16 @@ __device__ __forceinline__ const char* sptr(const char* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   return reinterpret_cast<const char*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+// A kernel-argument pointer as an opaque scalar value. A select between two
+// such values stays a scalar select; between the plain arguments the compiler
+// turns it into a load from a selected argument address, one more dependent
+// round trip.
+template <typename T>
+__device__ __forceinline__ T* sval(T* p) {
+  uint64_t u = (uint64_t)(uintptr_t)p;
+  asm volatile("" : "+s"(u));
+  return reinterpret_cast<T*>((uintptr_t)u);
 }
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, const void* lds) {
   const char* sbase = sptr(base);
@@ -390,15 +403,19 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
   t.e = p.z;
   const int nt = p.w;
   const int row = a_row();
-  const int w = threadIdx.x >> 6;
+  // the wave index as a scalar: the gate / up weight and scale pointers are
+  // then picked with scalar selects (from a per-lane index the compiler
+  // loads the chosen kernel argument with a vector load, whose wait would
+  // also drain the weight loads in flight)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (KIND == GATE_UP) {
     t.n0 = nt * 128;
     t.N = t.shared ? g.S * g.Is : g.I;
     t.abase = static_cast<const char*>(g.a);
     t.aoff = ((uint32_t)tok * (uint32_t)H + (uint32_t)(lane_chunk(row) * EPC)) * 2u;
     // waves 0, 1 load gate rows (weight rows 0..127), waves 2, 3 the up rows
-    const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? g.ws0 : g.w0)
-                                                    : (t.shared ? g.ws1 : g.w1));
+    const char* wm = static_cast<const char*>(w < 2 ? (t.shared ? sval(g.ws0) : sval(g.w0))
+                                                    : (t.shared ? sval(g.ws1) : sval(g.w1)));
     const uint32_t rb = (uint32_t)row_bytes<M>(H);
     t.bbase = wm + (t.shared ? 0 : (size_t)t.e * g.I * rb);
     if (row64<M>()) {
@@ -421,7 +438,8 @@ __device__ __forceinline__ void make_tile(const GemmArgs& g, int4 p, int tok, DT
       // of width Is one after another (one, slot E, when packed), so a
       // shared column n is column n - s*Is of matrix s = n / Is
       const int ns = t.shared ? g.Is : g.I;
-      const uint8_t* sm = w < 2 ? (t.shared ? g.sws0 : g.sw0) : (t.shared ? g.sws1 : g.sw1);
+      const uint8_t* sm = w < 2 ? (t.shared ? sval(g.sws0) : sval(g.sw0))
+                                : (t.shared ? sval(g.sws1) : sval(g.sw1));
       const int n = min(t.n0 + (scale_lane_row() & 127), t.N - 4);
       const int se = t.shared ? n / ns : 0;
       t.sbase = reinterpret_cast<const char*>(sm) + (t.shared ? 0 : (size_t)t.e * (H / 32) * ns);
@@ -703,6 +721,409 @@ __global__ void __launch_bounds__(NTHR) moe_down_routed_atomic_decode_kernel(Gem
 }
 
 // ---------------------------------------------------------------------------
+// Fused expert FFN of a small decode batch (bf16 weights; at most 32 tokens
+// and 256 routed rows; H = 256 * NT2 with NT2 = 2 or 4; the routed and
+// shared intermediate widths multiples of 128; E <= FFN_MAX_E).
+//
+// An expert's output down(act(gate x, up x)) (mlxcel #845 "Routing detail")
+// is a sum over the columns of h, so it splits into 128-column slices of I:
+// a work item is slice c of one expert (or of the shared experts' combined
+// width). Phase 1 is the gate/up tile above for n-tile c (K = H); its
+// epilogue keeps the activated 32 x 128 slice as bf16 in LDS, the values the
+// two-kernel path stores to h. Phase 2 multiplies that slice by columns
+// 128c .. 128c+127 of the down matrix for all H outputs: NT2 n-tiles of 256
+// weight rows, two 64-input K-steps each, accumulated side by side. Both
+// phases stream weight K-steps through the same four LDS stages, so the
+// weight stream runs on from the gate/up rows into the down rows and into
+// the next item. Phase-2 stages still carry the activation rows' load (of x,
+// never read) so that every stage is the same nine loads per thread and the
+// fixed load-counter waits hold. The fp32 product of slice c for routed row
+// r = t*k + j goes to row r of partial plane c (shared slices: row t of the
+// shared planes); the combine adds a row's planes in plane order and then
+// weights the sum. Phase-2 MFMAs take the weight rows as the A operand, so a
+// lane holds four consecutive output columns of one row and stores them at
+// once.
+//
+// Schedule. The potential items are the ns = S*Is/128 shared slices, then
+// slice q % (I/128) of expert q / (I/128) for q = p - ns. Workgroup b owns
+// potential item b and issues the weight loads of its first three K-steps
+// at once, before it knows whether the expert was chosen by any token (the
+// shared slices, first, always run at once); meanwhile it
+// copies the routed experts to LDS and works out, the same way in every
+// workgroup, which items are real and who runs those beyond the grid. A
+// workgroup whose own item is real keeps its loads and adds only the
+// activation rows; the real items beyond the grid go one each to the
+// workgroups whose own item is not (in order), any left over round-robin to
+// all workgroups.
+namespace {
+
+constexpr int FFN_CH = 128;      // intermediate columns per work item
+constexpr int FFN_MAX_E = 256;
+constexpr int FFN_MAX_ITEMS = 8; // work items per workgroup (the host checks)
+constexpr int FFN_MAX_GRID = 256;
+static_assert(FFN_MAX_E % 64 == 0, "chosen-expert mask words");
+
+// Phase-2 weight rows of an item: columns 128c .. 128c+127 of the down
+// matrix (routed: expert e's [H, I]; shared: matrix s of the S [H, Is]
+// matrices, the one that holds concatenated column 128c).
+struct FTile {
+  const char* bbase;  // row 0, column 128c of the slice's down matrix
+  uint32_t boff[8];   // this lane's rows (within a 256-row n-tile) + chunks
+  int rb;             // bytes per down-matrix row
+};
+
+__device__ __forceinline__ void make_ftile(const GemmArgs& g, int4 p, FTile& f) {
+  const int shared = p.y >> 16, e = p.z;
+  const int col = p.w * FFN_CH;
+  if (shared) {
+    const int s = col / g.Is;
+    f.rb = 2 * g.Is;
+    f.bbase = static_cast<const char*>(g.ws2) + ((size_t)s * g.H * g.Is + (col - s * g.Is)) * 2;
+  } else {
+    f.rb = 2 * g.I;
+    f.bbase = static_cast<const char*>(g.w2) + ((size_t)e * g.H * g.I + col) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int br = b_row(j);
+    f.boff[j] = (uint32_t)br * (uint32_t)f.rb + (uint32_t)(lane_chunk(br) * 16);
+  }
+}
+
+// The activation-row load (one per thread) and the weight-row loads (eight)
+// of gate/up K-step j (bf16; together the loads of issue_stage<W_BF16>).
+__device__ __forceinline__ void issue_gu_a(const DTile& t, int j, u32x4_t* la) {
+  dma16(t.abase + (long)j * KSB, t.aoff, la + 8 * (threadIdx.x >> 6) * NCH);
+}
+__device__ __forceinline__ void issue_gu_b(const DTile& t, int j, u32x4_t* lb) {
+  const int w = threadIdx.x >> 6;
+  const char* bb = t.bbase + (long)j * KSB;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
+}
+
+// Loads of phase-2 step jj (n-tile jj / 2, K-step jj % 2): the activation
+// rows of gate/up K-step jj (x, not read) and 256 down-matrix rows.
+__device__ __forceinline__ void issue_ffn_down(const DTile& t, const FTile& f, int jj,
+                                               u32x4_t* la, u32x4_t* lb) {
+  const int w = threadIdx.x >> 6;
+  dma16(t.abase + (long)jj * KSB, t.aoff, la + 8 * w * NCH);
+  const char* bb = f.bbase + (long)(jj >> 1) * 256 * f.rb + (long)(jj & 1) * KSB;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma16(bb, f.boff[q], lb + (64 * w + 8 * q) * NCH);
+}
+
+// One phase-2 K-step: h slice rows (la, one K-step of the LDS copy) against
+// the stage's down rows; wave w owns output columns 64w .. 64w+63 of the
+// n-tile, block nb the 32 at 64w + 32nb.
+__device__ __forceinline__ void compute_ffn_down(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, la[r * NCH + ((2 * s + q) ^ swz(r))]);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = 64 * w + 32 * nb + r;
+      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, lb[row * NCH + ((2 * s + q) ^ swz(row))]);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[nb], 0, 0, 0);
+    }
+  }
+}
+
+// Phase-1 epilogue: act(gate, up) as bf16 into the LDS slice (two K-steps of
+// 64 columns, rows laid out like a stage's activation rows). Lane (q, r) of
+// wave w holds column 32w + r of rows acc_row(0, v, q).
+__device__ __forceinline__ void ffn_h_to_lds(const GemmArgs& g, const Acc2& acc, u32x4_t* lds_h) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 5, r = lane & 31;
+  const int ch = 4 * (w & 1) + (r >> 3);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(lds_h + (w >> 1) * DBM * NCH);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = acc_row(0, v, q);
+    hb[(m * NCH + (ch ^ swz(m))) * 8 + (r & 7)] =
+        f32_to_bf16_bits(act_apply(acc[0][v], acc[1][v], g.act));
+  }
+}
+
+// Phase-2 epilogue: 2 * NT2 * 4 16-byte stores per thread into the item's
+// partial plane (routed planes [I/128][T*k][H] by routed row, then the
+// shared [S*Is/128][T][H] by token); rows past the item's are pushed out of
+// range. rows: the item's row ids (LDS).
+template <int NT2>
+__device__ __forceinline__ void ffn_epilogue(const GemmArgs& g, int4 p, const int* rows,
+                                             const Acc2 (&dacc)[NT2]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = lane >> 5, r = lane & 31;
+  const int nrows = p.y & 0xFFFF, shared = p.y >> 16, c = p.w;
+  const size_t routed_rows = (size_t)g.T * g.k;
+  float* plane = shared ? g.parts + ((size_t)g.nt_routed * routed_rows + (size_t)c * g.T) * g.H
+                        : g.parts + (size_t)c * routed_rows * g.H;
+  const __amdgpu_buffer_rsrc_t rs = out_rsrc(plane);
+  const bool ok = r < nrows;
+  const uint32_t row = (uint32_t)rows[min(r, nrows - 1)];
+#pragma unroll
+  for (int nt = 0; nt < NT2; ++nt)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int n = nt * 256 + 64 * w + 32 * nb + acc_row(0, 4 * v4, q);
+        const u32x4_t val = {__float_as_uint(dacc[nt][nb][4 * v4]),
+                             __float_as_uint(dacc[nt][nb][4 * v4 + 1]),
+                             __float_as_uint(dacc[nt][nb][4 * v4 + 2]),
+                             __float_as_uint(dacc[nt][nb][4 * v4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            val, rs, ok ? (row * (uint32_t)g.H + (uint32_t)n) * 4u : kDropped, 0, 0);
+      }
+}
+
+// Potential item p as a place (row-list slot 0, nrows, expert, slice).
+__device__ __forceinline__ int4 ffn_potential(const GemmArgs& g, int p, int nrows) {
+  const int nr = g.nt_routed;
+  const int ns = g.nt_shared;
+  if (p < ns) return make_int4(0, nrows | (1 << 16), 0, p);
+  return make_int4(0, nrows, (p - ns) / nr, (p - ns) % nr);
+}
+
+// The token of this lane's activation row (rows: the item's row ids).
+__device__ __forceinline__ int ffn_token(const GemmArgs& g, int4 p, const int* rows) {
+  const int R = min(a_row(), (p.y & 0xFFFF) - 1);
+  return (p.y >> 16) ? rows[R] : div_k(rows[R], g.k, g.kmagic);
+}
+
+}  // namespace
+
+template <int NT2>
+__global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
+  constexpr int NST = 4;
+  constexpr int LOADS = loads_of<W_BF16>();
+  constexpr int NK1 = 4 * NT2;       // gate/up K-steps (K = H = 256 NT2)
+  constexpr int NK = NK1 + 2 * NT2;  // + down: NT2 n-tiles x two 64-input K-steps
+  static_assert(NK % NST == 0, "an item is a whole number of stage rounds");
+  // vector memory ops of a phase-2 epilogue per thread (exact: the waits of
+  // the next item's first steps count them)
+  constexpr int EPI = 8 * NT2;
+  constexpr int STAGE = stage_u4<W_BF16>();
+  constexpr int STAGE_A = stage_a<W_BF16>();
+  __shared__ __align__(16) u32x4_t lds_st[NST][STAGE];
+  __shared__ __align__(16) u32x4_t lds_h[2 * DBM * NCH];  // the item's activated slice
+  __shared__ __align__(16) int tk[256];          // routed experts of the batch's rows
+  __shared__ int chosen[FFN_MAX_E];              // expert chosen by any row
+  __shared__ int4 items[FFN_MAX_ITEMS];          // this workgroup's items (x: row-list slot)
+  __shared__ int rows_of[FFN_MAX_ITEMS][DBM];    // their row ids
+  __shared__ int n_items, own_real;
+
+  // the kernel arguments the prologue needs, fetched in one batch of scalar
+  // loads (left to itself the compiler fetches them one by one as the
+  // prologue reaches them: a round trip each before the first weight load)
+  asm volatile("" ::"s"(g.topk_idx), "s"(g.a), "s"(g.w0), "s"(g.w1), "s"(g.ws0), "s"(g.ws1),
+               "s"(g.T), "s"(g.k), "s"(g.E), "s"(g.H), "s"(g.I), "s"(g.S), "s"(g.Is),
+               "s"(g.nt_routed), "s"(g.nt_shared));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b = blockIdx.x, G = gridDim.x;
+  const int rows = g.T * g.k, nr = g.nt_routed, E = g.E;
+  const int P = E * nr + g.nt_shared;  // potential items (G <= P: the host checks)
+  const uint64_t lt = (1ull << lane) - 1;
+
+  // the routed experts into LDS (one load per thread; lanes past the rows
+  // repeat the last), then the weight rows of the own item's first three
+  // K-steps
+  for (int e = threadIdx.x; e < E; e += NTHR) chosen[e] = 0;
+  dma4(reinterpret_cast<const char*>(g.topk_idx), (uint32_t)min((int)threadIdx.x, rows - 1) * 4u,
+       tk + 64 * w);
+  DTile cur, nxt;
+  FTile fd;
+  make_tile<GATE_UP, W_BF16>(g, ffn_potential(g, b, 1), 0, cur);
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue_gu_b(cur, st, lds_st[st] + STAGE_A);
+  wait_vmcnt<(NST - 1) * (LOADS - 1)>();  // the expert ids have landed
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  if ((int)threadIdx.x < rows && (unsigned)tk[threadIdx.x] < (unsigned)E) chosen[tk[threadIdx.x]] = 1;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+
+  // wave 0: which potential items are real (every shared slice; a routed
+  // slice when its expert was chosen) and this workgroup's list: its own item
+  // if real, then the real items p >= G handed to it. Every workgroup derives
+  // the same assignment: the i-th real item beyond the grid goes to the i-th
+  // workgroup (in index order) whose own item is not real, or round-robin
+  // over all workgroups once those are used up. Counts come from the chosen
+  // experts' bit mask; only the items beyond the grid are visited.
+  if (w == 0) {
+    uint64_t cm[FFN_MAX_E / 64];
+#pragma unroll
+    for (int j = 0; j < FFN_MAX_E / 64; ++j)
+      cm[j] = __ballot(lane + 64 * j < E && chosen[lane + 64 * j] != 0);
+    auto chosen_e = [&](int e) -> bool { return (cm[e >> 6] >> (e & 63)) & 1; };
+    // unreal potential items below p: the slices of unchosen experts
+    const int ns = g.nt_shared;
+    auto unreal_below = [&](int p) -> int {
+      const int pr = min(max(p - ns, 0), E * nr);
+      const int e = pr / nr, c = pr - e * nr;
+      int chosen_lt = 0;
+#pragma unroll
+      for (int j = 0; j < FFN_MAX_E / 64; ++j) {
+        const int lo = 64 * j;
+        if (e >= lo + 64) chosen_lt += __popcll(cm[j]);
+        else if (e > lo) chosen_lt += __popcll(cm[j] & ((1ull << (e - lo)) - 1));
+      }
+      return (e - chosen_lt) * nr + (c > 0 && !chosen_e(e) ? c : 0);
+    };
+    const bool own = b < ns || chosen_e((b - ns) / nr);
+    const int nfree = unreal_below(G);
+    const int my_rank = own ? -1 : unreal_below(b);
+    if (own && lane == 0) items[0] = ffn_potential(g, b, 0);
+    int mine = own ? 1 : 0, i0 = 0;
+    for (int p0 = G; p0 < P; p0 += 64) {
+      const int p = p0 + lane;
+      const bool beyond = p < P && (p < ns || chosen_e((p - ns) / nr));
+      const uint64_t bm = __ballot(beyond);
+      const int i = i0 + __popcll(bm & lt);
+      const bool to_me = beyond && (i < nfree ? i == my_rank : (i - nfree) % G == b);
+      const uint64_t tm = __ballot(to_me);
+      const int slot = mine + __popcll(tm & lt);
+      if (to_me && slot < FFN_MAX_ITEMS) items[slot] = ffn_potential(g, p, 0);
+      mine += __popcll(tm);
+      i0 += __popcll(bm);
+    }
+    if (lane == 0) {
+      n_items = min(mine, FFN_MAX_ITEMS);
+      own_real = own;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const int n_my = n_items;
+
+  // each item's rows: routed slices the rows that chose the expert, in row
+  // order (at most T, one per token; lane l checks rows 4l .. 4l+3); shared
+  // slices the T tokens
+  for (int it = w; it < n_my; it += NTHR / 64) {
+    const int4 p = items[it];
+    int cnt = 0;
+    if (p.y >> 16) {
+      if (lane < g.T) rows_of[it][lane] = lane;
+      cnt = g.T;
+    } else {
+      const int4 v = reinterpret_cast<const int4*>(tk)[lane];
+      const int r0 = 4 * lane;
+      const bool h0 = r0 < rows && v.x == p.z, h1 = r0 + 1 < rows && v.y == p.z;
+      const bool h2 = r0 + 2 < rows && v.z == p.z, h3 = r0 + 3 < rows && v.w == p.z;
+      const uint64_t m0 = __ballot(h0), m1 = __ballot(h1), m2 = __ballot(h2), m3 = __ballot(h3);
+      int at = __popcll(m0 & lt) + __popcll(m1 & lt) + __popcll(m2 & lt) + __popcll(m3 & lt);
+      if (h0 && at < DBM) rows_of[it][at] = r0;
+      at += h0;
+      if (h1 && at < DBM) rows_of[it][at] = r0 + 1;
+      at += h1;
+      if (h2 && at < DBM) rows_of[it][at] = r0 + 2;
+      at += h2;
+      if (h3 && at < DBM) rows_of[it][at] = r0 + 3;
+      // a token chooses an expert at most once: cnt <= T <= 32
+      cnt = min(__popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3), DBM);
+    }
+    if (lane == 0) items[it] = make_int4(it, cnt | (p.y & 0x10000), p.z, p.w);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  if (n_my == 0) {
+    // nothing to run: let the own item's loads land before leaving
+    wait_vmcnt<0>();
+    return;
+  }
+  auto place = [&](int i) -> int4 {
+    const int4 p = items[min(i, n_my - 1)];
+    return make_int4(__builtin_amdgcn_readfirstlane(p.x), __builtin_amdgcn_readfirstlane(p.y),
+                     __builtin_amdgcn_readfirstlane(p.z), __builtin_amdgcn_readfirstlane(p.w));
+  };
+
+  // the first item: the own one (its weight loads are in flight; add the
+  // activation rows' loads) or a handed-over one (wait for the own item's
+  // loads to land, then load all of its first three K-steps)
+  const int4 p0 = place(0);
+  const bool own = __builtin_amdgcn_readfirstlane(own_real) != 0;
+  make_tile<GATE_UP, W_BF16>(g, p0, ffn_token(g, p0, rows_of[p0.x]), cur);
+  if (own) {
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) issue_gu_a(cur, st, lds_st[st]);
+  } else {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) {
+      issue_gu_a(cur, st, lds_st[st]);
+      issue_gu_b(cur, st, lds_st[st] + STAGE_A);
+    }
+  }
+
+  bool first = true;
+  for (int li = 0;; ++li) {
+    const bool has_next = li + 1 < n_my;
+    const int4 pc = place(li), pn = place(li + 1);
+    make_ftile(g, pc, fd);
+    make_tile<GATE_UP, W_BF16>(g, pn, ffn_token(g, pn, rows_of[pn.x]), nxt);
+    Acc2 acc;
+    Acc2 dacc[NT2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[nb][v] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT2; ++nt) dacc[nt][nb][v] = 0.f;
+      }
+    // step s: wait for stage s, barrier, issue step s + 3 (this item's
+    // gate/up or down rows, or the next item's first steps), compute stage
+    // s; after the last gate/up step the slice goes to LDS. Waits: loads
+    // issued after stage s's are two stages, plus the previous item's
+    // epilogue stores in an item's first three steps; for the own first item
+    // the activation loads of steps 0 .. 2 came after the weight loads, so
+    // its steps 0 and 1 have 2 and 10 younger loads
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      if (s == 0 && first && own) wait_vmcnt<2>();
+      else if (s == 1 && first && own) wait_vmcnt<LOADS + 1>();
+      else if (s < NST - 1 && !first) wait_vmcnt<(NST - 2) * LOADS + EPI>();
+      else wait_vmcnt<(NST - 2) * LOADS>();
+      __builtin_amdgcn_s_barrier();
+      const int sl = s + NST - 1;
+      u32x4_t* la = lds_st[sl % NST];
+      if (sl < NK1) {
+        issue_gu_a(cur, sl, la);
+        issue_gu_b(cur, sl, la + STAGE_A);
+      } else if (sl < NK) {
+        issue_ffn_down(cur, fd, sl - NK1, la, la + STAGE_A);
+      } else {
+        issue_gu_a(nxt, sl - NK, la);
+        issue_gu_b(nxt, sl - NK, la + STAGE_A);
+      }
+      const u32x4_t* lc = lds_st[s % NST];
+      if (s < NK1) {
+        compute_stage<GATE_UP, W_BF16>(lc, lc + STAGE_A, acc);
+        if (s == NK1 - 1) {
+          ffn_h_to_lds(g, acc, lds_h);
+          // the slice is in LDS before the next step's barrier
+          __asm__ __volatile__("" ::: "memory");
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __asm__ __volatile__("" ::: "memory");
+        }
+      } else {
+        compute_ffn_down(lds_h + ((s - NK1) & 1) * DBM * NCH, lc + STAGE_A, dacc[(s - NK1) >> 1]);
+      }
+    }
+    ffn_epilogue<NT2>(g, pc, rows_of[pc.x], dacc);
+    if (!has_next) break;
+    first = false;
+    cur = nxt;
+  }
+  // the look-ahead loads after the last item are not used: let them land
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 int gemm_decode_bm() { return DBM; }
@@ -807,4 +1228,56 @@ hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t
   const Variant v = pick(g, false, true, false);
   if (atomic) return DEC_LAUNCH(moe_down_routed_atomic_decode_kernel, v, n, g, st);
   return DEC_LAUNCH(moe_down_routed_decode_kernel, v, n, g, st);
+}
+
+// Shapes the fused FFN kernel takes: H = 512 or 1024 (NT2 = 2 or 4), the
+// intermediate widths whole 128-column slices, E within the kernel's LDS
+// arrays, and one expert's (and all shared experts') weights within the
+// per-lane 32-bit offsets. The batch limits (T <= 32 tokens, T * k <= 256
+// rows) and bf16 weights are the caller's to check.
+bool ffn_decode_fits(int H, int I, int E, int S, int Is) {
+  if (H != 512 && H != 1024) return false;
+  if (I <= 0 || I % FFN_CH || E > FFN_MAX_E) return false;
+  if (S && (Is <= 0 || Is % FFN_CH)) return false;
+  const uint64_t lim = 1ull << 31;
+  return (uint64_t)H * I * 2 < lim && (uint64_t)S * H * Is * 2 < lim;
+}
+
+int ffn_decode_slice() { return FFN_CH; }
+
+// Grid of the fused kernel for P potential items: one workgroup per compute
+// unit at most (MOE_FFN_GRID=n caps it further: a testing knob that makes
+// workgroups run several items).
+static int ffn_grid(int P) {
+  int G = std::min(P, std::min(dec_num_cus(), FFN_MAX_GRID));
+  if (const char* e = std::getenv("MOE_FFN_GRID")) {
+    const int cap = std::atoi(e);
+    if (cap > 0) G = std::min(G, cap);
+  }
+  return G;
+}
+
+// The items of a workgroup fit its list: its own item plus the real items
+// beyond the grid handed to it, at most ceil((P - G) / G) of them.
+static bool ffn_items_fit(int P, int G) {
+  return G > 0 && 1 + (P - G + G - 1) / G <= FFN_MAX_ITEMS;
+}
+
+bool ffn_decode_schedulable(int E, int I, int S, int Is) {
+  const int P = E * (I / FFN_CH) + (S ? S * Is / FFN_CH : 0);
+  return ffn_items_fit(P, ffn_grid(P));
+}
+
+hipError_t launch_ffn_decode(const GemmArgs& g, hipStream_t st) {
+  const int P = g.E * g.nt_routed + g.nt_shared;
+  const int G = ffn_grid(P);
+  if (!ffn_items_fit(P, G) || g.T < 1 || g.T > DBM || g.T * g.k > 256 || g.E > FFN_MAX_E)
+    return hipErrorInvalidValue;
+  if (g.H == 1024)
+    hipLaunchKernelGGL(moe_ffn_decode_kernel<4>, dim3((unsigned)G), dim3(NTHR), 0, st, g);
+  else if (g.H == 512)
+    hipLaunchKernelGGL(moe_ffn_decode_kernel<2>, dim3((unsigned)G), dim3(NTHR), 0, st, g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }

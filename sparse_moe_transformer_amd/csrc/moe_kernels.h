@@ -47,6 +47,12 @@ struct GemmArgs {
   int32_t* offsets_out;
   int32_t* sorted_out;
   int32_t* row_pos_out;
+  // Fused decode FFN (launch_ffn_decode, which also reads topk_idx): the
+  // routed and shared down weights and the fp32 partial planes,
+  // [I/128][T*k][H] (by routed row t*k + j) then [S*Is/128][T][H].
+  const void* w2;
+  const void* ws2;
+  float* parts;
 };
 
 int gemm_bm();
@@ -64,6 +70,15 @@ hipError_t launch_gate_up_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st);
+// Fused gate/up + down of decode batches of at most 32 tokens and 256 routed
+// rows (bf16 weights; shapes: ffn_decode_fits), by 128-column slices of the
+// intermediate width (ffn_decode_slice) into fp32 partial planes.
+bool ffn_decode_fits(int H, int I, int E, int S, int Is);
+// ... and every workgroup's share of the work items fits its list (depends
+// on the device's compute units)
+bool ffn_decode_schedulable(int E, int I, int S, int Is);
+int ffn_decode_slice();
+hipError_t launch_ffn_decode(const GemmArgs& g, hipStream_t st);
 
 // 256-row tile kernels for prefill-sized bf16 batches (every K length a
 // multiple of 64; per-lane 32-bit offsets: gemm_wide_fits).
@@ -108,6 +123,17 @@ hipError_t launch_combine(const float* acc, const void* y_perm, const int32_t* r
                           const float* topk_w, void* out, int T, int H, int k, int dtype,
                           hipStream_t st);
 
+// fp32 partial planes of the fused decode FFN: nr routed planes [rows][H]
+// (rows = T*k, indexed by routed row t*k + j), then ns shared planes [T][H].
+struct PartsSrc {
+  const float* p;
+  int nr, ns, rows;
+};
+// out[t] = sum of the shared planes + sum_j topk_w[t,j] * (sum of the routed
+// planes at row t*k+j), every sum in index order
+hipError_t launch_combine_parts(const PartsSrc& parts, const float* topk_w, void* out, int T,
+                                int H, int k, int dtype, hipStream_t st);
+
 // RMSNorm rows (one workgroup per row, H <= 8192) and the finalising combine
 // with the post-norm and the residual add
 bool norm_fits(int H);
@@ -117,3 +143,6 @@ hipError_t launch_combine_norm(const float* acc, const void* y_perm, const int32
                                const float* topk_w, const float* w, int add_one, float eps,
                                const void* residual, void* out, int T, int H, int k, int dtype,
                                hipStream_t st);
+hipError_t launch_combine_norm_parts(const PartsSrc& parts, const float* topk_w, const float* w,
+                                     int add_one, float eps, const void* residual, void* out,
+                                     int T, int H, int k, int dtype, hipStream_t st);

@@ -5,7 +5,9 @@
 //   rmsnorm_kernel:      y[t] = x[t] * r_t * (w + off),
 //                        r_t = 1 / sqrt(sum_i x[t,i]^2 / H + eps)
 //   combine_norm_kernel: v[t] = acc[t] (+ sum_j topk_w[t,j] * y_perm[row_pos[t*k+j]]
-//                        in j order), then out[t] = residual[t] + v[t] * r_t * (w + off)
+//                        in j order), or v[t] from the fused decode FFN's partial
+//                        planes (moe_parts.h), then
+//                        out[t] = residual[t] + v[t] * r_t * (w + off)
 //
 // off = 1 gives the Gemma-style scale of MiniMax-M3 (mlxcel issue #763,
 // Norms bullet). One workgroup per row: each thread holds up to MAXCH
@@ -16,6 +18,7 @@
 // rounding to the storage dtype.
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "moe_parts.h"
 
 namespace {
 
@@ -74,12 +77,13 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const T* __restrict__ x,
   }
 }
 
-template <typename T, bool GATHER, int NCH>
+// MODE: 0 acc only, 1 acc + the gathered y_perm rows, 2 the partial planes
+template <typename T, int MODE, int NCH>
 __global__ void __launch_bounds__(256) combine_norm_kernel(
-    const float* __restrict__ acc, const T* __restrict__ y_perm,
+    const float* __restrict__ acc, const T* __restrict__ y_perm, PartsSrc parts,
     const int32_t* __restrict__ row_pos, const float* __restrict__ topk_w,
     const float* __restrict__ w, float off, float eps, float inv_h, const T* residual, T* out,
-    int H, int k) {
+    int T_, int H, int k) {
   __shared__ float red[MAXWAVES];
   const size_t t = blockIdx.x;
   const size_t row = t * H;
@@ -89,8 +93,9 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(
   for (int ch = 0; ch < NCH; ++ch) {
     const int c = (ch * blockDim.x + threadIdx.x) * VEC8;
     if (c < H) {
-      Vec8<float>::load(acc + row + c, v[ch]);
-      if (GATHER) {
+      if (MODE == 2) parts_value(parts, topk_w, t, c, T_, H, k, v[ch]);
+      else Vec8<float>::load(acc + row + c, v[ch]);
+      if (MODE == 1) {
         for (int j0 = 0; j0 < k; j0 += KGROUP) {
           const int m = min(KGROUP, k - j0);
           int p[KGROUP];
@@ -149,20 +154,25 @@ void rmsnorm_go(const void* x, const float* w, float off, float eps, void* y, in
                      H);
 }
 
+// parts.p != NULL: the partial planes (acc and y_perm unused)
 template <typename T, int NCH>
-void combine_norm_go(const float* acc, const void* y_perm, const int32_t* row_pos,
-                     const float* topk_w, const float* w, float off, float eps,
-                     const void* residual, void* out, int T_, int H, int k, int nt,
+void combine_norm_go(const float* acc, const void* y_perm, const PartsSrc& parts,
+                     const int32_t* row_pos, const float* topk_w, const float* w, float off,
+                     float eps, const void* residual, void* out, int T_, int H, int k, int nt,
                      hipStream_t st) {
-  if (y_perm)
-    hipLaunchKernelGGL((combine_norm_kernel<T, true, NCH>), dim3(T_), dim3(nt), 0, st, acc,
-                       static_cast<const T*>(y_perm), row_pos, topk_w, w, off, eps,
-                       1.0f / (float)H, static_cast<const T*>(residual), static_cast<T*>(out), H,
-                       k);
+  const T* yp = static_cast<const T*>(y_perm);
+  const T* res = static_cast<const T*>(residual);
+  T* o = static_cast<T*>(out);
+  const float inv_h = 1.0f / (float)H;
+  if (parts.p)
+    hipLaunchKernelGGL((combine_norm_kernel<T, 2, NCH>), dim3(T_), dim3(nt), 0, st, acc, yp,
+                       parts, row_pos, topk_w, w, off, eps, inv_h, res, o, T_, H, k);
+  else if (y_perm)
+    hipLaunchKernelGGL((combine_norm_kernel<T, 1, NCH>), dim3(T_), dim3(nt), 0, st, acc, yp,
+                       parts, row_pos, topk_w, w, off, eps, inv_h, res, o, T_, H, k);
   else
-    hipLaunchKernelGGL((combine_norm_kernel<T, false, NCH>), dim3(T_), dim3(nt), 0, st, acc,
-                       (const T*)nullptr, row_pos, topk_w, w, off, eps, 1.0f / (float)H,
-                       static_cast<const T*>(residual), static_cast<T*>(out), H, k);
+    hipLaunchKernelGGL((combine_norm_kernel<T, 0, NCH>), dim3(T_), dim3(nt), 0, st, acc, yp,
+                       parts, row_pos, topk_w, w, off, eps, inv_h, res, o, T_, H, k);
 }
 
 template <typename T>
@@ -177,15 +187,15 @@ void rmsnorm_dispatch(int nch, const void* x, const float* w, float off, float e
 }
 
 template <typename T>
-void combine_norm_dispatch(int nch, const float* acc, const void* y_perm, const int32_t* row_pos,
-                           const float* topk_w, const float* w, float off, float eps,
-                           const void* residual, void* out, int T_, int H, int k, int nt,
-                           hipStream_t st) {
+void combine_norm_dispatch(int nch, const float* acc, const void* y_perm, const PartsSrc& parts,
+                           const int32_t* row_pos, const float* topk_w, const float* w,
+                           float off, float eps, const void* residual, void* out, int T_, int H,
+                           int k, int nt, hipStream_t st) {
   switch (nch) {
-    case 1: combine_norm_go<T, 1>(acc, y_perm, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
-    case 2: combine_norm_go<T, 2>(acc, y_perm, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
-    case 3: combine_norm_go<T, 3>(acc, y_perm, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
-    default: combine_norm_go<T, 4>(acc, y_perm, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
+    case 1: combine_norm_go<T, 1>(acc, y_perm, parts, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
+    case 2: combine_norm_go<T, 2>(acc, y_perm, parts, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
+    case 3: combine_norm_go<T, 3>(acc, y_perm, parts, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
+    default: combine_norm_go<T, 4>(acc, y_perm, parts, row_pos, topk_w, w, off, eps, residual, out, T_, H, k, nt, st); break;
   }
 }
 
@@ -206,19 +216,35 @@ hipError_t launch_rmsnorm(const void* x, const float* w, int add_one, float eps,
   return hipGetLastError();
 }
 
-hipError_t launch_combine_norm(const float* acc, const void* y_perm, const int32_t* row_pos,
-                               const float* topk_w, const float* w, int add_one, float eps,
-                               const void* residual, void* out, int T, int H, int k, int dtype,
-                               hipStream_t st) {
+static hipError_t combine_norm_any(const float* acc, const void* y_perm, const PartsSrc& parts,
+                                   const int32_t* row_pos, const float* topk_w, const float* w,
+                                   int add_one, float eps, const void* residual, void* out, int T,
+                                   int H, int k, int dtype, hipStream_t st) {
   if (!norm_fits(H) || T <= 0) return hipErrorInvalidValue;
   int nt, nch;
   row_shape(H, &nt, &nch);
   const float off = add_one ? 1.0f : 0.0f;
   if (dtype == MOE_BF16)
-    combine_norm_dispatch<bf16_t>(nch, acc, y_perm, row_pos, topk_w, w, off, eps, residual, out,
-                                  T, H, k, nt, st);
+    combine_norm_dispatch<bf16_t>(nch, acc, y_perm, parts, row_pos, topk_w, w, off, eps,
+                                  residual, out, T, H, k, nt, st);
   else
-    combine_norm_dispatch<float>(nch, acc, y_perm, row_pos, topk_w, w, off, eps, residual, out,
-                                 T, H, k, nt, st);
+    combine_norm_dispatch<float>(nch, acc, y_perm, parts, row_pos, topk_w, w, off, eps, residual,
+                                 out, T, H, k, nt, st);
   return hipGetLastError();
+}
+
+hipError_t launch_combine_norm(const float* acc, const void* y_perm, const int32_t* row_pos,
+                               const float* topk_w, const float* w, int add_one, float eps,
+                               const void* residual, void* out, int T, int H, int k, int dtype,
+                               hipStream_t st) {
+  return combine_norm_any(acc, y_perm, PartsSrc{nullptr, 0, 0, 0}, row_pos, topk_w, w, add_one,
+                          eps, residual, out, T, H, k, dtype, st);
+}
+
+hipError_t launch_combine_norm_parts(const PartsSrc& parts, const float* topk_w, const float* w,
+                                     int add_one, float eps, const void* residual, void* out,
+                                     int T, int H, int k, int dtype, hipStream_t st) {
+  if (!parts.p) return hipErrorInvalidValue;
+  return combine_norm_any(nullptr, nullptr, parts, nullptr, topk_w, w, add_one, eps, residual,
+                          out, T, H, k, dtype, st);
 }
