@@ -71,8 +71,13 @@ def algorithmic(cfg: dict, T: int, idx: np.ndarray | None):
     gate_up_flops = 4 * T * H * (k * I + S * Is)
     gate_up_bytes = touched * 2 * H * I * bw + S * 2 * H * Is * bw + T * H * bx \
         + (T * k * I + T * S * Is) * bx
+    # the fused decode FFN: every weight of the touched and shared experts, x,
+    # and its fp32 partial planes (one per 128-column slice of I and I_s)
+    ffn_flops = 6 * T * H * (k * I + S * Is)
+    ffn_bytes = touched * 3 * H * I * bw + S * 3 * H * Is * bw + T * H * bx \
+        + 4 * H * (I // 128 * T * k + S * Is // 128 * T)
     return dict(flops=flops, bytes=bytes_, touched=touched, gate_up_flops=gate_up_flops,
-                gate_up_bytes=gate_up_bytes)
+                gate_up_bytes=gate_up_bytes, ffn_flops=ffn_flops, ffn_bytes=ffn_bytes)
 
 
 GEMM_SOURCES = ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_decode.hip", "moe_gemm_common.h",
@@ -234,7 +239,7 @@ def summarize_traffic(d: str, kernel: str | None = None) -> str:
         raise SystemExit(f"no copy kernel in the calibration run: {sorted(cal_f)}")
     f_scale = copy_bytes / (cal_f[ck[0]] * 1024)
     w_scale = copy_bytes / (cal_w[ck[0]] * 1024)
-    alg = line["layer"]["gate_up_bytes"]
+    alg = line["roofline"].get("algorithmic_bytes", line["layer"]["gate_up_bytes"])
     hbm = fetch[kernel] * 1024 * f_scale + write[kernel] * 1024 * w_scale
     wl = line["config"]["workload"]
     rec = {"kernel": kernel, "workload": wl, "source_sha256": gemm_source_sha(),
@@ -384,13 +389,22 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     dev = t["x"].device
     ws = moe.alloc_block_workspace(keys, T)
     f32, i32 = torch.float32, torch.int32
+    # where the layer takes the fused decode FFN, the stage-call pass calls its
+    # entry points (moe_expert_ffn, moe_combine_partials) instead of the
+    # grouping and the two grouped GEMMs
+    parts_bytes = moe.moe_expert_ffn_size(keys, T)
+    fused = (parts_bytes is not None and os.environ.get("MOE_DECODE_FFN") != "0"
+             and os.environ.get("MOE_GEMM_TILE") != "128")
     st = dict(
         logits=torch.empty(T * E, dtype=f32, device=dev),
         idx=torch.empty(T * k, dtype=i32, device=dev),
         w=torch.empty(T * k, dtype=f32, device=dev),
-        offs=torch.empty(E + 1, dtype=i32, device=dev),
-        sr=torch.empty(T * k, dtype=i32, device=dev),
-        rp=torch.empty(T * k, dtype=i32, device=dev),
+        # grouping outputs start as zeros: the fused stage pass never writes
+        # them, and the block's combine timings still gather through row_pos
+        offs=torch.zeros(E + 1, dtype=i32, device=dev),
+        sr=torch.zeros(T * k, dtype=i32, device=dev),
+        rp=torch.zeros(T * k, dtype=i32, device=dev),
+        parts=torch.empty(max(parts_bytes or 0, 4) // 4, dtype=f32, device=dev),
         h=torch.empty(T * k * I, dtype=dt, device=dev),
         hs=torch.empty(T * S * Is, dtype=dt, device=dev) if S else None,
         acc=torch.empty(T * H, dtype=f32, device=dev),
@@ -398,9 +412,26 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
         yp=torch.empty(T * k * H, dtype=dt, device=dev) if ordered else None,
         ws=ws)
     x, mx = t["x"], t["mx"]
-    stages = ["router", "route", "permute", "gate_up", "down", "combine"]
+    stages = (["router", "route", "ffn", "combine"] if fused else
+              ["router", "route", "permute", "gate_up", "down", "combine"])
+
+    def fused_step(events=None):
+        s = torch.cuda.current_stream()
+        rec = (lambda i: events[i].record(s)) if events else (lambda i: None)
+        rec(0)
+        moe.moe_router_logits(keys, T, x, t["wr"], st["logits"], ws, s, mx=mx)
+        rec(1)
+        moe.moe_route(keys, T, st["logits"], t["b"], st["idx"], st["w"], None, s)
+        rec(2)
+        moe.moe_expert_ffn(keys, T, x, t["wg"], t["wu"], t["wd"], t["sg"], t["su"], t["sd"],
+                           st["idx"], st["parts"], s)
+        rec(3)
+        moe.moe_combine_partials(keys, T, st["parts"], st["w"], st["out"], s)
+        rec(4)
 
     def step(events=None):
+        if fused:
+            return fused_step(events)
         s = torch.cuda.current_stream()
         rec = (lambda i: events[i].record(s)) if events else (lambda i: None)
         rec(0)
@@ -438,7 +469,9 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     per_stage = {s: [sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(steps)]
                  for j, s in enumerate(stages)}
     stage_ms = {s: float(np.median(v)) for s, v in per_stage.items()}
-    gate_up_mean = float(np.mean(per_stage["gate_up"]))
+    # the roofline kernel's stage: the fused FFN, else the grouped gate/up
+    roof_stage = "ffn" if fused else "gate_up"
+    roof_mean = float(np.mean(per_stage[roof_stage]))
 
     # the timed steps: flush (outside the events), then the layer call alone;
     # everything is queued on one stream and synchronised once, so the flush
@@ -496,7 +529,7 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
     return dict(ms=float(np.median(per_call)), ms_min=float(np.min(per_call)),
                 ms_max=float(np.max(per_call)), wall_s=wall, ms_warm=ms_warm,
                 ms_write_flush=ms_write_flush, ms_graph=ms_graph,
-                stage_ms=stage_ms, gate_up_mean_ms=gate_up_mean, st=st, keys=keys,
+                stage_ms=stage_ms, roof_mean_ms=roof_mean, roof_stage=roof_stage, st=st, keys=keys,
                 stream=stream)
 
 
@@ -517,10 +550,13 @@ def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
     # prefill-sized batches are priced against the MFMA peak, decode-sized
     # ones (at most 32 rows per expert on average) against HBM
     decode = T * k <= 32 * E
-    gu_ms = m["gate_up_mean_ms"]
-    kname = gate_up_kernel(cfg, T)
-    gu_tf = alg["gate_up_flops"] / (gu_ms * 1e-3) / 1e12
-    gu_gb = alg["gate_up_bytes"] / (gu_ms * 1e-3) / 1e9
+    gu_ms = m["roof_mean_ms"]
+    fused = m["roof_stage"] == "ffn"
+    kname = "moe_ffn_decode_kernel" if fused else gate_up_kernel(cfg, T)
+    k_flops = alg["ffn_flops"] if fused else alg["gate_up_flops"]
+    k_bytes = alg["ffn_bytes"] if fused else alg["gate_up_bytes"]
+    gu_tf = k_flops / (gu_ms * 1e-3) / 1e12
+    gu_gb = k_bytes / (gu_ms * 1e-3) / 1e9
     if decode:
         roof = {"bound": "hbm", "achieved": gu_gb, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
@@ -528,6 +564,8 @@ def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_profile(kname, name, gemm_source_sha())
     roof["kernel"] = kname
+    roof["algorithmic_bytes"] = k_bytes
+    roof["algorithmic_flops"] = k_flops
     roof["ms_per_launch"] = gu_ms
     roof["launches_timed"] = steps
     roof["frac_other_roof"] = (gu_gb / PEAK_HBM_GBS) if not decode else (gu_tf / peak_mm)
@@ -535,6 +573,7 @@ def layer_report(name, cfg, T, m, idx_h, logits_h, bias, steps):
              "frac_hbm_peak": gbs / PEAK_HBM_GBS, "flops": alg["flops"], "bytes": alg["bytes"],
              "arith_intensity": alg["flops"] / alg["bytes"],
              "gate_up_flops": alg["gate_up_flops"], "gate_up_bytes": alg["gate_up_bytes"],
+             "ffn_flops": alg["ffn_flops"], "ffn_bytes": alg["ffn_bytes"],
              "bound": "hbm" if decode else "mfma", "touched_experts": alg["touched"],
              "stage_ms": m["stage_ms"], "ms_median": ms, "ms_min": m["ms_min"],
              "ms_max": m["ms_max"], "ms_per_step_warm": m["ms_warm"],

@@ -26,6 +26,7 @@ MOE_ROUTER_F32, MOE_ROUTER_MXFP8 = 0, 1
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
     "moe_grouped_gate_up_swiglu", "moe_grouped_down", "moe_combine",
+    "moe_expert_ffn_size", "moe_expert_ffn", "moe_combine_partials",
     "moe_layer_forward", "moe_rms_norm", "moe_combine_norm_residual",
     "moe_block_workspace_size", "moe_block_forward", "moe_status_string",
     "moe_build_info",
@@ -164,6 +165,9 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_gate_up_swiglu": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
             "moe_grouped_down": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
             "moe_combine": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
+            "moe_expert_ffn_size": [cp, i64, ctypes.POINTER(sz)],
+            "moe_expert_ffn": [cp, i64] + [_vp] * 9 + [_vp],
+            "moe_combine_partials": [cp, i64, _vp, _vp, _vp, _vp],
             "moe_layer_forward": [cp, i64] + [_vp] * 15 + [i32, _vp, sz, _vp],
             "moe_rms_norm": [cp, ncp, i64, _vp, _vp, _vp, _vp],
             "moe_combine_norm_residual": [cp, ncp, i64] + [_vp] * 7 + [_vp],
@@ -301,6 +305,36 @@ def moe_combine(cfg, T, acc, y_perm, row_pos, topk_w, out, stream=None):
     _need(out, T * c.hidden_size, "out")
     _call("moe_combine", ctypes.byref(c), int(T), _p(acc), _p(y_perm), _p(row_pos), _p(topk_w),
           _p(out), _stream(stream))
+
+
+def moe_expert_ffn_size(cfg, T: int):
+    """Bytes of the fused FFN's partial planes, or None where it does not
+    apply (MOE_ERR_UNSUPPORTED)."""
+    c = make_config(cfg)
+    n = ctypes.c_size_t(0)
+    st = lib().moe_expert_ffn_size(ctypes.byref(c), int(T), ctypes.byref(n))
+    if st == MOE_ERR_UNSUPPORTED:
+        return None
+    if st != MOE_OK:
+        raise MoeError(st, "moe_expert_ffn_size")
+    return n.value
+
+
+def moe_expert_ffn(cfg, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_idx, parts,
+                   stream=None):
+    c = make_config(cfg)
+    need = moe_expert_ffn_size(cfg, T)
+    if need is not None:
+        _need(parts, need // 4, "parts")
+    _call("moe_expert_ffn", ctypes.byref(c), int(T), _p(x), _p(w_gate), _p(w_up), _p(w_down),
+          _p(ws_gate), _p(ws_up), _p(ws_down), _p(topk_idx), _p(parts), _stream(stream))
+
+
+def moe_combine_partials(cfg, T, parts, topk_w, out, stream=None):
+    c = make_config(cfg)
+    _need(out, T * c.hidden_size, "out")
+    _call("moe_combine_partials", ctypes.byref(c), int(T), _p(parts), _p(topk_w), _p(out),
+          _stream(stream))
 
 
 def moe_layer_forward(cfg, T, x, w_router, expert_bias, w_gate, w_up, w_down, ws_gate, ws_up,

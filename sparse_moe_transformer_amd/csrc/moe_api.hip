@@ -113,9 +113,14 @@ bool ffn_shape(const Dims& d) {
   return d.dtype == MOE_BF16 && d.wfmt == WF_DTYPE && ffn_decode_fits(d.H, d.I, d.E, d.S, d.Is);
 }
 
+// the batch and the launch fit too (T = 0 aside)
+bool ffn_supported(const Dims& d) {
+  return ffn_shape(d) && d.T <= 32 && d.T * d.k <= 256 &&
+         ffn_decode_schedulable(d.E, d.I, d.S, d.Is);
+}
+
 bool use_ffn(const Dims& d) {
-  if (!ffn_shape(d) || d.T > 32 || d.T * d.k > 256) return false;
-  if (!ffn_decode_schedulable(d.E, d.I, d.S, d.Is)) return false;
+  if (!ffn_supported(d)) return false;
   if (const char* e = std::getenv("MOE_DECODE_FFN"))
     if (std::strcmp(e, "0") == 0) return false;
   if (const char* e = std::getenv("MOE_GEMM_TILE"))
@@ -126,12 +131,16 @@ bool use_ffn(const Dims& d) {
 // Partial planes for min(T, 32) tokens whenever the shapes allow the fused
 // path (whatever the batch and the knobs), so a workspace sized for T tokens
 // serves every smaller batch too.
+size_t ffn_planes_bytes(const Dims& d, int64_t T) {
+  const size_t slice = (size_t)ffn_decode_slice();
+  const size_t planes_rows =
+      (size_t)d.I / slice * (size_t)T * d.k + (size_t)d.S * d.Is / slice * (size_t)T;
+  return planes_rows * d.H * 4;
+}
+
 size_t ffn_parts_bytes(const Dims& d) {
   if (!ffn_shape(d)) return 0;
-  const size_t T = (size_t)std::min<int64_t>(d.T, 32);
-  const size_t slice = (size_t)ffn_decode_slice();
-  const size_t planes_rows = (size_t)d.I / slice * T * d.k + (size_t)d.S * d.Is / slice * T;
-  return planes_rows * d.H * 4;
+  return ffn_planes_bytes(d, std::min<int64_t>(d.T, 32));
 }
 
 Ws carve(const Dims& d, void* base) {
@@ -610,6 +619,43 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc, const
   if (y_perm && (!row_pos || !topk_w)) return MOE_ERR_INVALID_ARG;
   return hip_ok(launch_combine(acc, y_perm, row_pos, topk_w, out, (int)T, d.H, d.k, d.dtype,
                                (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims d;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (!ffn_supported(d)) return MOE_ERR_UNSUPPORTED;
+  *bytes = ffn_planes_bytes(d, T);
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
+                          const void* w_up, const void* w_down, const void* ws_gate,
+                          const void* ws_up, const void* ws_down, const int32_t* topk_idx,
+                          float* parts, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (!ffn_supported(d)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !topk_idx || !parts) return MOE_ERR_INVALID_ARG;
+  if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  PartsSrc src;
+  return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_idx, parts,
+                (hipStream_t)stream, &src);
+}
+
+moe_status moe_combine_partials(const moe_config* cfg, int64_t T, const float* parts,
+                                const float* topk_w, void* out, moe_stream_t stream) {
+  Dims d;
+  MOE_TRY(check_cfg(cfg, T, &d));
+  if (!ffn_supported(d)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!parts || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  const int slice = ffn_decode_slice();
+  const PartsSrc src{parts, d.I / slice, d.S ? d.S * d.Is / slice : 0, (int)(T * d.k)};
+  return hip_ok(launch_combine_parts(src, topk_w, out, (int)T, d.H, d.k, d.dtype,
+                                     (hipStream_t)stream));
 }
 
 moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,

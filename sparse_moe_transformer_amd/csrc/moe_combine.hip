@@ -5,7 +5,9 @@
 //                   summed in j order, so the result does not depend on timing.
 // Each thread handles 8 consecutive columns of one token (H % 64 == 0). The
 // k gathered rows are fetched in groups of 8 slots whose loads are all in
-// flight together; the sum still runs slot by slot in j order.
+// flight together (unconditional loads: a predicated load makes the compiler
+// wait for each before the next); the sum still runs slot by slot in j
+// order.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "moe_parts.h"
@@ -31,24 +33,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     Vec8<float>::load(acc + t * H + c, v);
     if (GATHER) {
       for (int j0 = 0; j0 < k; j0 += KGROUP) {
+        // slots past k re-read the last slot's row and are masked by a
+        // select: every load is unconditional, so all are in flight at once
         const int m = min(KGROUP, k - j0);
         int p[KGROUP];
         float w[KGROUP];
 #pragma unroll
         for (int j = 0; j < KGROUP; ++j) {
-          p[j] = j < m ? row_pos[t * k + j0 + j] : 0;
-          w[j] = j < m ? topk_w[t * k + j0 + j] : 0.f;
+          const size_t r = t * k + j0 + min(j, m - 1);
+          p[j] = row_pos[r];
+          w[j] = topk_w[r];
         }
         float y[KGROUP][CW];
 #pragma unroll
-        for (int j = 0; j < KGROUP; ++j)
-          if (j < m) Vec8<T>::load(y_perm + (size_t)p[j] * H + c, y[j]);
+        for (int j = 0; j < KGROUP; ++j) Vec8<T>::load(y_perm + (size_t)p[j] * H + c, y[j]);
 #pragma unroll
         for (int j = 0; j < KGROUP; ++j)
-          if (j < m) {
 #pragma unroll
-            for (int u = 0; u < CW; ++u) v[u] += w[j] * y[j][u];
-          }
+          for (int u = 0; u < CW; ++u) v[u] = j < m ? v[u] + w[j] * y[j][u] : v[u];
       }
     }
     Vec8<T>::store(out + t * H + c, v);

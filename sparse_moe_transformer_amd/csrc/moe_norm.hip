@@ -97,24 +97,24 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(
       else Vec8<float>::load(acc + row + c, v[ch]);
       if (MODE == 1) {
         for (int j0 = 0; j0 < k; j0 += KGROUP) {
+          // unconditional loads (slots past k re-read the last row, masked
+          // by a select), so all of a group's loads are in flight at once
           const int m = min(KGROUP, k - j0);
           int p[KGROUP];
           float wj[KGROUP];
 #pragma unroll
           for (int j = 0; j < KGROUP; ++j) {
-            p[j] = j < m ? row_pos[t * k + j0 + j] : 0;
-            wj[j] = j < m ? topk_w[t * k + j0 + j] : 0.f;
+            const size_t r = t * k + j0 + min(j, m - 1);
+            p[j] = row_pos[r];
+            wj[j] = topk_w[r];
           }
           float yv[KGROUP][VEC8];
 #pragma unroll
-          for (int j = 0; j < KGROUP; ++j)
-            if (j < m) Vec8<T>::load(y_perm + (size_t)p[j] * H + c, yv[j]);
+          for (int j = 0; j < KGROUP; ++j) Vec8<T>::load(y_perm + (size_t)p[j] * H + c, yv[j]);
 #pragma unroll
           for (int j = 0; j < KGROUP; ++j)
-            if (j < m) {
 #pragma unroll
-              for (int u = 0; u < VEC8; ++u) v[ch][u] += wj[j] * yv[j][u];
-            }
+            for (int u = 0; u < VEC8; ++u) v[ch][u] = j < m ? v[ch][u] + wj[j] * yv[j][u] : v[ch][u];
         }
       }
 #pragma unroll

@@ -12,50 +12,61 @@
 
 namespace {
 
-constexpr int PARTS_KGROUP = 8;  // gathered rows in flight per plane
+constexpr int PARTS_KGROUP = 8;  // routed slots per group of loads
 
+// Every load below is unconditional (slots past k and planes past the count
+// re-read a valid row and are then masked by a select), so all of a group's
+// loads are in flight at once; predicated loads leave the compiler waiting
+// for each one before the next.
 __device__ __forceinline__ void parts_value(const PartsSrc& s, const float* __restrict__ topk_w,
                                             size_t t, int c, int T, int H, int k,
                                             float (&v)[VEC8]) {
   const float* sh = s.p + (size_t)s.nr * s.rows * H;
 #pragma unroll
   for (int u = 0; u < VEC8; ++u) v[u] = 0.f;
-  if (s.ns > 0) Vec8<float>::load(sh + t * H + c, v);
-  for (int a = 1; a < s.ns; ++a) {
-    float z[VEC8];
-    Vec8<float>::load(sh + ((size_t)a * T + t) * H + c, z);
+  // shared planes, two at a time, added in plane order
+  for (int a0 = 0; a0 < s.ns; a0 += 2) {
+    float z0[VEC8], z1[VEC8];
+    const bool two = a0 + 1 < s.ns;
+    Vec8<float>::load(sh + ((size_t)a0 * T + t) * H + c, z0);
+    Vec8<float>::load(sh + ((size_t)(two ? a0 + 1 : a0) * T + t) * H + c, z1);
 #pragma unroll
-    for (int u = 0; u < VEC8; ++u) v[u] += z[u];
+    for (int u = 0; u < VEC8; ++u) {
+      v[u] += z0[u];
+      v[u] = two ? v[u] + z1[u] : v[u];
+    }
   }
   for (int j0 = 0; j0 < k; j0 += PARTS_KGROUP) {
     const int m = min(PARTS_KGROUP, k - j0);
     const size_t p0 = t * k + j0;  // this group's routed rows p0 .. p0 + m - 1
     float w[PARTS_KGROUP];
 #pragma unroll
-    for (int j = 0; j < PARTS_KGROUP; ++j) w[j] = j < m ? topk_w[p0 + j] : 0.f;
+    for (int j = 0; j < PARTS_KGROUP; ++j) w[j] = topk_w[p0 + min(j, m - 1)];
+    // y[j] = the row's planes summed in plane order, two planes per round
     float y[PARTS_KGROUP][VEC8];
+    for (int c0 = 0; c0 < s.nr; c0 += 2) {
+      const bool two = c0 + 1 < s.nr;
+      const float* pl0 = s.p + (size_t)c0 * s.rows * H;
+      const float* pl1 = s.p + (size_t)(two ? c0 + 1 : c0) * s.rows * H;
+      float z0[PARTS_KGROUP][VEC8], z1[PARTS_KGROUP][VEC8];
 #pragma unroll
-    for (int j = 0; j < PARTS_KGROUP; ++j)
-      if (j < m) Vec8<float>::load(s.p + (p0 + j) * H + c, y[j]);
-    for (int a = 1; a < s.nr; ++a) {
-      const float* pl = s.p + (size_t)a * s.rows * H;
-      float z[PARTS_KGROUP][VEC8];
+      for (int j = 0; j < PARTS_KGROUP; ++j) {
+        const size_t row = p0 + min(j, m - 1);
+        Vec8<float>::load(pl0 + row * H + c, z0[j]);
+        Vec8<float>::load(pl1 + row * H + c, z1[j]);
+      }
 #pragma unroll
       for (int j = 0; j < PARTS_KGROUP; ++j)
-        if (j < m) Vec8<float>::load(pl + (p0 + j) * H + c, z[j]);
 #pragma unroll
-      for (int j = 0; j < PARTS_KGROUP; ++j)
-        if (j < m) {
-#pragma unroll
-          for (int u = 0; u < VEC8; ++u) y[j][u] += z[j][u];
+        for (int u = 0; u < VEC8; ++u) {
+          const float a = c0 == 0 ? z0[j][u] : y[j][u] + z0[j][u];
+          y[j][u] = two ? a + z1[j][u] : a;
         }
     }
 #pragma unroll
     for (int j = 0; j < PARTS_KGROUP; ++j)
-      if (j < m) {
 #pragma unroll
-        for (int u = 0; u < VEC8; ++u) v[u] += w[j] * y[j][u];
-      }
+      for (int u = 0; u < VEC8; ++u) v[u] = j < m ? v[u] + w[j] * y[j][u] : v[u];
   }
 }
 

@@ -185,3 +185,51 @@ def test_group_routing_accepted():
     assert moe.moe_workspace_size(_cfg(n_group=8, topk_group=3), 16) > 0
     assert moe.moe_workspace_size(_cfg(n_group=1, topk_group=0), 16) > 0   # off
 
+
+
+def _tri(**kw):
+    c = synth.layer_keys(synth.config("trinity_nano_decode_T32"))
+    c.update(kw)
+    return c
+
+
+def test_expert_ffn_applies_where_documented():
+    """moe_expert_ffn_size: the partial planes' bytes where the fused decode
+    FFN applies (bf16 weights, H 512 or 1024, widths in 128-column slices,
+    E <= 256, T <= 32 and T*k <= 256), MOE_ERR_UNSUPPORTED (None) elsewhere."""
+    H, I, k = 1024, 256, 8
+    for T in (0, 1, 7, 32):
+        assert moe.moe_expert_ffn_size(_tri(), T) == (I // 128 * T * k + 256 // 128 * T) * H * 4
+    assert moe.moe_expert_ffn_size(_tri(hidden_size=512, num_shared_experts=0), 5) == \
+        I // 128 * 5 * k * 512 * 4
+    for bad, T in [({}, 33), ({"num_experts_per_tok": 9}, 32), ({"hidden_size": 768}, 8),
+                   ({"hidden_size": 2048}, 8), ({"moe_intermediate_size": 192}, 8),
+                   ({"shared_intermediate_size": 320}, 8), ({"num_experts": 300}, 8),
+                   ({"dtype": "f32"}, 8), ({"weight_format": "mxfp4"}, 8)]:
+        assert moe.moe_expert_ffn_size(_tri(**bad), T) is None, bad
+
+
+def test_expert_ffn_host_checks():
+    """Null arguments and unsupported shapes are refused before any launch."""
+    L = moe.lib()
+    p = 0x1000
+    c = moe.make_config(_tri())
+    ffn = lambda T, parts=p, idx=p, cc=c: L.moe_expert_ffn(ctypes.byref(cc), T, p, p, p, p, p, p, p,
+                                                          idx, parts, None)
+    assert ffn(0) == moe.MOE_OK
+    assert ffn(8, parts=None) == moe.MOE_ERR_INVALID_ARG
+    assert ffn(8, idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert ffn(33) == moe.MOE_ERR_UNSUPPORTED
+    assert ffn(8, cc=moe.make_config(_tri(hidden_size=768))) == moe.MOE_ERR_UNSUPPORTED
+    comb = lambda T, parts=p: L.moe_combine_partials(ctypes.byref(c), T, parts, p, p, None)
+    assert comb(0) == moe.MOE_OK
+    assert comb(8, parts=None) == moe.MOE_ERR_INVALID_ARG
+    assert comb(40) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_covers_smaller_batches_with_the_fused_ffn():
+    """The layer's workspace reserves the fused FFN's planes for min(T, 32)
+    tokens, so a workspace sized for T tokens serves every smaller batch."""
+    c = _tri()
+    sizes = [moe.moe_workspace_size(c, t) for t in (1, 8, 31, 32, 33, 64, 8192)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))

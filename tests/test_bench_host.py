@@ -114,7 +114,7 @@ def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
     kernel's mean time."""
     from workloads import synth
     m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, ms_write_flush=2.5, ms_graph=None,
-             gate_up_mean_ms=1.0, stage_ms={"gate_up": 1.0})
+             roof_mean_ms=1.0, roof_stage="gate_up", stage_ms={"gate_up": 1.0})
     for name, bound in (("minimax_m3_prefill_T8192", "mfma"), ("minimax_m3_decode_T64", "hbm"),
                         ("trinity_nano_decode_T32", "hbm")):
         cfg = synth.config(name)
@@ -133,6 +133,27 @@ def test_layer_report_prices_prefill_on_mfma_and_decode_on_hbm():
         assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"])
         assert layer["frac_hbm_peak"] == pytest.approx(alg["bytes"] / 2e-3 / 1e9 / 8000.0)
         assert layer["frac_bf16_peak"] == pytest.approx(alg["flops"] / 2e-3 / 1e12 / 2516.6)
+
+
+def test_fused_ffn_roofline():
+    """Where the stage-call pass ran the fused decode FFN, the roofline object
+    is that kernel against HBM, over every touched and shared expert weight,
+    x and the fp32 partial planes."""
+    from workloads import synth
+    cfg = synth.config("trinity_nano_decode_T32")
+    T, E, k, H = cfg["T"], cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"]
+    I, Is = cfg["moe_intermediate_size"], cfg["shared_intermediate_size"]
+    idx = (np.arange(T * k).reshape(T, k) % E).astype(np.int64)
+    m = dict(ms=2.0, ms_min=1.9, ms_max=2.2, ms_warm=1.8, ms_write_flush=2.5, ms_graph=None,
+             roof_mean_ms=0.5, roof_stage="ffn", stage_ms={"ffn": 0.5})
+    layer, roof = bench.layer_report("trinity_nano_decode_T32", cfg, T, m, idx,
+                                     np.zeros((T, E), np.float32), np.zeros(E, np.float32), 5)
+    touched = len(np.unique(idx))
+    want = (touched * 3 * H * I * 2 + 3 * H * Is * 2 + T * H * 2
+            + 4 * H * (I // 128 * T * k + Is // 128 * T))
+    assert roof["kernel"] == "moe_ffn_decode_kernel" and roof["bound"] == "hbm"
+    assert roof["algorithmic_bytes"] == want
+    assert roof["achieved"] == pytest.approx(want / 0.5e-3 / 1e9)
 
 
 def test_gate_up_kernel_names_follow_the_library_selection():

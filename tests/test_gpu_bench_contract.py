@@ -60,7 +60,10 @@ def test_bench_json_line():
         assert d["tokens_per_s"] == pytest.approx(T / (d["ms_per_step"] * 1e-3), rel=1e-6)
         assert 0 < d["layer"]["frac_hbm_peak"] < 1.0
         _check_roofline(d["roofline"], "hbm")
-        assert d["roofline"]["kernel"] == "moe_gate_up_decode_kernel"
+        # the Trinity-like layer takes the fused decode FFN
+        want = "moe_ffn_decode_kernel" if name == "trinity_nano_decode_T32" else \
+            "moe_gate_up_decode_kernel"
+        assert d["roofline"]["kernel"] == want
     cb = L["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == "tokens/s"
     print(f"[bench-contract] {L['value']:.4g} tokens/s, roofline frac {L['roofline']['frac']:.3f}, "

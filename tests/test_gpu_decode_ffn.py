@@ -163,3 +163,61 @@ def test_fused_ffn_inside_the_block(monkeypatch):
     check_block(cfg, inp, nw, split)
     assert not np.array_equal(split["out"], res["out"]), "the fused kernel did not run"
     say(f"[ffn] block worst err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("name", ["trinity_nano_decode_T32", "two_shared_four_slices",
+                                  "packed_clamp_h512"])
+def test_ffn_entry_points(name, monkeypatch):
+    """moe_expert_ffn and moe_combine_partials called on their own: every
+    partial plane against the oracle's expert FFN restricted to that slice of
+    the intermediate width (routed rows and shared rows), and the combined
+    output bitwise equal to the layer's."""
+    monkeypatch.delenv("MOE_DECODE_FFN", raising=False)
+    inp = generated(name) if name in synth.CONFIGS else synth.generate(FFN[name])
+    cfg, c = inp.cfg, synth.layer_keys(inp.cfg)
+    dev = Dev(inp)
+    layer = dev.forward(deterministic=1)
+    T, k, H = dev.T, cfg["num_experts_per_tok"], cfg["hidden_size"]
+    I, S = cfg["moe_intermediate_size"], cfg["num_shared_experts"]
+    Is = cfg["shared_intermediate_size"] or I
+    idx = torch.from_numpy(layer["idx"].astype(np.int32)).cuda().reshape(-1)
+    w = torch.from_numpy(layer["w"].astype(np.float32)).cuda().reshape(-1)
+    n = moe.moe_expert_ffn_size(c, T)
+    nr, ns = I // 128, S * Is // 128
+    assert n == (nr * T * k + ns * T) * H * 4
+    parts = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(c, T, dev.x, dev.w_gate, dev.w_up, dev.w_down, dev.ws_gate, dev.ws_up,
+                       dev.ws_down, idx, parts)
+    out = torch.empty(T * H, dtype=moe.torch_dtype(c), device="cuda")
+    moe.moe_combine_partials(c, T, parts, w, out)
+    torch.cuda.synchronize()
+    got = out.view(T, H).float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, layer["out"]), "entry points differ from the layer"
+
+    P = parts.cpu().numpy().astype(np.float64)
+    routed = P[: nr * T * k * H].reshape(nr, T * k, H)
+    shared = P[nr * T * k * H:].reshape(ns, T, H) if ns else None
+    x = O.as_f64(inp.x)
+    act = O.activation(cfg)
+    worst = 0.0
+    for cs in range(nr):
+        C = slice(128 * cs, 128 * cs + 128)
+        ref = np.zeros((T * k, H))
+        for r in range(T * k):
+            e = int(layer["idx"].reshape(-1)[r])
+            he = O.mlp_hidden(x[r // k][None], O.as_f64(inp.w_gate[e][C]), O.as_f64(inp.w_up[e][C]),
+                              act)
+            ref[r] = O.mlp_out(he, O.as_f64(inp.w_down[e][:, C]))[0]
+        e_c = rel_err(routed[cs], ref)
+        assert e_c <= TOL["bf16"], f"routed plane {cs}: {e_c:.3e}"
+        worst = max(worst, e_c)
+    sw = O._shared_weights(inp, cfg)
+    for a in range(ns):
+        s, off = divmod(128 * a, Is)
+        wg, wu, wd = sw[s]
+        C = slice(off, off + 128)
+        ref = O.mlp_out(O.mlp_hidden(x, wg[C], wu[C], act), wd[:, C])
+        e_a = rel_err(shared[a], ref)
+        assert e_a <= TOL["bf16"], f"shared plane {a}: {e_a:.3e}"
+        worst = max(worst, e_a)
+    say(f"[ffn] entry points {name}: planes worst {worst:.2e}")
