@@ -193,8 +193,39 @@ def test_deterministic_repeats_bitwise():
     assert np.array_equal(a["idx"], c["idx"]) and np.array_equal(a["w"], c["w"])
 
 
-# (E, k): E <= 256 selects by ranks, E > 256 by k rounds of wave reductions
+# (E, k): the k rounds of wave reductions (at most 64 tokens with sigmoid
+# scores and E <= 256 select by ranks instead)
 TIE_CASES = [(300, 8), (256, 8), (128, 8), (64, 6), (7, 3)]
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (200, 32), (128, 8), (129, 4), (64, 6), (33, 1),
+                                 (8, 8), (7, 3)])
+def test_route_rank_selection_equals_the_rounds(E, k, monkeypatch):
+    """The rank selection (one workgroup per token; decode-sized batches) and
+    the k arg-max rounds (one wavefront per token) forced on the same
+    logits, random and with exact ties: indices, weights and expert counts
+    bitwise equal."""
+    cfg = dict(synth.layer_keys(EDGE["e300_k8"]), num_experts=E, num_experts_per_tok=k)
+    T = 97
+    rng = np.random.default_rng(E * 31 + k)
+    Lr = rng.standard_normal((T, E)).astype(np.float32) * 3
+    Lt = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(T, E)).astype(np.float32)
+    b = (rng.uniform(-0.05, 0.05, E)).astype(np.float32)
+    for L in (Lr, Lt):
+        res = []
+        for knob in ("1", "0"):
+            monkeypatch.setenv("MOE_ROUTE_RANK", knob)
+            idx = torch.empty(T * k, dtype=torch.int32, device="cuda")
+            w = torch.empty(T * k, dtype=torch.float32, device="cuda")
+            cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+            moe.moe_route(cfg, T, torch.from_numpy(L).cuda(), torch.from_numpy(b).cuda(), idx, w,
+                          cnt)
+            torch.cuda.synchronize()
+            res.append((idx.cpu().numpy(), w.cpu().numpy(), cnt.cpu().numpy()))
+        for a, b_ in zip(res[0], res[1]):
+            assert np.array_equal(a, b_)
+        _, _, ridx, _ = O.route(L, b, k, "sigmoid", True, cfg["route_scale"])
+        assert np.array_equal(res[0][0].reshape(T, k), ridx)
 
 
 @pytest.mark.parametrize("score_func", ["sigmoid", "softmax"])
