@@ -424,7 +424,7 @@ def measure_layer(moe, cfg, t, T, steps, warmup, ordered, flush):
         moe.moe_route(keys, T, st["logits"], t["b"], st["idx"], st["w"], None, s)
         rec(2)
         moe.moe_expert_ffn(keys, T, x, t["wg"], t["wu"], t["wd"], t["sg"], t["su"], t["sd"],
-                           st["idx"], st["parts"], s)
+                           st["idx"], st["parts"], s, mx=mx)
         rec(3)
         moe.moe_combine_partials(keys, T, st["parts"], st["w"], st["out"], s)
         rec(4)

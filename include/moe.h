@@ -267,11 +267,12 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* acc,
  * adds a row's planes in slice order. moe_layer_forward and
  * moe_block_forward take this path by themselves where it applies.
  *
- * Applies to: dtype bf16 with bf16 expert weights (weight_format DTYPE),
- * hidden_size 512 or 1024, moe_intermediate_size and (S > 0) the shared
- * width multiples of 128, num_experts <= 256, T <= 32 and T*k <= 256, and
- * at most 8 slices per workgroup of the launch (one workgroup per compute
- * unit). Elsewhere the three calls return MOE_ERR_UNSUPPORTED. */
+ * Applies to: dtype bf16 with bf16, MXFP8 or MXFP4 expert weights,
+ * hidden_size 512 or 1024 (MXFP4: 1024), moe_intermediate_size and (S > 0)
+ * the shared width multiples of 128, num_experts <= 256, T <= 32 and
+ * T*k <= 256, and at most 8 slices per workgroup of the launch (one
+ * workgroup per compute unit). Elsewhere the three calls return
+ * MOE_ERR_UNSUPPORTED. */
 
 /* Bytes of the partial planes for T tokens,
  *   (I/128 * T*k + S*I_s/128 * T) * H * 4.  bytes: host pointer. */
@@ -281,17 +282,20 @@ moe_status moe_expert_ffn_size(const moe_config* cfg, int64_t T, size_t* bytes);
  *   routed plane c < I/128, row r = t*k + j (expert e = topk_idx[r]):
  *     parts_c[r, :] = bf16(act(x[t] . W_g[e, C]^T, x[t] . W_u[e, C]^T)) . W_d[e][:, C]^T
  *     with C the columns 128c .. 128c+127 (the activation rounded to bf16
- *     as the grouped path stores h);
+ *     as the grouped path stores h; MX weights as their exact values);
  *   then shared plane a < S*I_s/128, row t: the same for slice a of the
  *     shared experts' concatenated width.
  * x [T,H]; weights as for the grouped calls (ws_* NULL when packed or
- * S == 0); topk_idx [T,k]: a token's k experts distinct (as moe_route
- * emits them); rows naming an expert outside [0, E) are skipped (their
- * rows of parts are left unwritten). parts: moe_expert_ffn_size bytes. */
+ * S == 0); mx: the MX scales (gate, up, down and the shared ones) when
+ * weight_format is MXFP8 or MXFP4, else ignored; topk_idx [T,k]: a token's
+ * k experts distinct (as moe_route emits them); rows naming an expert
+ * outside [0, E) are skipped (their rows of parts are left unwritten).
+ * parts: moe_expert_ffn_size bytes. */
 moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x,
                           const void* w_gate, const void* w_up, const void* w_down,
                           const void* ws_gate, const void* ws_up, const void* ws_down,
-                          const int32_t* topk_idx, float* parts, moe_stream_t stream);
+                          const moe_mx_scales* mx, const int32_t* topk_idx, float* parts,
+                          moe_stream_t stream);
 
 /* Finalise from the partial planes:
  *   out[t] = sum_a shared_a[t] + sum_j topk_w[t,j] * (sum_c parts_c[t*k+j])

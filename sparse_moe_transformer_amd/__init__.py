@@ -166,7 +166,7 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_down": [cp, i64] + [_vp] * 10 + [_vp, sz, _vp],
             "moe_combine": [cp, i64, _vp, _vp, _vp, _vp, _vp, _vp],
             "moe_expert_ffn_size": [cp, i64, ctypes.POINTER(sz)],
-            "moe_expert_ffn": [cp, i64] + [_vp] * 9 + [_vp],
+            "moe_expert_ffn": [cp, i64] + [_vp] * 10 + [_vp],
             "moe_combine_partials": [cp, i64, _vp, _vp, _vp, _vp],
             "moe_layer_forward": [cp, i64] + [_vp] * 15 + [i32, _vp, sz, _vp],
             "moe_rms_norm": [cp, ncp, i64, _vp, _vp, _vp, _vp],
@@ -321,13 +321,15 @@ def moe_expert_ffn_size(cfg, T: int):
 
 
 def moe_expert_ffn(cfg, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_idx, parts,
-                   stream=None):
+                   stream=None, mx=None):
+    """mx: MX scales, in the C argument list after ws_down."""
     c = make_config(cfg)
+    m = make_mx_scales(mx)
     need = moe_expert_ffn_size(cfg, T)
     if need is not None:
         _need(parts, need // 4, "parts")
     _call("moe_expert_ffn", ctypes.byref(c), int(T), _p(x), _p(w_gate), _p(w_up), _p(w_down),
-          _p(ws_gate), _p(ws_up), _p(ws_down), _p(topk_idx), _p(parts), _stream(stream))
+          _p(ws_gate), _p(ws_up), _p(ws_down), _mxp(m), _p(topk_idx), _p(parts), _stream(stream))
 
 
 def moe_combine_partials(cfg, T, parts, topk_w, out, stream=None):

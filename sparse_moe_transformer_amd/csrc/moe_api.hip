@@ -106,11 +106,11 @@ struct Ws {
 
 // The fused decode FFN (gate/up and down in one kernel, by 128-column slices
 // of the intermediate width into fp32 partial planes that the combine sums):
-// bf16 weights and activations, shapes the kernel takes, at most 32 tokens
-// and 256 routed rows. Testing knobs: MOE_DECODE_FFN=0 turns it off, and so
+// bf16 activations (bf16, MXFP8 or MXFP4 weights), shapes the kernel takes,
+// at most 32 tokens and 256 routed rows. Testing knobs: MOE_DECODE_FFN=0 turns it off, and so
 // does MOE_GEMM_TILE=128 (the 128-row tile kernels forced).
 bool ffn_shape(const Dims& d) {
-  return d.dtype == MOE_BF16 && d.wfmt == WF_DTYPE && ffn_decode_fits(d.H, d.I, d.E, d.S, d.Is);
+  return d.dtype == MOE_BF16 && ffn_decode_fits(d.H, d.I, d.E, d.S, d.Is, d.wfmt);
 }
 
 // the batch and the launch fit too (T = 0 aside)
@@ -416,9 +416,19 @@ struct LayerOut {
 // every chosen expert and of the shared experts into the partial planes.
 moe_status do_ffn(const moe_config* c, const Dims& d, const void* x, const void* w_gate,
                   const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
-                  const void* ws_down, const int32_t* topk_idx, float* parts, hipStream_t st,
-                  PartsSrc* src) {
+                  const void* ws_down, const moe_mx_scales* mx, const int32_t* topk_idx,
+                  float* parts, hipStream_t st, PartsSrc* src) {
   GemmArgs g = base_args(c, d);
+  if (d.wfmt != WF_DTYPE) {
+    g.wfmt = d.wfmt;
+    g.sw0 = mx->gate;
+    g.sw1 = mx->up;
+    g.sw2 = mx->down;
+    const size_t per_gu = (size_t)(d.H / 32) * d.I, per_dn = (size_t)(d.I / 32) * d.H;
+    g.sws0 = d.packed ? scale_slot(mx->gate, d, per_gu) : mx->shared_gate;
+    g.sws1 = d.packed ? scale_slot(mx->up, d, per_gu) : mx->shared_up;
+    g.sws2 = d.packed ? scale_slot(mx->down, d, per_dn) : mx->shared_down;
+  }
   const int slice = ffn_decode_slice();
   const int64_t rows = d.T * d.k;
   g.a = x;
@@ -496,7 +506,7 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
   res->y_perm = nullptr;
   res->parts = PartsSrc{nullptr, 0, 0, 0};
   if (use_ffn(d))
-    return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, idx, w.parts, st,
+    return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, mx, idx, w.parts, st,
                   &res->parts);
   const bool fused = group_in_gate_up(d);
   if (!fused)
@@ -632,16 +642,17 @@ moe_status moe_expert_ffn_size(const moe_config* cfg, int64_t T, size_t* bytes) 
 
 moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const void* w_gate,
                           const void* w_up, const void* w_down, const void* ws_gate,
-                          const void* ws_up, const void* ws_down, const int32_t* topk_idx,
-                          float* parts, moe_stream_t stream) {
+                          const void* ws_up, const void* ws_down, const moe_mx_scales* mx,
+                          const int32_t* topk_idx, float* parts, moe_stream_t stream) {
   Dims d;
   MOE_TRY(check_cfg(cfg, T, &d));
   if (!ffn_supported(d)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_gate || !w_up || !w_down || !topk_idx || !parts) return MOE_ERR_INVALID_ARG;
   if (d.S && !d.packed && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_mx(d, mx, true, true));
   PartsSrc src;
-  return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_idx, parts,
+  return do_ffn(cfg, d, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, mx, topk_idx, parts,
                 (hipStream_t)stream, &src);
 }
 

@@ -765,60 +765,166 @@ static_assert(FFN_MAX_E % 64 == 0, "chosen-expert mask words");
 
 // Phase-2 weight rows of an item: columns 128c .. 128c+127 of the down
 // matrix (routed: expert e's [H, I]; shared: matrix s of the S [H, Is]
-// matrices, the one that holds concatenated column 128c).
+// matrices, the one that holds concatenated column 128c), every H row; MX
+// weights also the slice's four scale blocks.
 struct FTile {
-  const char* bbase;  // row 0, column 128c of the slice's down matrix
+  const char* bbase;  // row 0 of the slice's down matrix, at the slice's first input
+  const char* sbase;  // MX: the slice's first scale block of that matrix
   uint32_t boff[8];   // this lane's rows (within a 256-row n-tile) + chunks
+  uint32_t soff;      // MX: this lane's scale bytes within the step's blocks
   int rb;             // bytes per down-matrix row
 };
 
+template <int M>
 __device__ __forceinline__ void make_ftile(const GemmArgs& g, int4 p, FTile& f) {
   const int shared = p.y >> 16, e = p.z;
   const int col = p.w * FFN_CH;
-  if (shared) {
-    const int s = col / g.Is;
-    f.rb = 2 * g.Is;
-    f.bbase = static_cast<const char*>(g.ws2) + ((size_t)s * g.H * g.Is + (col - s * g.Is)) * 2;
+  const int s = shared ? col / g.Is : 0;
+  const int K = shared ? g.Is : g.I;      // inputs per down-matrix row
+  const int c0 = col - s * g.Is * shared;  // the slice's first column in that matrix
+  f.rb = row_bytes<M>(K);
+  const char* mat = shared ? static_cast<const char*>(g.ws2) + (size_t)s * g.H * f.rb
+                           : static_cast<const char*>(g.w2) + (size_t)e * g.H * f.rb;
+  f.bbase = mat + row_bytes<M>(c0);
+  if (M != W_BF16) {
+    // scales [K/32, H] per matrix; lanes 16b .. 16b+15 load block b
+    const uint8_t* sm = shared ? g.sws2 + (size_t)s * (K / 32) * g.H
+                               : g.sw2 + (size_t)e * (K / 32) * g.H;
+    f.sbase = reinterpret_cast<const char*>(sm) + (size_t)(c0 / 32) * g.H;
+    f.soff = (uint32_t)(scale_lane_row() + ((threadIdx.x & 63) >> 4) * g.H);
+  }
+  if (row64<M>()) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int br = b_row_fp8(j);
+      f.boff[j] = (uint32_t)br * (uint32_t)f.rb + (uint32_t)(((threadIdx.x & 3) ^ swz4(br)) * 16);
+    }
   } else {
-    f.rb = 2 * g.I;
-    f.bbase = static_cast<const char*>(g.w2) + ((size_t)e * g.H * g.I + col) * 2;
-  }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int br = b_row(j);
-    f.boff[j] = (uint32_t)br * (uint32_t)f.rb + (uint32_t)(lane_chunk(br) * 16);
+    for (int j = 0; j < 8; ++j) {
+      const int br = b_row(j);
+      f.boff[j] = (uint32_t)br * (uint32_t)f.rb + (uint32_t)(lane_chunk(br) * 16);
+    }
   }
 }
 
-// The activation-row load (one per thread) and the weight-row loads (eight)
-// of gate/up K-step j (bf16; together the loads of issue_stage<W_BF16>).
+// activation-row loads per stage: one, or two 128-byte halves
+template <int M>
+constexpr int a_loads() { return halves<M>() ? 2 : 1; }
+
+// The activation-row loads of gate/up K-step j, then its weight-row loads
+// (with the scale bytes of MX weights): together the loads of issue_stage.
+template <int M>
 __device__ __forceinline__ void issue_gu_a(const DTile& t, int j, u32x4_t* la) {
-  dma16(t.abase + (long)j * KSB, t.aoff, la + 8 * (threadIdx.x >> 6) * NCH);
-}
-__device__ __forceinline__ void issue_gu_b(const DTile& t, int j, u32x4_t* lb) {
   const int w = threadIdx.x >> 6;
-  const char* bb = t.bbase + (long)j * KSB;
+  const char* ab = t.abase + (long)j * (halves<M>() ? 2 * KSB : KSB);
+  dma16(ab, t.aoff, la + 8 * w * NCH);
+  if (halves<M>()) dma16(ab + KSB, t.aoff, la + DBM * NCH + 8 * w * NCH);
+}
+template <int M>
+__device__ __forceinline__ void weight_rows(const char* bb, const uint32_t (&boff)[8],
+                                            u32x4_t* lb) {
+  const int w = threadIdx.x >> 6;
+  if (row64<M>()) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma16(bb, t.boff[q], lb + (64 * w + 8 * q) * NCH);
+    for (int q = 0; q < 4; ++q) dma16(bb, boff[q], lb + (64 * w + 16 * q) * 4);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16(bb, boff[q], lb + (64 * w + 8 * q) * NCH);
+  }
+}
+template <int M>
+__device__ __forceinline__ void issue_gu_b(const DTile& t, int j, u32x4_t* lb) {
+  weight_rows<M>(t.bbase + (long)j * (row64<M>() ? KSB / 2 : KSB), t.boff, lb);
+  if (M != W_BF16)
+    dma4(t.sbase + (long)j * t.sstep, t.soff,
+         reinterpret_cast<const char*>(lb + scales_at<M>()) + 256 * (threadIdx.x >> 6));
 }
 
-// Loads of phase-2 step jj (n-tile jj / 2, K-step jj % 2): the activation
-// rows of gate/up K-step jj (x, not read) and 256 down-matrix rows.
+// Loads of phase-2 step jj: n-tile jj / SPN, K-step jj % SPN of the slice
+// (SPN = 128 / inputs per K-step: two bf16 steps, one MX step): the
+// activation rows of gate/up K-step jj (x, not read), 256 down-matrix rows
+// and their scale bytes.
+template <int M>
 __device__ __forceinline__ void issue_ffn_down(const DTile& t, const FTile& f, int jj,
                                                u32x4_t* la, u32x4_t* lb) {
-  const int w = threadIdx.x >> 6;
-  dma16(t.abase + (long)jj * KSB, t.aoff, la + 8 * w * NCH);
-  const char* bb = f.bbase + (long)(jj >> 1) * 256 * f.rb + (long)(jj & 1) * KSB;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dma16(bb, f.boff[q], lb + (64 * w + 8 * q) * NCH);
+  constexpr int SPN = FFN_CH / k_of<M>();
+  issue_gu_a<M>(t, jj, la);
+  const int nt = jj / SPN, kk = jj % SPN;
+  weight_rows<M>(f.bbase + (long)nt * 256 * f.rb + (long)kk * (row64<M>() ? KSB / 2 : KSB),
+                 f.boff, lb);
+  if (M != W_BF16)
+    dma4(f.sbase + (long)nt * 256, f.soff,
+         reinterpret_cast<const char*>(lb + scales_at<M>()) + 256 * (threadIdx.x >> 6));
 }
 
-// One phase-2 K-step: h slice rows (la, one K-step of the LDS copy) against
-// the stage's down rows; wave w owns output columns 64w .. 64w+63 of the
-// n-tile, block nb the 32 at 64w + 32nb.
+// One phase-2 K-step: h slice rows (la: the LDS copy, one 64-input block
+// for bf16, both for MX) against the stage's down rows, the weights as the
+// MFMA's A operand (so the accumulators hold output columns down a lane's
+// four rows); wave w owns output columns 64w .. 64w+63 of the n-tile, block
+// nb the 32 at 64w + 32nb. The fragments and conversions are those of
+// compute_stage for the same weight mode.
+template <int M>
 __device__ __forceinline__ void compute_ffn_down(const u32x4_t* la, const u32x4_t* lb, Acc2& acc) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int q = lane >> 5, r = lane & 31;
+  if (M == W_FP4) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + scales_at<M>());
+    const u32x4_t* lah = la + q * DBM * NCH;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t wv[2];
+      float scale[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = 64 * w + 32 * nb + r;
+        wv[nb] = lb[row * 4 + ((2 * q + h) ^ swz4(row))];
+        scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * (2 * q + h) + (row & 63)]);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int s = 4 * h + s4;
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lah[r * NCH + (s ^ swz(r))]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4_t& c = wv[nb];
+          const bf16x8_t fb =
+              fp4x8_to_bf16(s4 == 0 ? c.x : s4 == 1 ? c.y : s4 == 2 ? c.z : c.w, scale[nb]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    return;
+  }
+  if (M == W_FP8L) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(lb + scales_at<M>());
+    const u32x4_t* lah = la + q * DBM * NCH;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t wv[2][2];
+      float scale[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = 64 * w + 32 * nb + r;
+        wv[nb][0] = lb[row * NCH + ((4 * q + 2 * h) ^ swz(row))];
+        wv[nb][1] = lb[row * NCH + ((4 * q + 2 * h + 1) ^ swz(row))];
+        scale[nb] = e8m0_scale(sc[256 * (row >> 6) + 64 * (2 * q + h) + (row & 63)]);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int s = 4 * h + s4;
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lah[r * NCH + (s ^ swz(r))]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4_t& c = wv[nb][s4 >> 1];
+          const bf16x8_t fb = (s4 & 1) ? fp8x8_to_bf16(c.z, c.w, scale[nb])
+                                       : fp8x8_to_bf16(c.x, c.y, scale[nb]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, la[r * NCH + ((2 * s + q) ^ swz(r))]);
@@ -895,18 +1001,34 @@ __device__ __forceinline__ int ffn_token(const GemmArgs& g, int4 p, const int* r
 
 }  // namespace
 
-template <int NT2>
+// For the own first item the weight loads of its first NST-1 K-steps went
+// out before their activation loads: the loads younger than stage s's are
+// the activation loads of the later early stages and the full stages issued
+// since.
+template <int NST, int AL, int LOADS>
+__device__ __forceinline__ void spec_wait(int s) {
+  static_assert(NST >= 3 && NST <= 4, "the early steps below");
+  if (s == 0) wait_vmcnt<(NST - 2) * AL>();
+  else if (s == 1) wait_vmcnt<(NST - 3) * AL + LOADS>();
+  else wait_vmcnt<(NST - 2) * LOADS>();
+}
+
+// M: weight mode (W_BF16, W_FP4 or W_FP8L, the K-steps of the 32-row
+// kernels above); NST LDS stages.
+template <int M, int NT2, int NST>
 __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
-  constexpr int NST = 4;
-  constexpr int LOADS = loads_of<W_BF16>();
-  constexpr int NK1 = 4 * NT2;       // gate/up K-steps (K = H = 256 NT2)
-  constexpr int NK = NK1 + 2 * NT2;  // + down: NT2 n-tiles x two 64-input K-steps
+  constexpr int LOADS = loads_of<M>();
+  constexpr int AL = a_loads<M>();
+  constexpr int NK1 = 256 * NT2 / k_of<M>();  // gate/up K-steps (K = H = 256 NT2)
+  constexpr int SPN = FFN_CH / k_of<M>();     // down K-steps per n-tile
+  constexpr int NK = NK1 + NT2 * SPN;         // + down: NT2 n-tiles of the 128-input slice
   static_assert(NK % NST == 0, "an item is a whole number of stage rounds");
   // vector memory ops of a phase-2 epilogue per thread (exact: the waits of
   // the next item's first steps count them)
   constexpr int EPI = 8 * NT2;
-  constexpr int STAGE = stage_u4<W_BF16>();
-  constexpr int STAGE_A = stage_a<W_BF16>();
+  static_assert((NST - 2) * LOADS + EPI < 64, "waits within the load counter's range");
+  constexpr int STAGE = stage_u4<M>();
+  constexpr int STAGE_A = stage_a<M>();
   __shared__ __align__(16) u32x4_t lds_st[NST][STAGE];
   __shared__ __align__(16) u32x4_t lds_h[2 * DBM * NCH];  // the item's activated slice
   __shared__ __align__(16) int tk[256];          // routed experts of the batch's rows
@@ -921,6 +1043,8 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
   asm volatile("" ::"s"(g.topk_idx), "s"(g.a), "s"(g.w0), "s"(g.w1), "s"(g.ws0), "s"(g.ws1),
                "s"(g.T), "s"(g.k), "s"(g.E), "s"(g.H), "s"(g.I), "s"(g.S), "s"(g.Is),
                "s"(g.nt_routed), "s"(g.nt_shared));
+  if (M != W_BF16)
+    asm volatile("" ::"s"(g.sw0), "s"(g.sw1), "s"(g.sws0), "s"(g.sws1));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = blockIdx.x, G = gridDim.x;
   const int rows = g.T * g.k, nr = g.nt_routed, E = g.E;
@@ -935,10 +1059,10 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
        tk + 64 * w);
   DTile cur, nxt;
   FTile fd;
-  make_tile<GATE_UP, W_BF16>(g, ffn_potential(g, b, 1), 0, cur);
+  make_tile<GATE_UP, M>(g, ffn_potential(g, b, 1), 0, cur);
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st) issue_gu_b(cur, st, lds_st[st] + STAGE_A);
-  wait_vmcnt<(NST - 1) * (LOADS - 1)>();  // the expert ids have landed
+  for (int st = 0; st < NST - 1; ++st) issue_gu_b<M>(cur, st, lds_st[st] + STAGE_A);
+  wait_vmcnt<(NST - 1) * (LOADS - AL)>();  // the expert ids have landed
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   if ((int)threadIdx.x < rows && (unsigned)tk[threadIdx.x] < (unsigned)E) chosen[tk[threadIdx.x]] = 1;
@@ -1044,17 +1168,17 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
   // loads to land, then load all of its first three K-steps)
   const int4 p0 = place(0);
   const bool own = __builtin_amdgcn_readfirstlane(own_real) != 0;
-  make_tile<GATE_UP, W_BF16>(g, p0, ffn_token(g, p0, rows_of[p0.x]), cur);
+  make_tile<GATE_UP, M>(g, p0, ffn_token(g, p0, rows_of[p0.x]), cur);
   if (own) {
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st) issue_gu_a(cur, st, lds_st[st]);
+    for (int st = 0; st < NST - 1; ++st) issue_gu_a<M>(cur, st, lds_st[st]);
   } else {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st) {
-      issue_gu_a(cur, st, lds_st[st]);
-      issue_gu_b(cur, st, lds_st[st] + STAGE_A);
+      issue_gu_a<M>(cur, st, lds_st[st]);
+      issue_gu_b<M>(cur, st, lds_st[st] + STAGE_A);
     }
   }
 
@@ -1062,8 +1186,8 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
   for (int li = 0;; ++li) {
     const bool has_next = li + 1 < n_my;
     const int4 pc = place(li), pn = place(li + 1);
-    make_ftile(g, pc, fd);
-    make_tile<GATE_UP, W_BF16>(g, pn, ffn_token(g, pn, rows_of[pn.x]), nxt);
+    make_ftile<M>(g, pc, fd);
+    make_tile<GATE_UP, M>(g, pn, ffn_token(g, pn, rows_of[pn.x]), nxt);
     Acc2 acc;
     Acc2 dacc[NT2];
 #pragma unroll
@@ -1074,34 +1198,32 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
 #pragma unroll
         for (int nt = 0; nt < NT2; ++nt) dacc[nt][nb][v] = 0.f;
       }
-    // step s: wait for stage s, barrier, issue step s + 3 (this item's
+    // step s: wait for stage s, barrier, issue step s + NST-1 (this item's
     // gate/up or down rows, or the next item's first steps), compute stage
     // s; after the last gate/up step the slice goes to LDS. Waits: loads
-    // issued after stage s's are two stages, plus the previous item's
-    // epilogue stores in an item's first three steps; for the own first item
-    // the activation loads of steps 0 .. 2 came after the weight loads, so
-    // its steps 0 and 1 have 2 and 10 younger loads
+    // issued after stage s's are NST-2 stages, plus the previous item's
+    // epilogue stores in an item's first NST-1 steps (spec_wait for the own
+    // first item)
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
-      if (s == 0 && first && own) wait_vmcnt<2>();
-      else if (s == 1 && first && own) wait_vmcnt<LOADS + 1>();
+      if (s < NST - 1 && first && own) spec_wait<NST, AL, LOADS>(s);
       else if (s < NST - 1 && !first) wait_vmcnt<(NST - 2) * LOADS + EPI>();
       else wait_vmcnt<(NST - 2) * LOADS>();
       __builtin_amdgcn_s_barrier();
       const int sl = s + NST - 1;
       u32x4_t* la = lds_st[sl % NST];
       if (sl < NK1) {
-        issue_gu_a(cur, sl, la);
-        issue_gu_b(cur, sl, la + STAGE_A);
+        issue_gu_a<M>(cur, sl, la);
+        issue_gu_b<M>(cur, sl, la + STAGE_A);
       } else if (sl < NK) {
-        issue_ffn_down(cur, fd, sl - NK1, la, la + STAGE_A);
+        issue_ffn_down<M>(cur, fd, sl - NK1, la, la + STAGE_A);
       } else {
-        issue_gu_a(nxt, sl - NK, la);
-        issue_gu_b(nxt, sl - NK, la + STAGE_A);
+        issue_gu_a<M>(nxt, sl - NK, la);
+        issue_gu_b<M>(nxt, sl - NK, la + STAGE_A);
       }
       const u32x4_t* lc = lds_st[s % NST];
       if (s < NK1) {
-        compute_stage<GATE_UP, W_BF16>(lc, lc + STAGE_A, acc);
+        compute_stage<GATE_UP, M>(lc, lc + STAGE_A, acc);
         if (s == NK1 - 1) {
           ffn_h_to_lds(g, acc, lds_h);
           // the slice is in LDS before the next step's barrier
@@ -1110,7 +1232,9 @@ __global__ void __launch_bounds__(NTHR) moe_ffn_decode_kernel(GemmArgs g) {
           __asm__ __volatile__("" ::: "memory");
         }
       } else {
-        compute_ffn_down(lds_h + ((s - NK1) & 1) * DBM * NCH, lc + STAGE_A, dacc[(s - NK1) >> 1]);
+        // bf16: the 64-input block of the slice for this K-step; MX: both
+        compute_ffn_down<M>(lds_h + (M == W_BF16 ? ((s - NK1) % SPN) * DBM * NCH : 0),
+                            lc + STAGE_A, dacc[(s - NK1) / SPN]);
       }
     }
     ffn_epilogue<NT2>(g, pc, rows_of[pc.x], dacc);
@@ -1230,13 +1354,15 @@ hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t
   return DEC_LAUNCH(moe_down_routed_decode_kernel, v, n, g, st);
 }
 
-// Shapes the fused FFN kernel takes: H = 512 or 1024 (NT2 = 2 or 4), the
+// Shapes the fused FFN kernel takes: H = 512 or 1024 (NT2 = 2 or 4; MXFP4
+// weights H = 1024, whose 12 K-steps per item fill the four stages), the
 // intermediate widths whole 128-column slices, E within the kernel's LDS
 // arrays, and one expert's (and all shared experts') weights within the
 // per-lane 32-bit offsets. The batch limits (T <= 32 tokens, T * k <= 256
-// rows) and bf16 weights are the caller's to check.
-bool ffn_decode_fits(int H, int I, int E, int S, int Is) {
+// rows) and bf16 activations are the caller's to check.
+bool ffn_decode_fits(int H, int I, int E, int S, int Is, int wfmt) {
   if (H != 512 && H != 1024) return false;
+  if (wfmt == WF_MXFP4 && H != 1024) return false;
   if (I <= 0 || I % FFN_CH || E > FFN_MAX_E) return false;
   if (S && (Is <= 0 || Is % FFN_CH)) return false;
   const uint64_t lim = 1ull << 31;
@@ -1273,11 +1399,16 @@ hipError_t launch_ffn_decode(const GemmArgs& g, hipStream_t st) {
   const int G = ffn_grid(P);
   if (!ffn_items_fit(P, G) || g.T < 1 || g.T > DBM || g.T * g.k > 256 || g.E > FFN_MAX_E)
     return hipErrorInvalidValue;
-  if (g.H == 1024)
-    hipLaunchKernelGGL(moe_ffn_decode_kernel<4>, dim3((unsigned)G), dim3(NTHR), 0, st, g);
-  else if (g.H == 512)
-    hipLaunchKernelGGL(moe_ffn_decode_kernel<2>, dim3((unsigned)G), dim3(NTHR), 0, st, g);
-  else
-    return hipErrorInvalidValue;
+  void (*kern)(GemmArgs) = nullptr;
+  if (g.wfmt == WF_DTYPE)
+    kern = g.H == 1024 ? moe_ffn_decode_kernel<W_BF16, 4, 4>
+         : g.H == 512  ? moe_ffn_decode_kernel<W_BF16, 2, 4> : nullptr;
+  else if (g.wfmt == WF_MXFP4)
+    kern = g.H == 1024 ? moe_ffn_decode_kernel<W_FP4, 4, 4> : nullptr;
+  else if (g.wfmt == WF_MXFP8)
+    kern = g.H == 1024 ? moe_ffn_decode_kernel<W_FP8L, 4, 3>
+         : g.H == 512  ? moe_ffn_decode_kernel<W_FP8L, 2, 3> : nullptr;
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(NTHR), 0, st, g);
   return hipGetLastError();
 }

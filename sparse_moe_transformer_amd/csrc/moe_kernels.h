@@ -48,10 +48,13 @@ struct GemmArgs {
   int32_t* sorted_out;
   int32_t* row_pos_out;
   // Fused decode FFN (launch_ffn_decode, which also reads topk_idx): the
-  // routed and shared down weights and the fp32 partial planes,
-  // [I/128][T*k][H] (by routed row t*k + j) then [S*Is/128][T][H].
+  // routed and shared down weights (MX: their scales too) and the fp32
+  // partial planes, [I/128][T*k][H] (by routed row t*k + j) then
+  // [S*Is/128][T][H].
   const void* w2;
   const void* ws2;
+  const uint8_t* sw2;
+  const uint8_t* sws2;
   float* parts;
 };
 
@@ -71,9 +74,10 @@ hipError_t launch_down_both_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_shared_decode(const GemmArgs& g, hipStream_t st);
 hipError_t launch_down_routed_decode(const GemmArgs& g, bool atomic, hipStream_t st);
 // Fused gate/up + down of decode batches of at most 32 tokens and 256 routed
-// rows (bf16 weights; shapes: ffn_decode_fits), by 128-column slices of the
-// intermediate width (ffn_decode_slice) into fp32 partial planes.
-bool ffn_decode_fits(int H, int I, int E, int S, int Is);
+// rows (bf16 activations, bf16 / MXFP8 / MXFP4 weights; shapes:
+// ffn_decode_fits), by 128-column slices of the intermediate width
+// (ffn_decode_slice) into fp32 partial planes.
+bool ffn_decode_fits(int H, int I, int E, int S, int Is, int wfmt);
 // ... and every workgroup's share of the work items fits its list (depends
 // on the device's compute units)
 bool ffn_decode_schedulable(int E, int I, int S, int Is);

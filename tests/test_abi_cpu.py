@@ -205,8 +205,12 @@ def test_expert_ffn_applies_where_documented():
     for bad, T in [({}, 33), ({"num_experts_per_tok": 9}, 32), ({"hidden_size": 768}, 8),
                    ({"hidden_size": 2048}, 8), ({"moe_intermediate_size": 192}, 8),
                    ({"shared_intermediate_size": 320}, 8), ({"num_experts": 300}, 8),
-                   ({"dtype": "f32"}, 8), ({"weight_format": "mxfp4"}, 8)]:
+                   ({"dtype": "f32"}, 8), ({"weight_format": "mxfp4", "hidden_size": 512}, 8)]:
         assert moe.moe_expert_ffn_size(_tri(**bad), T) is None, bad
+    # MX weights: MXFP8 at hidden 512 and 1024, MXFP4 at 1024
+    for wf, H in (("mxfp8", 512), ("mxfp8", 1024), ("mxfp4", 1024)):
+        assert moe.moe_expert_ffn_size(_tri(weight_format=wf, hidden_size=H), 4) == \
+            (I // 128 * 4 * k + 256 // 128 * 4) * H * 4
 
 
 def test_expert_ffn_host_checks():
@@ -215,12 +219,14 @@ def test_expert_ffn_host_checks():
     p = 0x1000
     c = moe.make_config(_tri())
     ffn = lambda T, parts=p, idx=p, cc=c: L.moe_expert_ffn(ctypes.byref(cc), T, p, p, p, p, p, p, p,
-                                                          idx, parts, None)
+                                                          None, idx, parts, None)
     assert ffn(0) == moe.MOE_OK
     assert ffn(8, parts=None) == moe.MOE_ERR_INVALID_ARG
     assert ffn(8, idx=None) == moe.MOE_ERR_INVALID_ARG
     assert ffn(33) == moe.MOE_ERR_UNSUPPORTED
     assert ffn(8, cc=moe.make_config(_tri(hidden_size=768))) == moe.MOE_ERR_UNSUPPORTED
+    # MX weights need their scales
+    assert ffn(8, cc=moe.make_config(_tri(weight_format="mxfp4"))) == moe.MOE_ERR_INVALID_ARG
     comb = lambda T, parts=p: L.moe_combine_partials(ctypes.byref(c), T, parts, p, p, None)
     assert comb(0) == moe.MOE_OK
     assert comb(8, parts=None) == moe.MOE_ERR_INVALID_ARG

@@ -13,7 +13,8 @@ GPU's own router logits: routing exactly, the output at the layer's bf16 bar
 no shared expert, two separate shared experts (one slice each) and a shared
 width of three slices, the packed shared slot with clamp-SwiGLU, one token,
 256 experts (the kernel's limit), 256 routed rows with every expert full
-(k = E), and hidden 512 and 1024 (two and four down n-tiles). The same layer
+(k = E), hidden 512 and 1024 (two and four down n-tiles), and MXFP8 and
+MXFP4 expert weights (the oracle on their exact values). The same layer
 with the fused kernel switched off (MOE_DECODE_FFN=0: separate gate/up and
 down kernels) is held to the same bar, and the two differ in rounding only
 (the fused path never rounds an expert's output to bf16), which also shows
@@ -25,6 +26,7 @@ import pytest
 from oracle import moe_oracle as O
 from tests.moe_harness import TOL, Dev, custom, generated, rel_err, say
 from tests.test_gpu_block import check_block, run_block
+from tests.test_gpu_mxfp8 import oracle_view
 from tests.test_gpu_parity import check_routing
 from workloads import synth
 
@@ -58,6 +60,18 @@ FFN = {
     "k_eq_E_full_tiles": custom(T=32, hidden_size=512, num_experts=8, num_experts_per_tok=8,
                                 moe_intermediate_size=128, num_shared_experts=1,
                                 shared_intermediate_size=384),
+    # MX expert weights (the gate/up and down K-steps of 128 inputs)
+    "mxfp8_h512_two_shared": custom(T=7, hidden_size=512, num_experts=32, num_experts_per_tok=4,
+                                    moe_intermediate_size=256, num_shared_experts=2,
+                                    shared_intermediate_size=128, weight_format="mxfp8"),
+    "mxfp4_packed_clamp": custom(T=24, hidden_size=1024, num_experts=64, num_experts_per_tok=6,
+                                 moe_intermediate_size=256, num_shared_experts=1,
+                                 shared_packed=1, hidden_act="swigluoai", route_scale=2.0,
+                                 weight_format="mxfp4"),
+    "mxfp8_one_token_i512": custom(T=1, hidden_size=1024, num_experts=128,
+                                   num_experts_per_tok=8, moe_intermediate_size=512,
+                                   num_shared_experts=1, shared_intermediate_size=256,
+                                   weight_format="mxfp8"),
 }
 
 
@@ -71,13 +85,15 @@ def _layer(dev, det, monkeypatch, fused):
 
 def _check(cfg, inp, res):
     check_routing(cfg, inp, res)
-    ref = O.moe_forward(inp, cfg, logits=res["logits"])
+    ref = O.moe_forward(oracle_view(inp), cfg, logits=res["logits"])
     e = rel_err(res["out"], ref["out"])
     assert e <= TOL["bf16"], f"out rel err {e:.3e}"
     return e
 
 
-@pytest.mark.parametrize("name", list(FFN) + ["trinity_nano_decode_T32"])
+@pytest.mark.parametrize("name", list(FFN) + ["trinity_nano_decode_T32",
+                                              "trinity_nano_decode_T32_mxfp4",
+                                              "trinity_nano_decode_T32_mxfp8"])
 def test_fused_ffn_matches_oracle(name, monkeypatch):
     inp = generated(name) if name in synth.CONFIGS else synth.generate(FFN[name])
     cfg = inp.cfg
@@ -95,7 +111,7 @@ def test_fused_ffn_matches_oracle(name, monkeypatch):
 
 
 @pytest.mark.parametrize("grid,name", [(1, "few_items"), (3, "few_items"), (3, "many_items"),
-                                       (5, "many_items")])
+                                       (5, "many_items"), (3, "many_items_mxfp4")])
 def test_fused_ffn_small_grids(grid, name, monkeypatch):
     """Fewer workgroups than work items (MOE_FFN_GRID caps the grid): the
     items beyond the grid go to the workgroups whose own item is not real,
@@ -106,7 +122,11 @@ def test_fused_ffn_small_grids(grid, name, monkeypatch):
                                shared_intermediate_size=128),
            "many_items": custom(T=9, hidden_size=1024, num_experts=16, num_experts_per_tok=2,
                                 moe_intermediate_size=128, num_shared_experts=2,
-                                shared_intermediate_size=128)}[name]
+                                shared_intermediate_size=128),
+           "many_items_mxfp4": custom(T=9, hidden_size=1024, num_experts=16,
+                                      num_experts_per_tok=2, moe_intermediate_size=128,
+                                      num_shared_experts=2, shared_intermediate_size=128,
+                                      weight_format="mxfp4")}[name]
     inp = synth.generate(cfg)
     dev = Dev(inp)
     monkeypatch.setenv("MOE_FFN_GRID", str(grid))
@@ -166,7 +186,8 @@ def test_fused_ffn_inside_the_block(monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["trinity_nano_decode_T32", "two_shared_four_slices",
-                                  "packed_clamp_h512"])
+                                  "packed_clamp_h512", "trinity_nano_decode_T32_mxfp4",
+                                  "mxfp8_h512_two_shared"])
 def test_ffn_entry_points(name, monkeypatch):
     """moe_expert_ffn and moe_combine_partials called on their own: every
     partial plane against the oracle's expert FFN restricted to that slice of
@@ -187,7 +208,7 @@ def test_ffn_entry_points(name, monkeypatch):
     assert n == (nr * T * k + ns * T) * H * 4
     parts = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
     moe.moe_expert_ffn(c, T, dev.x, dev.w_gate, dev.w_up, dev.w_down, dev.ws_gate, dev.ws_up,
-                       dev.ws_down, idx, parts)
+                       dev.ws_down, idx, parts, mx=dev.mx)
     out = torch.empty(T * H, dtype=moe.torch_dtype(c), device="cuda")
     moe.moe_combine_partials(c, T, parts, w, out)
     torch.cuda.synchronize()
@@ -197,6 +218,7 @@ def test_ffn_entry_points(name, monkeypatch):
     P = parts.cpu().numpy().astype(np.float64)
     routed = P[: nr * T * k * H].reshape(nr, T * k, H)
     shared = P[nr * T * k * H:].reshape(ns, T, H) if ns else None
+    ov = oracle_view(inp)   # MX weights as their exact values
     x = O.as_f64(inp.x)
     act = O.activation(cfg)
     worst = 0.0
@@ -205,13 +227,13 @@ def test_ffn_entry_points(name, monkeypatch):
         ref = np.zeros((T * k, H))
         for r in range(T * k):
             e = int(layer["idx"].reshape(-1)[r])
-            he = O.mlp_hidden(x[r // k][None], O.as_f64(inp.w_gate[e][C]), O.as_f64(inp.w_up[e][C]),
+            he = O.mlp_hidden(x[r // k][None], O.as_f64(ov.w_gate[e][C]), O.as_f64(ov.w_up[e][C]),
                               act)
-            ref[r] = O.mlp_out(he, O.as_f64(inp.w_down[e][:, C]))[0]
+            ref[r] = O.mlp_out(he, O.as_f64(ov.w_down[e][:, C]))[0]
         e_c = rel_err(routed[cs], ref)
         assert e_c <= TOL["bf16"], f"routed plane {cs}: {e_c:.3e}"
         worst = max(worst, e_c)
-    sw = O._shared_weights(inp, cfg)
+    sw = O._shared_weights(ov, cfg)
     for a in range(ns):
         s, off = divmod(128 * a, Is)
         wg, wu, wd = sw[s]
