@@ -476,8 +476,9 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
                      int32_t deterministic, const Ws& w, hipStream_t st, LayerOut* res) {
   const int T = (int)d.T;
   const float* logits = router_logits_in;
-  // small bf16 batches: the router leaves per-K-group planes and the routing
-  // kernel sums them (storing the logits) before it routes
+  // bf16 batches: the router leaves per-K-group planes (small batches) or
+  // its K-chunk partials (larger ones) and the routing kernel sums them in
+  // order (storing the logits) before it routes
   const float* planes = nullptr;
   int np = 0;
   float* lo = router_logits_out ? router_logits_out : w.logits;
@@ -489,7 +490,8 @@ moe_status run_layer(const moe_config* cfg, const Dims& d, const void* x, const 
       planes = static_cast<const float*>(w.router);
       MOE_TRY(hip_ok(launch_router_planes(x, wr, static_cast<float*>(w.router), T, d.H, d.E, st)));
     } else {
-      MOE_TRY(hip_ok(launch_router_logits(x, wr, lo, T, d.H, d.E, d.dtype, w.router, st)));
+      MOE_TRY(hip_ok(launch_router_chunks(x, wr, lo, T, d.H, d.E, d.dtype, w.router, st, &planes,
+                                          &np)));
     }
     logits = lo;
   }

@@ -108,6 +108,13 @@ constexpr int ROUTER_MAX_PLANES = 32;
 int router_planes(int64_t T, int H, int dtype);
 hipError_t launch_router_planes(const void* x, const float* w_router, float* part, int T, int H,
                                 int E, hipStream_t st);
+// Larger batches: the router GEMM with its K-chunk partials ([kc][T][E] fp32,
+// kc <= ROUTER_MAX_PLANES) left for the routing kernel to sum in chunk order
+// (*planes, *np = kc), or, when there is one chunk or more than that many,
+// the logits written whole (*np = 0).
+hipError_t launch_router_chunks(const void* x, const float* w_router, float* logits, int T, int H,
+                                int E, int dtype, void* ws, hipStream_t st, const float** planes,
+                                int* np);
 
 hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k,
                         int score_func, int route_norm, float route_scale, int32_t* idx,

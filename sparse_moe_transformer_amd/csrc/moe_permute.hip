@@ -4,7 +4,8 @@
 //     expert histogram in LDS and the rank of every row among the earlier
 //     rows of its chunk with the same expert;
 //  2. scan pass (one workgroup): per expert, the running count over chunks
-//     (column scan) and the exclusive scan over experts -> expert_offsets;
+//     (column scan, split over up to 16 threads per expert) and the
+//     exclusive scan over experts -> expert_offsets;
 //  3. scatter pass: pos = offsets[e] + rows of e in earlier chunks + rank.
 // Up to 1024 rows (decode batches) the same sort runs in one workgroup.
 // Nothing returns to the host; the result does not depend on timing.
@@ -39,29 +40,55 @@ __global__ void __launch_bounds__(CH) permute_chunk_kernel(const int32_t* __rest
 }
 
 // One workgroup of 1024 threads. chunk_hist is rewritten in place with the
-// exclusive column prefix (rows of expert e in chunks before c).
-__global__ void __launch_bounds__(1024) permute_scan_kernel(int nchunks, int E,
+// exclusive column prefix (rows of expert e in chunks before c). P threads
+// share an expert (P * E <= 1024, P <= 16): thread (e, p) owns the chunks
+// [p * L, (p + 1) * L), sums them (pass 1), takes the sum of the ranges
+// before its own from LDS, and writes its range's running prefix (pass 2,
+// re-reading the same L2-resident values). Each pass keeps 16 loads in
+// flight, so a pass takes about L / 16 round trips instead of nchunks / 16.
+__global__ void __launch_bounds__(1024) permute_scan_kernel(int nchunks, int E, int P,
                                                             int32_t* __restrict__ chunk_hist,
                                                             int32_t* __restrict__ offsets) {
+  __shared__ int psum[1024];  // [P][E]: the sum of each thread's range
   __shared__ int wsum[16];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    // 16 independent loads in flight per round trip
-    constexpr int B = 16;
-    for (int c0 = 0; c0 < nchunks; c0 += B) {
+  constexpr int B = 16;
+  const int e = threadIdx.x % E, p = threadIdx.x / E;
+  const bool active = p < P;
+  const int L = (nchunks + P - 1) / P;
+  const int c_lo = min(nchunks, p * L), c_hi = min(nchunks, c_lo + L);
+  int mine = 0;
+  if (active) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += B) {
       int v[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u)
-        v[u] = (c0 + u < nchunks) ? chunk_hist[(size_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < B; ++u) v[u] = (c0 + u < c_hi) ? chunk_hist[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) mine += v[u];
+    }
+    psum[p * E + e] = mine;
+  }
+  __syncthreads();
+  int before = 0, run = 0;  // rows of e in the ranges before p; in all ranges
+  if (active) {
+    for (int q = 0; q < P; ++q) {
+      const int s = psum[q * E + e];
+      if (q < p) before += s;
+      run += s;
+    }
+    int acc = before;
+    for (int c0 = c_lo; c0 < c_hi; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) v[u] = (c0 + u < c_hi) ? chunk_hist[(size_t)(c0 + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < B; ++u) {
-        if (c0 + u < nchunks) chunk_hist[(size_t)(c0 + u) * E + e] = run;
-        run += v[u];
+        if (c0 + u < c_hi) chunk_hist[(size_t)(c0 + u) * E + e] = acc;
+        acc += v[u];
       }
     }
   }
-  // exclusive scan of run over experts (E <= 1024)
+  // exclusive scan over experts of the totals (threads e < E, E <= 1024)
+  if (threadIdx.x >= E) run = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = run;
 #pragma unroll
@@ -83,8 +110,8 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(int nchunks, int E,
   }
   __syncthreads();
   const int excl = incl - run + wsum[wave];
-  if (e < E) offsets[e] = excl;
-  if (e == E - 1) offsets[E] = excl + run;
+  if ((int)threadIdx.x < E) offsets[threadIdx.x] = excl;
+  if ((int)threadIdx.x == E - 1) offsets[E] = excl + run;
 }
 
 __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __restrict__ idx,
@@ -138,7 +165,10 @@ hipError_t launch_permute(const int32_t* idx, int rows, int E, int32_t* offsets,
   const int nch = (rows + CH - 1) / CH;
   hipLaunchKernelGGL(permute_chunk_kernel, dim3(nch), dim3(CH), E * sizeof(int), st, idx, rows,
                      E, local_rank, chunk_hist);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, st, nch, E, chunk_hist,
+  int P = 1024 / E;  // threads per expert (E <= 1024)
+  if (P > 16) P = 16;
+  if (P > nch) P = nch;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, st, nch, E, P, chunk_hist,
                      offsets);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, idx,
                      rows, E, offsets, chunk_hist, local_rank, sorted_rows, row_pos);

@@ -459,8 +459,15 @@ hipError_t launch_router_planes(const void* x, const float* w_router, float* par
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
-                                int H, int E, int dtype, void* ws, hipStream_t st) {
+// The router GEMM. With `chunks` given, a bf16 batch whose K range is split
+// into chunks (at most ROUTER_MAX_PLANES of them) leaves the chunk partials
+// [kc, T, E] in the workspace for the consumer to sum in chunk order (the
+// routing kernel in the layer), and *chunks / *np say where; otherwise, and
+// with *np = 0, the logits are written whole.
+static hipError_t router_logits(const void* x, const float* w_router, float* logits, int T, int H,
+                                int E, int dtype, void* ws, hipStream_t st, const float** chunks,
+                                int* np) {
+  if (np) *np = 0;
   if (dtype != MOE_BF16) {
     dim3 grid((T + RT_M - 1) / RT_M, (E + RT_N - 1) / RT_N);
     hipLaunchKernelGGL(router_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(x),
@@ -494,10 +501,24 @@ hipError_t launch_router_logits(const void* x, const float* w_router, float* log
     hipLaunchKernelGGL(router_partial_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(x), planes, part, T, H, E, H / kc);
   }
-  if (kc > 1) {
+  if (kc > 1 && chunks && kc <= ROUTER_MAX_PLANES) {
+    *chunks = part;
+    *np = kc;
+  } else if (kc > 1) {
     const size_t m = (size_t)T * E;
     hipLaunchKernelGGL(router_reduce_kernel, dim3(grid_blocks(m)), dim3(256), 0, st, part, kc, m,
                        logits);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const void* x, const float* w_router, float* logits, int T,
+                                int H, int E, int dtype, void* ws, hipStream_t st) {
+  return router_logits(x, w_router, logits, T, H, E, dtype, ws, st, nullptr, nullptr);
+}
+
+hipError_t launch_router_chunks(const void* x, const float* w_router, float* logits, int T, int H,
+                                int E, int dtype, void* ws, hipStream_t st, const float** planes,
+                                int* np) {
+  return router_logits(x, w_router, logits, T, H, E, dtype, ws, st, planes, np);
 }
