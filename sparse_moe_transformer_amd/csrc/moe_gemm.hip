@@ -23,9 +23,9 @@
 // MFMAs, one barrier per step. The load stream runs on across tiles: the last
 // two steps of a tile load the first two stages of the next tile, so they are
 // in flight during this tile's epilogue. Each tile's step count is padded to
-// a multiple of three with loads of a zero line, so the LDS stage of every
-// step is known at compile time; the padding steps (at most the tile's last
-// two) skip their MFMAs. The three stages are
+// a multiple of three, so the LDS stage of every step is known at compile
+// time; the padding steps (at most the tile's last two) skip their MFMAs and
+// their loads re-read the tile's last real step. The three stages are
 // distinct __shared__ arrays and the barrier is a raw s_barrier, so the
 // compiler does not drain all loads before each LDS read. Nothing that a later
 // step must wait for is loaded after the look-ahead loads of a step (vector
@@ -132,39 +132,39 @@ struct Tile {
   int shared, e, row0, nrows, n0, N;
 };
 
-// Load this lane's chunks for step j of tile t into LDS stage (la, lb) (the
-// zero line for padding steps j >= nk: zero codes and zero activations add
-// exactly zero).
+// Load this lane's chunks for step j of tile t into LDS stage (la, lb).
+// Padding steps (j >= nk) re-read the tile's last real step: their MFMAs are
+// skipped, so what they load is never used, and a valid address keeps every
+// step's loads the same without a per-lane choice of source.
 template <int WM>
 __device__ __forceinline__ void issue_stage(const Tile& t, int j, u32x4_t* la, u32x4_t* lb) {
-  const bool real = j < t.nk;
-  const int kb = j * KSB;
+  const int jr = j < t.nk ? j : t.nk - 1;
+  const int kb = jr * KSB;
   // weight bytes per step
-  const int kw = WM == WF_MXFP8 ? j * (KSB / 2) : WM == WF_MXFP4 ? j * (KSB / 4) : kb;
+  const int kw = WM == WF_MXFP8 ? jr * (KSB / 2) : WM == WF_MXFP4 ? jr * (KSB / 4) : kb;
   const int seg = kw / t.kseg;
   const long boff = (long)seg * t.bstride_kb * 1024 + (kw - seg * t.kseg);
-  const char* z = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 7) * 16;
-  const int w = threadIdx.x >> 6;
+  // wave-uniform, so the LDS addresses are scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_global_load_lds(real ? t.a[q] + kb : z, la + (w * 4 + q) * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(t.a[q] + kb, la + (w * 4 + q) * 64, 16, 0, 0);
   if (WM != WF_DTYPE) {
     if (WM == WF_MXFP8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 256 + q * 64, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(t.b[q] + boff, lb + w * 256 + q * 64, 16, 0, 0);
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + w * 128 + q * 64, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(t.b[q] + boff, lb + w * 128 + q * 64, 16, 0, 0);
     }
-    const char* zs = reinterpret_cast<const char*>(g_zero_line) + (threadIdx.x & 31) * 4;
-    __builtin_amdgcn_global_load_lds(real ? t.s + (long)j * t.sstep : zs,
-                                     lb + scales_at<WM>() + w * 16, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(t.s + (long)jr * t.sstep, lb + scales_at<WM>() + w * 16, 4,
+                                     0, 0);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds(real ? t.b[q] + boff : z, lb + (w * 8 + q) * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(t.b[q] + boff, lb + (w * 8 + q) * 64, 16, 0, 0);
   }
 }
 
