@@ -543,9 +543,12 @@ __device__ __forceinline__ void moe_gemm_body(const GemmArgs& g) {
   if (KIND != DOWN_SHARED) build_tile_prefix<BM>(g.offsets, g.E, offs, cum);
   __syncthreads();
   const int ntiles = tile_count<KIND>(g, cum);
-  // this workgroup's tiles: its XCD's contiguous range (the shared down
-  // tiles of the combined down launch are split over the XCDs separately)
-  const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH ? g.mt_shared * g.nt_shared : 0);
+  // this workgroup's tiles: its XCD's contiguous range of the shared-expert
+  // tiles and of the routed ones, each split over the XCDs separately, so
+  // every XCD streams its share of the routed experts' weights (with the
+  // shared tiles first in one range, two XCDs would take the dense shared
+  // expert and the other six every routed weight)
+  const WgTiles wt = wg_tiles(ntiles, KIND == DOWN_BOTH || KIND == GATE_UP ? g.mt_shared * g.nt_shared : 0);
   const int n_my = wt.n_my;
   if (n_my == 0) return;
   auto gtile = [&](int i) { return wt.global(i); };
