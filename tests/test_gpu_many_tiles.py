@@ -1,16 +1,27 @@
-"""A batch large enough that every workgroup of the 128-row grouped GEMMs
+"""Batches large enough that every workgroup of the persistent grouped GEMMs
 runs more tiles than it places up front: a workgroup stores the places of
-its first 256 tiles in LDS and computes the places of later ones on the fly.
-600000 tokens, hidden 64, 4 experts top-2, intermediate 1024 (8 gate/up
-column tiles): about 290 gate/up tiles per workgroup on a 256-CU chip.
-Routing is checked over every token, and every token's output against the
-float64 oracle (per token, in chunks), at the layer's bf16 bar."""
+its first tiles in LDS (256 for the 128-row kernels, 128 for the 256-row
+ones) and computes the places of later ones on the fly.
+
+* 128-row kernels: 600000 tokens, hidden 64, 4 experts top-2, intermediate
+  1024 (8 gate/up column tiles): about 290 gate/up tiles per workgroup.
+  Every token's output is compared with the float64 oracle (per token, in
+  chunks).
+* 256-row kernels: 600000 tokens, hidden and intermediate 1024, 4 experts
+  top-2: about 146 gate/up tiles per workgroup. 24576 sampled tokens are
+  compared (a 256-row tile holds none of their rows with probability about
+  2e-5, (1 - 24576/600000)^256), the oracle's cost at full size being about
+  7 TFLOP in float64.
+
+Routing is checked over every token in both, at the layer's bf16 bar."""
 import numpy as np
 import pytest
 
 from oracle import moe_oracle as O
 from tests.moe_harness import TOL, Dev, custom, say
 from workloads import synth
+
+import bench
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +41,9 @@ def _gpu():
 
 
 def test_more_tiles_per_workgroup_than_placed_up_front():
+    assert bench.gate_up_kernel(custom(T=600000, hidden_size=64, num_experts=4,
+                                       num_experts_per_tok=2, moe_intermediate_size=1024,
+                                       num_shared_experts=0), 600000) == "moe_gate_up_kernel"
     cfg = custom(T=600000, hidden_size=64, num_experts=4, num_experts_per_tok=2,
                  moe_intermediate_size=1024, num_shared_experts=0, name="many_tiles")
     inp = synth.generate(cfg)
@@ -56,3 +70,32 @@ def test_more_tiles_per_workgroup_than_placed_up_front():
         err = max(err, float(np.max(np.abs(res["out"][tok] - ref["out"]))))
     say(f"[many tiles] all {T} tokens compared, rel err {err / scale:.3e}")
     assert err / scale <= TOL[cfg["dtype"]]
+
+
+WIDE_PLACED_UP_FRONT = 128
+WIDE_BM = 256
+
+
+def test_wide_tiles_more_per_workgroup_than_placed_up_front():
+    cfg = custom(T=600000, hidden_size=1024, num_experts=4, num_experts_per_tok=2,
+                 moe_intermediate_size=1024, num_shared_experts=0, name="many_wide_tiles")
+    T, k, E, I = cfg["T"], cfg["num_experts_per_tok"], cfg["num_experts"], cfg["moe_intermediate_size"]
+    assert bench.gate_up_kernel(cfg, T) == "moe_gate_up_wide_kernel"
+    inp = synth.generate(cfg)
+    dev = Dev(inp)
+    say(f"[many wide tiles] T={T}")
+    res = dev.forward(deterministic=1)
+    s, keys, idx, w = O.route(res["logits"], inp.expert_bias, k, cfg["score_func"],
+                              bool(cfg["route_norm"]), cfg["route_scale"])
+    assert np.array_equal(res["idx"], idx)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    tiles = int(sum((n + WIDE_BM - 1) // WIDE_BM for n in counts)) * (2 * I // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"[many wide tiles] {tiles} gate/up tiles on {cus} compute units: {tiles / cus:.0f} each")
+    assert tiles > WIDE_PLACED_UP_FRONT * cus
+    tok = np.sort(np.random.default_rng(5).choice(T, 24576, replace=False))
+    ref = O.moe_forward_tokens(inp, cfg, tok, logits_rows=res["logits"][tok])
+    assert np.array_equal(ref["idx"], res["idx"][tok])
+    e = float(np.max(np.abs(res["out"][tok] - ref["out"]))) / float(np.max(np.abs(ref["out"])))
+    say(f"[many wide tiles] {tok.size} sampled tokens compared, rel err {e:.3e}")
+    assert e <= TOL[cfg["dtype"]]
