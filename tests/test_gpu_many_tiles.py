@@ -1,12 +1,15 @@
 """Batches large enough that every workgroup of the persistent grouped GEMMs
 runs more tiles than it places up front: a workgroup stores the places of
-its first tiles in LDS (256 for the 128-row kernels, 128 for the 256-row
-ones) and computes the places of later ones on the fly.
+its first tiles in LDS (256 for the 128-row kernels, 128 for the 32-row and
+256-row ones) and computes the places of later ones on the fly.
 
 * 128-row kernels: 600000 tokens, hidden 64, 4 experts top-2, intermediate
   1024 (8 gate/up column tiles): about 290 gate/up tiles per workgroup.
   Every token's output is compared with the float64 oracle (per token, in
   chunks).
+* 32-row (decode) kernels, forced with MOE_GEMM_TILE=32 (they place 128 up
+  front): 70000 tokens, hidden 256, 4 experts top-2, intermediate 1024: about
+  137 gate/up tiles per workgroup, every token against the oracle.
 * 256-row kernels: 600000 tokens, hidden and intermediate 1024, 4 experts
   top-2: about 146 gate/up tiles per workgroup. 24576 sampled tokens are
   compared (a 256-row tile holds none of their rows with probability about
@@ -99,3 +102,35 @@ def test_wide_tiles_more_per_workgroup_than_placed_up_front():
     e = float(np.max(np.abs(res["out"][tok] - ref["out"]))) / float(np.max(np.abs(ref["out"])))
     say(f"[many wide tiles] {tok.size} sampled tokens compared, rel err {e:.3e}")
     assert e <= TOL[cfg["dtype"]]
+
+
+DECODE_PLACED_UP_FRONT = 128
+DECODE_BM = 32
+
+
+def test_decode_tiles_more_per_workgroup_than_placed_up_front(monkeypatch):
+    monkeypatch.setenv("MOE_GEMM_TILE", "32")
+    cfg = custom(T=70000, hidden_size=256, num_experts=4, num_experts_per_tok=2,
+                 moe_intermediate_size=1024, num_shared_experts=0, name="many_decode_tiles")
+    T, k, E, I = cfg["T"], cfg["num_experts_per_tok"], cfg["num_experts"], cfg["moe_intermediate_size"]
+    inp = synth.generate(cfg)
+    dev = Dev(inp)
+    say(f"[many decode tiles] T={T}")
+    res = dev.forward(deterministic=1)
+    s, keys, idx, w = O.route(res["logits"], inp.expert_bias, k, cfg["score_func"],
+                              bool(cfg["route_norm"]), cfg["route_scale"])
+    assert np.array_equal(res["idx"], idx)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    tiles = int(sum((n + DECODE_BM - 1) // DECODE_BM for n in counts)) * (I // GATE_UP_COLS)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"[many decode tiles] {tiles} gate/up tiles on {cus} compute units: {tiles / cus:.0f} each")
+    assert tiles > DECODE_PLACED_UP_FRONT * cus
+    scale, err = 0.0, 0.0
+    for c0 in range(0, T, 35000):
+        tok = np.arange(c0, min(T, c0 + 35000))
+        ref = O.moe_forward_tokens(inp, cfg, tok, logits_rows=res["logits"][tok])
+        assert np.array_equal(ref["idx"], res["idx"][tok])
+        scale = max(scale, float(np.max(np.abs(ref["out"]))))
+        err = max(err, float(np.max(np.abs(res["out"][tok] - ref["out"]))))
+    say(f"[many decode tiles] all {T} tokens compared, rel err {err / scale:.3e}")
+    assert err / scale <= TOL[cfg["dtype"]]
